@@ -1,0 +1,102 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail a pin.
+
+Each case monkeypatches one plausible bug into oracle.moe_share and checks
+that at least one of the pin tests raises.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_share as om
+import test_oracle_route_layout as RL
+import test_oracle_ffn_combine as FC
+
+
+def _route_ties_high(logits, k, gate_kind):
+    lg = np.asarray(logits, dtype=np.float32)
+    E = lg.shape[1]
+    order = E - 1 - np.argsort(-lg[:, ::-1], axis=1, kind="stable")   # ties -> higher id
+    ids = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(lg, ids, axis=1).astype(np.float64)
+    z = np.exp(sel - sel[:, :1])
+    return ids, z / z.sum(axis=1, keepdims=True)
+
+
+def _route_unnormalised(logits, k, gate_kind):
+    lg = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    ids = np.argsort(-lg, axis=1, kind="stable")[:, :k].astype(np.int32)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return ids, np.take_along_axis(p, ids.astype(np.int64), axis=1)
+
+
+def _silu_wrong_sign(u):
+    return u / (1.0 + np.exp(u))
+
+
+def _ffn_swapped(X, W1, W3, W2):
+    if W3 is None:
+        return om.silu(X @ W1.T) @ W2.T
+    return (om.silu(X @ W3.T) * (X @ W1.T)) @ W2.T
+
+
+def _order_local_first(R, r_self):
+    return [r_self] + [s for s in range(R) if s != r_self]
+
+
+MUTATIONS = {
+    "ties_to_higher_id": ("route", _route_ties_high, [RL.test_route_ties_go_to_lower_expert_id]),
+    "gates_not_renormalised": ("route", _route_unnormalised,
+                               [lambda: RL.test_softmax_gates_equal_renormalised_full_softmax()]),
+    "silu_sign": ("silu", _silu_wrong_sign,
+                  [lambda: FC.test_sum_of_shares_equals_moe_definition(FC.TINY[0], 4)]),
+    "w1_w3_swapped": ("expert_ffn", _ffn_swapped,
+                      [lambda: FC.test_sum_of_shares_equals_moe_definition(FC.TINY[0], 1)]),
+    "local_group_first": ("group_order", _order_local_first,
+                          [lambda: RL.test_layout_matches_brute_force(4, 16, 8, 2, 0, 4)]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, bad, pins = MUTATIONS[name]
+    monkeypatch.setattr(om, attr, bad)
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            pin()
+
+
+def test_dropped_gate_is_caught(monkeypatch):
+    orig = om.weighted_reduction
+
+    def no_gate(bufs, y_perm, gates, lay):
+        return orig(bufs, y_perm, np.ones_like(gates), lay)
+    monkeypatch.setattr(om, "weighted_reduction", no_gate)
+    with pytest.raises(AssertionError):
+        FC.test_sum_of_shares_equals_moe_definition(FC.TINY[1], 4)
+
+
+def test_ascending_expert_order_is_caught(monkeypatch):
+    def tile_schedule_ascending(lay):
+        b = om.Bands.__new__(om.Bands)
+        res = ORIG_SCHED(lay)
+        # plant: reverse the order of experts' remote blocks
+        n = res.n_remote
+        blocks = []
+        i = 0
+        while i < n:
+            j = i
+            while j < n and res.expert[j] == res.expert[i]:
+                j += 1
+            blocks.append(list(range(i, j)))
+            i = j
+        perm = [p for blk in reversed(blocks) for p in blk] + list(range(n, len(res.row0)))
+        for f in ("expert", "row0", "dest", "recv0", "valid"):
+            setattr(b, f, getattr(res, f)[perm])
+        b.n_remote = n
+        return b
+    monkeypatch.setattr(om, "tile_schedule", tile_schedule_ascending)
+    with pytest.raises(AssertionError):
+        RL.test_schedule_matches_page_example()
+
+
+ORIG_SCHED = om.tile_schedule
