@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark: one EP rank's MoE-layer share on one MI355X, overlap vs non-overlap.
+
+A step is one pass of the whole share over one batch of synthetic input:
+route -> counts to host -> partition (consumer CUs, segment size) ->
+permute -> expert FFN with the overlapped combine transfer -> weighted
+reduction. Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line on stdout (details on stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+DEFAULT_TB = {1: 64, 2: 128, 3: 128, 4: 64, 5: 64}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload id (1-5); 2 = Mixtral-shaped")
+    ap.add_argument("--layer", type=int, default=0, help="layer of the layered workload")
+    ap.add_argument("--tb", type=int, default=0, help="band height (0 = per-workload default)")
+    ap.add_argument("--c", type=int, default=0, help="consumer CUs (0 = cost model)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, tb, target_s):
+    """Times the CPU oracle (as it is) on a bounded sample of the same workload."""
+    from oracle import moe_share as om
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    ids, gates = om.route(inp.logits, w.k, w.gate_kind)
+    lay = om.row_layout(ids, w.R, w.T, w.E_local, inp.r_self, tb)
+    t_route = time.perf_counter() - t0
+    # expert FFN on the first n rows of every non-empty local expert
+    x_perm = om.gather_rows(inp.x, lay)
+    experts = [e for e in range(w.E_local) if lay.M_e[e] > 0]
+    wts = {}
+    for e in experts:
+        wts[e] = (om.widen_bf16(inp.W1[e]), om.widen_bf16(inp.W3[e]) if inp.W3 is not None else None,
+                  om.widen_bf16(inp.W2[e]))
+    per_row = (6 if w.gated else 4) * w.H * w.F
+    n = 8
+    flops = 0.0
+    t_ffn = 0.0
+    while True:
+        flops = 0.0
+        t0 = time.perf_counter()
+        for e in experts:
+            lo = int(lay.expert_base[e])
+            m = min(n, int(lay.M_e[e]))
+            om.expert_ffn(x_perm[lo:lo + m], *wts[e])
+            flops += per_row * m
+        t_ffn = time.perf_counter() - t0
+        if t_ffn >= target_s / 4 or n >= 4096:
+            break
+        n *= 2
+    val = flops / t_ffn / 1e12
+    return {"value": round(val, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle: routing+layout of all {w.R * w.T} tokens ({t_route:.2f} s, "
+                       f"not in value) and the expert FFN on the first {n} rows of each of "
+                       f"{len(experts)} local experts ({flops / 1e9:.1f} GFLOP in {t_ffn:.2f} s)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share only (this build runs on a single MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from synth import WORKLOADS, make_logits, make_x, make_local_weights
+    from synth.workloads import ShareInputs
+    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL
+    from combine_overlap_amd.share import MoEShare, bf16_tensor
+
+    w = WORKLOADS[args.config]
+    tb = args.tb or DEFAULT_TB[args.config]
+    r_self = 0
+    log(f"[bench] workload {w.name} layer {args.layer} tb_m={tb}: generating inputs")
+    W1, W3, W2 = make_local_weights(w, r_self)
+    inp = ShareInputs(w, r_self, make_logits(w, args.layer), make_x(w), W1, W3, W2)
+    dev = torch.device("cuda:0")
+    sh = MoEShare(w.R, w.T, w.H, w.F, w.E, w.k, w.gated, w.gate_kind, r_self=r_self, tb_m=tb,
+                  device=dev)
+    sh.allocate(torch.from_numpy(inp.logits).to(dev), bf16_tensor(inp.x, dev), bf16_tensor(W1, dev),
+                bf16_tensor(W3, dev) if W3 is not None else None, bf16_tensor(W2, dev))
+    torch.cuda.synchronize()
+    n_cu = sh.ctx.num_cus
+    log(f"[bench] device CUs {n_cu}; buffers ready")
+
+    def step(mode):
+        sh.route()
+        c, mgb, _ = sh.partition()
+        if args.c:
+            c = args.c
+        sh.shape.mgb = mgb
+        sh.permute()
+        sh.expert_forward(mode, n_consumer_cu=c)
+        sh.combine()
+        return c, mgb
+
+    # warmup + sanity
+    for _ in range(max(1, args.warmup)):
+        c_used, mgb_used = step(MOE_MODE_OVERLAP)
+    torch.cuda.synchronize()
+    if sh.status() != 0:
+        raise RuntimeError(f"device status {sh.status()} after warmup")
+    counts = sh.buf.counts.cpu().numpy()
+    M = int(counts.sum())
+    remote = int(counts.sum() - counts[:, r_self].sum())
+    per_row = (6 if w.gated else 4) * w.H * w.F
+    flops = float(per_row) * M
+    flops1 = float((4 if w.gated else 2) * w.H * w.F) * M
+    plan = sh.plan_arrays()
+    m_pad = plan["m_pad"]
+    log(f"[bench] valid rows {M}, remote rows {remote}, padded rows {m_pad}, bands {plan['n_bands']}, "
+        f"segments {plan['n_seg']}, c={c_used}, mgb={mgb_used}")
+
+    def timed(mode, k):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(k):
+            step(mode)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / k
+
+    t_ovl = timed(MOE_MODE_OVERLAP, args.steps)
+    log(f"[bench] overlap layer step {t_ovl * 1e3:.3f} ms")
+    for _ in range(args.warmup):
+        step(MOE_MODE_SEQUENTIAL)
+    t_seq = timed(MOE_MODE_SEQUENTIAL, args.steps)
+    log(f"[bench] sequential layer step {t_seq * 1e3:.3f} ms")
+
+    # per-phase device timings (HIP events on the kernels' own streams)
+    sh.ctx.set_timing(True)
+    ph = {MOE_MODE_OVERLAP: [], MOE_MODE_SEQUENTIAL: []}
+    for mode in (MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL):
+        for _ in range(max(3, args.steps)):
+            sh.expert_forward(mode, n_consumer_cu=c_used)
+            ph[mode].append(sh.ctx.timings())
+    sh.ctx.set_timing(False)
+
+    def med(mode, key):
+        return float(np.median([d[key] for d in ph[mode]]))
+    g1 = med(MOE_MODE_OVERLAP, "gemm1")
+    prod = med(MOE_MODE_OVERLAP, "producer")
+    ovl_total = med(MOE_MODE_OVERLAP, "total")
+    exposed = med(MOE_MODE_OVERLAP, "exposed")
+    seq_g2 = med(MOE_MODE_SEQUENTIAL, "producer")
+    seq_copy = med(MOE_MODE_SEQUENTIAL, "exposed")
+    seq_total = med(MOE_MODE_SEQUENTIAL, "total")
+    log(f"[bench] overlap: gemm1 {g1:.3f} ms, producer {prod:.3f} ms, expert phase {ovl_total:.3f} ms, "
+        f"exposed copy {exposed * 1e3:.1f} us")
+    log(f"[bench] sequential: gemm2 {seq_g2:.3f} ms, bulk copy {seq_copy * 1e3:.1f} us, "
+        f"expert phase {seq_total:.3f} ms")
+    ach1 = flops1 / (g1 * 1e-3) / 1e12
+
+    out = {
+        "metric": "MoE-layer TFLOP/s per EP rank (overlapped combine), % of bf16 MFMA peak",
+        "value": round(flops / t_ovl / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_ovl * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": w.name, "layer": args.layer, "R": w.R, "T": w.T, "H": w.H, "F": w.F,
+                   "E": w.E, "k": w.k, "r_self": r_self, "tb_m": tb, "consumer_cus": c_used,
+                   "mgb": mgb_used, "parallelism": "one EP rank share on one GPU"},
+        "layer": {
+            "valid_rows": M, "remote_rows": remote, "padded_rows": m_pad,
+            "algorithmic_tflop": round(flops / 1e12, 4),
+            "overlap_ms": round(t_ovl * 1e3, 4), "sequential_ms": round(t_seq * 1e3, 4),
+            "speedup_vs_sequential": round(t_seq / t_ovl, 4),
+            "pct_mfma_peak_layer": round(100 * flops / t_ovl / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "expert_phase_overlap_ms": round(ovl_total, 4),
+            "expert_phase_sequential_ms": round(seq_total, 4),
+            "gemm1_ms": round(g1, 4), "producer_ms": round(prod, 4),
+            "exposed_copy_us": round(exposed * 1e3, 2), "bulk_copy_us": round(seq_copy * 1e3, 2),
+            "exposed_copy_fraction": round(exposed / seq_copy, 4) if seq_copy > 0 else None,
+            "producer_tflops": round(float(2 * w.H * w.F * M) / (prod * 1e-3) / 1e12, 2),
+        },
+        "roofline": {"kernel": "k_gemm first projection (x W1^T, x W3^T, SiLU gate)",
+                     "bound": "mfma", "achieved": round(ach1, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach1 / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, inp, tb, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

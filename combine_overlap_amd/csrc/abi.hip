@@ -1,0 +1,347 @@
+// Host side of the C ABI: argument validation (always before any HIP call),
+// workspace layout, and the launch order of the share's kernels.
+#include <string.h>
+
+#include "common.hpp"
+
+struct moe_ctx {
+  int device;
+  int n_cu;
+  hipEvent_t ev_producer;   // first projection done -> consumer may start
+  hipEvent_t ev_consumer;   // consumer done -> joined back into the producer stream
+  int timing;               // 1: record tev[] in the forward
+  int timed;                // a timed call has been enqueued
+  int timed_mode;
+  hipEvent_t tev[5];        // start, first projection end, producer end, consumer end, join
+};
+
+namespace moe {
+
+static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int make_geometry(const moe_shape_t* s, Geometry* g) {
+  if (s == nullptr || g == nullptr) return MOE_ERR_INVALID_ARG;
+  if (s->R < 1 || s->R > MOE_MAX_RANKS || s->T < 1 || s->E < 1 || s->k < 1) return MOE_ERR_INVALID_ARG;
+  if (s->E % s->R != 0) return MOE_ERR_INVALID_ARG;
+  if (s->k > s->E || s->k > 16) return MOE_ERR_INVALID_ARG;
+  if (s->r_self < 0 || s->r_self >= s->R) return MOE_ERR_INVALID_ARG;
+  if ((s->gated != 0 && s->gated != 1) || (s->gate_kind != MOE_GATE_SOFTMAX && s->gate_kind != MOE_GATE_SIGMOID))
+    return MOE_ERR_INVALID_ARG;
+  if (s->mgb < 1) return MOE_ERR_INVALID_ARG;
+  if (s->H < 256 || s->H % 256 != 0 || s->F < 128 || s->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (s->tb_m != 64 && s->tb_m != 128 && s->tb_m != 256) return MOE_ERR_UNSUPPORTED;
+  if (s->E > 512) return MOE_ERR_UNSUPPORTED;
+  const int El = s->E / s->R;
+  if (El > 256 || (int64_t)El * s->R > 2048) return MOE_ERR_UNSUPPORTED;
+  const int64_t n_tok = (int64_t)s->R * s->T;
+  if (n_tok * s->k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  g->R = s->R; g->T = s->T; g->H = s->H; g->F = s->F; g->E = s->E; g->k = s->k;
+  g->r_self = s->r_self; g->gated = s->gated; g->gate_kind = s->gate_kind;
+  g->tb_m = s->tb_m; g->mgb = s->mgb;
+  g->El = El;
+  g->chunks_per_rank = (int32_t)ceil_div64(s->T, kChunk);
+  g->n_chunks = g->chunks_per_rank * s->R;
+  const int64_t valid_max = n_tok * (s->k < El ? s->k : El);
+  const int64_t m_pad_max = valid_max + (int64_t)El * s->R * (s->tb_m - 1);
+  if (m_pad_max * (s->H > s->F ? s->H : s->F) >= (int64_t)1 << 40 || m_pad_max >= (int64_t)1 << 31)
+    return MOE_ERR_UNSUPPORTED;
+  g->m_pad_max = ceil_div64(m_pad_max, s->tb_m) * s->tb_m;
+  g->max_bands = (int32_t)(g->m_pad_max / s->tb_m);
+  // per-shape tile table: output projection 256 wide; first projection
+  // 256-wide MFMA tiles (128 h columns when gated)
+  g->bn2 = 256;
+  g->tiles2 = s->H / g->bn2;
+  if (s->gated) { g->bn1 = 256; g->bn1_out = 128; }
+  else if (s->F % 256 == 0) { g->bn1 = 256; g->bn1_out = 256; }
+  else { g->bn1 = 128; g->bn1_out = 128; }
+  g->tiles1 = s->F / g->bn1_out;
+  const int64_t flags = (int64_t)g->max_bands * g->tiles2;
+  if (flags >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  g->max_flags = (int32_t)flags;
+  g->recv_rows_max = (int32_t)((int64_t)s->T * (s->k < El ? s->k : El));
+  return MOE_OK;
+}
+
+WsLayout ws_layout(const Geometry& g) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t n_i32) {
+    const size_t at = off;
+    off += (n_i32 * 4 + 255) / 256 * 256;
+    return at;
+  };
+  const size_t nce = (size_t)g.n_chunks * g.El, er = (size_t)g.El * g.R, mb = (size_t)g.max_bands;
+  L.meta = take(META_WORDS);
+  L.chunk_counts = take(nce);
+  L.chunk_base = take(nce);
+  L.group_row = take(er);
+  L.expert_base = take(g.El + 1);
+  L.recv_off = take(er);
+  L.band_row0 = take(mb); L.band_expert = take(mb); L.band_dest = take(mb);
+  L.band_recv0 = take(mb); L.band_valid = take(mb);
+  L.seg_band0 = take(mb); L.seg_nbands = take(mb); L.seg_dest = take(mb);
+  L.seg_src_row = take(mb); L.seg_dst_row = take(mb); L.seg_rows = take(mb);
+  L.row_src = take((size_t)g.m_pad_max);
+  L.recv_row = take((size_t)g.R * g.T * g.k);
+  L.total = off;
+  return L;
+}
+
+void plan_from_ws(const Geometry& g, void* ws, moe_plan_t* p) {
+  const WsLayout L = ws_layout(g);
+  char* b = static_cast<char*>(ws);
+  auto at = [&](size_t o) { return reinterpret_cast<int32_t*>(b + o); };
+  p->meta = at(L.meta);
+  p->group_row = at(L.group_row);
+  p->expert_base = at(L.expert_base);
+  p->recv_off = at(L.recv_off);
+  p->band_row0 = at(L.band_row0); p->band_expert = at(L.band_expert); p->band_dest = at(L.band_dest);
+  p->band_recv0 = at(L.band_recv0); p->band_valid = at(L.band_valid);
+  p->seg_band0 = at(L.seg_band0); p->seg_nbands = at(L.seg_nbands); p->seg_dest = at(L.seg_dest);
+  p->seg_src_row = at(L.seg_src_row); p->seg_dst_row = at(L.seg_dst_row); p->seg_rows = at(L.seg_rows);
+  p->row_src = at(L.row_src);
+  p->recv_row = at(L.recv_row);
+  p->chunk_base = at(L.chunk_base);
+  p->chunk_counts = at(L.chunk_counts);
+}
+
+static inline bool ws_ok(const void* ws) {
+  return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0;
+}
+
+static inline int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_error_string(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or tile configuration";
+    case MOE_ERR_WORKSPACE: return "workspace pointer missing or not 256-byte aligned";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_TIMEOUT: return "device watchdog: a ready-flag wait exceeded its budget";
+    case MOE_ERR_DEVICE: return "device-side consistency check failed";
+    default: return "unknown error";
+  }
+}
+
+int moe_query_sizes(const moe_shape_t* shape, moe_sizes_t* out) {
+  if (out == nullptr) return MOE_ERR_INVALID_ARG;
+  Geometry g;
+  const int rc = make_geometry(shape, &g);
+  if (rc != MOE_OK) return rc;
+  out->ws_bytes = ws_layout(g).total;
+  out->m_pad_max = g.m_pad_max;
+  out->max_bands = g.max_bands;
+  out->max_flags = g.max_flags;
+  out->recv_rows_max = g.recv_rows_max;
+  out->bn_out = g.bn2;
+  return MOE_OK;
+}
+
+int moe_plan_view(const moe_shape_t* shape, void* ws, moe_plan_t* out) {
+  if (out == nullptr) return MOE_ERR_INVALID_ARG;
+  Geometry g;
+  const int rc = make_geometry(shape, &g);
+  if (rc != MOE_OK) return rc;
+  if (!ws_ok(ws)) return MOE_ERR_WORKSPACE;
+  plan_from_ws(g, ws, out);
+  return MOE_OK;
+}
+
+int moe_ctx_create(moe_ctx_t** out) {
+  if (out == nullptr) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  moe_ctx* c = new moe_ctx();
+  c->timing = 0;
+  c->timed = 0;
+  if (hipGetDevice(&c->device) != hipSuccess ||
+      hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess ||
+      hipEventCreateWithFlags(&c->ev_producer, hipEventDisableTiming) != hipSuccess) {
+    delete c;
+    return MOE_ERR_HIP;
+  }
+  if (hipEventCreateWithFlags(&c->ev_consumer, hipEventDisableTiming) != hipSuccess) {
+    (void)hipEventDestroy(c->ev_producer);
+    delete c;
+    return MOE_ERR_HIP;
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+int moe_ctx_set_timing(moe_ctx_t* ctx, int enable) {
+  if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
+  if (enable && !ctx->timing) {
+    for (int i = 0; i < 5; ++i)
+      if (hipEventCreate(&ctx->tev[i]) != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(ctx->tev[j]);
+        return MOE_ERR_HIP;
+      }
+    ctx->timing = 1;
+  } else if (!enable && ctx->timing) {
+    for (int i = 0; i < 5; ++i) (void)hipEventDestroy(ctx->tev[i]);
+    ctx->timing = 0;
+  }
+  ctx->timed = 0;
+  return MOE_OK;
+}
+
+int moe_ctx_timings(moe_ctx_t* ctx, float* ms) {
+  if (ctx == nullptr || ms == nullptr || !ctx->timing || !ctx->timed) return MOE_ERR_INVALID_ARG;
+  if (hipEventSynchronize(ctx->tev[4]) != hipSuccess) return MOE_ERR_HIP;
+  float t01, t12, t13, t04, t23;
+  if (hipEventElapsedTime(&t01, ctx->tev[0], ctx->tev[1]) != hipSuccess ||
+      hipEventElapsedTime(&t12, ctx->tev[1], ctx->tev[2]) != hipSuccess ||
+      hipEventElapsedTime(&t13, ctx->tev[1], ctx->tev[3]) != hipSuccess ||
+      hipEventElapsedTime(&t04, ctx->tev[0], ctx->tev[4]) != hipSuccess ||
+      hipEventElapsedTime(&t23, ctx->tev[2], ctx->tev[3]) != hipSuccess)
+    return MOE_ERR_HIP;
+  ms[0] = t01;
+  ms[1] = t12;
+  ms[2] = t13;
+  ms[3] = t04;
+  ms[4] = t23 > 0.f ? t23 : 0.f;
+  return MOE_OK;
+}
+
+int moe_ctx_destroy(moe_ctx_t* ctx) {
+  if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
+  if (ctx->timing) (void)moe_ctx_set_timing(ctx, 0);
+  const hipError_t a = hipEventDestroy(ctx->ev_producer);
+  const hipError_t b = hipEventDestroy(ctx->ev_consumer);
+  delete ctx;
+  return (a == hipSuccess && b == hipSuccess) ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_ctx_num_cus(const moe_ctx_t* ctx) { return ctx ? ctx->n_cu : MOE_ERR_INVALID_ARG; }
+
+int moe_route(const moe_shape_t* shape, const float* logits, int32_t* topk_ids, float* gates,
+              int32_t* counts, void* ws, void* stream) {
+  Geometry g;
+  int rc = make_geometry(shape, &g);
+  if (rc != MOE_OK) return rc;
+  if (!logits || !topk_ids || !gates || !counts) return MOE_ERR_INVALID_ARG;
+  if (!ws_ok(ws)) return MOE_ERR_WORKSPACE;
+  moe_plan_t p;
+  plan_from_ws(g, ws, &p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_rc(launch_route(g, logits, topk_ids, gates, p, st));
+  if (rc != MOE_OK) return rc;
+  return hip_rc(launch_count(g, counts, p, st));
+}
+
+int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_ids,
+                const int32_t* counts, uint16_t* x_perm, void* ws, void* stream) {
+  Geometry g;
+  int rc = make_geometry(shape, &g);
+  if (rc != MOE_OK) return rc;
+  if (!x || !topk_ids || !counts || !x_perm) return MOE_ERR_INVALID_ARG;
+  if (!ws_ok(ws)) return MOE_ERR_WORKSPACE;
+  moe_plan_t p;
+  plan_from_ws(g, ws, &p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = hip_rc(launch_plan(g, counts, p, st))) != MOE_OK) return rc;
+  if ((rc = hip_rc(launch_padzero(g, x_perm, counts, p, st))) != MOE_OK) return rc;
+  return hip_rc(launch_gather(g, x, topk_ids, x_perm, p, st));
+}
+
+int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16_t* x_perm,
+                               const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                               void* ws, uint16_t* h, uint16_t* y_perm,
+                               uint16_t* const* combine_buf, uint32_t* flags, uint32_t epoch,
+                               int32_t n_consumer_cu, int32_t mode, void* producer_stream,
+                               void* consumer_stream) {
+  Geometry g;
+  int rc = make_geometry(shape, &g);
+  if (rc != MOE_OK) return rc;
+  if (!ctx || !x_perm || !w1 || !w2 || !h || !y_perm || !combine_buf) return MOE_ERR_INVALID_ARG;
+  if ((g.gated != 0) != (w3 != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_MODE_OVERLAP && mode != MOE_MODE_SEQUENTIAL) return MOE_ERR_INVALID_ARG;
+  if (!ws_ok(ws)) return MOE_ERR_WORKSPACE;
+  BufPtrs bufs{};
+  for (int s = 0; s < g.R; ++s) {
+    if (s == g.r_self) continue;
+    if (combine_buf[s] == nullptr) return MOE_ERR_INVALID_ARG;
+    bufs.p[s] = combine_buf[s];
+  }
+  if (mode == MOE_MODE_OVERLAP) {
+    if (!flags || epoch == 0 || n_consumer_cu < 1 || n_consumer_cu > 64 ||
+        n_consumer_cu >= ctx->n_cu || consumer_stream == producer_stream)
+      return MOE_ERR_INVALID_ARG;
+  }
+  moe_plan_t p;
+  plan_from_ws(g, ws, &p);
+  hipStream_t ps = static_cast<hipStream_t>(producer_stream);
+  hipStream_t cs = static_cast<hipStream_t>(consumer_stream);
+  const int ncu = ctx->n_cu;
+  const bool tm = ctx->timing != 0;
+  auto rec = [&](int i, hipStream_t st) { return tm ? hip_rc(hipEventRecord(ctx->tev[i], st)) : MOE_OK; };
+  if ((rc = rec(0, ps)) != MOE_OK) return rc;
+  if ((rc = hip_rc(launch_gemm1(g, x_perm, w1, w3, h, p, ncu, ps))) != MOE_OK) return rc;
+  if ((rc = rec(1, ps)) != MOE_OK) return rc;
+  if (mode == MOE_MODE_SEQUENTIAL) {
+    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ncu, ps))) != MOE_OK) return rc;
+    if ((rc = rec(2, ps)) != MOE_OK) return rc;
+    if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 2 * ncu, ps))) != MOE_OK) return rc;
+    if ((rc = rec(3, ps)) != MOE_OK) return rc;
+    if ((rc = rec(4, ps)) != MOE_OK) return rc;
+    ctx->timed = tm;
+    ctx->timed_mode = mode;
+    return MOE_OK;
+  }
+  if ((rc = hip_rc(hipEventRecord(ctx->ev_producer, ps))) != MOE_OK) return rc;
+  if ((rc = hip_rc(hipStreamWaitEvent(cs, ctx->ev_producer, 0))) != MOE_OK) return rc;
+  if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ncu - n_consumer_cu, ps))) != MOE_OK)
+    return rc;
+  if ((rc = rec(2, ps)) != MOE_OK) return rc;
+  if ((rc = hip_rc(launch_consumer(g, y_perm, bufs, p, flags, epoch, n_consumer_cu, cs))) != MOE_OK)
+    return rc;
+  if ((rc = rec(3, cs)) != MOE_OK) return rc;
+  if ((rc = hip_rc(hipEventRecord(ctx->ev_consumer, cs))) != MOE_OK) return rc;
+  if ((rc = hip_rc(hipStreamWaitEvent(ps, ctx->ev_consumer, 0))) != MOE_OK) return rc;
+  if ((rc = rec(4, ps)) != MOE_OK) return rc;
+  ctx->timed = tm;
+  ctx->timed_mode = mode;
+  return MOE_OK;
+}
+
+int moe_combine(const moe_shape_t* shape, uint16_t* const* combine_buf, const uint16_t* y_perm,
+                const float* gates, void* ws, uint16_t* y_share, void* stream) {
+  Geometry g;
+  int rc = make_geometry(shape, &g);
+  if (rc != MOE_OK) return rc;
+  if (!combine_buf || !y_perm || !gates || !y_share) return MOE_ERR_INVALID_ARG;
+  if (!ws_ok(ws)) return MOE_ERR_WORKSPACE;
+  BufPtrs bufs{};
+  for (int s = 0; s < g.R; ++s) {
+    if (s == g.r_self) continue;
+    if (combine_buf[s] == nullptr) return MOE_ERR_INVALID_ARG;
+    bufs.p[s] = combine_buf[s];
+  }
+  moe_plan_t p;
+  plan_from_ws(g, ws, &p);
+  return hip_rc(launch_combine(g, bufs, y_perm, gates, p, y_share, static_cast<hipStream_t>(stream)));
+}
+
+int moe_read_status(const moe_shape_t* shape, void* ws, int32_t* status, void* stream) {
+  Geometry g;
+  const int rc = make_geometry(shape, &g);
+  if (rc != MOE_OK) return rc;
+  if (!status) return MOE_ERR_INVALID_ARG;
+  if (!ws_ok(ws)) return MOE_ERR_WORKSPACE;
+  moe_plan_t p;
+  plan_from_ws(g, ws, &p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(status, p.meta + META_STATUS, sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_HIP;
+  return *status;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal definitions shared by the gfx950 kernels and the host ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "moe_overlap.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// tokens per routing chunk: a chunk never spans two source ranks
+constexpr int kChunk = 256;
+// meta words in the workspace
+enum { META_MPAD = 0, META_NBANDS = 1, META_NREMOTE = 2, META_NSEG = 3, META_STATUS = 4, META_WORDS = 64 };
+
+struct Geometry {
+  int32_t R, T, H, F, E, k, r_self, gated, gate_kind, tb_m, mgb;
+  int32_t El;                 // local experts
+  int32_t chunks_per_rank;    // ceil(T / kChunk)
+  int32_t n_chunks;           // R * chunks_per_rank
+  int64_t m_pad_max;
+  int32_t max_bands;
+  int32_t bn1;                // first projection: MFMA tile width (u and v columns for gated)
+  int32_t bn1_out;            // first projection: h columns per tile
+  int32_t bn2;                // output projection tile width
+  int32_t tiles1;             // h column tiles per band
+  int32_t tiles2;             // y column tiles per band
+  int32_t max_flags;
+  int32_t recv_rows_max;
+};
+
+// Byte offsets of the workspace sections (all 256-byte aligned).
+struct WsLayout {
+  size_t meta, chunk_counts, chunk_base, group_row, expert_base, recv_off;
+  size_t band_row0, band_expert, band_dest, band_recv0, band_valid;
+  size_t seg_band0, seg_nbands, seg_dest, seg_src_row, seg_dst_row, seg_rows;
+  size_t row_src, recv_row, total;
+};
+
+int make_geometry(const moe_shape_t* s, Geometry* g);
+WsLayout ws_layout(const Geometry& g);
+void plan_from_ws(const Geometry& g, void* ws, moe_plan_t* p);
+
+// combine-buffer pointers travel to kernels by value
+struct BufPtrs { uint16_t* p[MOE_MAX_RANKS]; };
+
+// ---- kernel launchers (enqueue only) ----
+hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, float* gates,
+                        const moe_plan_t& p, hipStream_t st);
+hipError_t launch_count(const Geometry& g, int32_t* counts, const moe_plan_t& p, hipStream_t st);
+hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, hipStream_t st);
+hipError_t launch_padzero(const Geometry& g, uint16_t* x_perm, const int32_t* counts,
+                          const moe_plan_t& p, hipStream_t st);
+hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
+                         uint16_t* x_perm, const moe_plan_t& p, hipStream_t st);
+hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_t* w1,
+                        const uint16_t* w3, uint16_t* h, const moe_plan_t& p, int grid,
+                        hipStream_t st);
+hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
+                        const moe_plan_t& p, uint32_t* flags, uint32_t epoch, int grid,
+                        hipStream_t st);
+hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
+                           const uint32_t* flags, uint32_t epoch, int n_wg, hipStream_t st);
+hipError_t launch_bulk_copy(const Geometry& g, const uint16_t* y, BufPtrs bufs,
+                            const moe_plan_t& p, int grid, hipStream_t st);
+hipError_t launch_combine(const Geometry& g, BufPtrs bufs, const uint16_t* y, const float* gates,
+                          const moe_plan_t& p, uint16_t* out, hipStream_t st);
+
+// ---- device helpers ----
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+}  // namespace moe

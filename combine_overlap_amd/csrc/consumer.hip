@@ -1,0 +1,125 @@
+// Consumer of the tile-signalling overlap paper (sec. 3.3.2-3.3.3): a
+// persistent kernel on a small set of CUs that walks the transfer segments
+// in schedule order, waits until every tile of a segment's row bands carries
+// the current epoch flag (acquire loads at agent scope), and then moves the
+// segment's valid rows with one contiguous copy into the combine buffer of
+// the owner rank. On one GPU the owner's receive buffer is a buffer in local
+// HBM; the copy is split evenly across the c consumer workgroups.
+//
+// Each consumer workgroup (1024 threads) also reserves enough LDS that no
+// producer workgroup can share its CU, which keeps the two partitions
+// disjoint (sec. 2.4: persistent kernels with fixed workgroup counts).
+//
+// Every wait is bounded: after kWaitTicks of the 100 MHz constant clock the
+// device status word becomes MOE_ERR_TIMEOUT and all consumer workgroups exit.
+//
+// The bulk copy (the non-overlapped baseline's second all-to-all, sec. 4.1.3)
+// copies all segments after the producer has finished, using every CU.
+#include "common.hpp"
+
+namespace moe {
+
+constexpr uint64_t kWaitTicks = 200000000ull;   // 2 s at 100 MHz
+constexpr int kConsumerThreads = 1024;
+constexpr int kConsumerLdsBytes = 80 * 1024;
+
+__device__ __forceinline__ void copy_units(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                           size_t lo, size_t hi, int tid, int nthr) {
+  size_t i = lo + tid;
+  for (; i + 3 * (size_t)nthr < hi; i += 4 * (size_t)nthr) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + nthr);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * (size_t)nthr);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * (size_t)nthr);
+    __builtin_nontemporal_store(a, dst + i);
+    __builtin_nontemporal_store(b, dst + i + nthr);
+    __builtin_nontemporal_store(c, dst + i + 2 * (size_t)nthr);
+    __builtin_nontemporal_store(d, dst + i + 3 * (size_t)nthr);
+  }
+  for (; i < hi; i += nthr) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+__global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* __restrict__ y,
+                                                                BufPtrs bufs, moe_plan_t p,
+                                                                const uint32_t* flags,
+                                                                uint32_t epoch, int tiles2,
+                                                                int H) {
+  __shared__ int s_abort;
+  __shared__ __attribute__((aligned(16))) uint32_t s_reserve[kConsumerLdsBytes / 4];
+  const int tid = threadIdx.x;
+  if (tid == 0) { s_abort = 0; s_reserve[0] = 0; }
+  __syncthreads();
+  const int n_seg = p.meta[META_NSEG];
+  const int nwg = gridDim.x, wg = blockIdx.x;
+  for (int sgi = 0; sgi < n_seg; ++sgi) {
+    const int b0 = p.seg_band0[sgi];
+    const int nb = p.seg_nbands[sgi];
+    if (tid < 64) {
+      const uint32_t* f = flags + (size_t)b0 * tiles2;
+      const int nf = nb * tiles2;
+      const uint64_t t_start = wall_clock64();
+      while (true) {
+        bool ok = true;
+        for (int i = tid; i < nf; i += 64)
+          ok &= (__hip_atomic_load(f + i, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == epoch);
+        if (__ballot(!ok) == 0ull) break;
+        if (wall_clock64() - t_start > kWaitTicks) {
+          if (tid == 0) {
+            s_abort = 1;
+            int expected = 0;
+            __hip_atomic_compare_exchange_strong(p.meta + META_STATUS, &expected, MOE_ERR_TIMEOUT,
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+          }
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    if (s_abort) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const size_t units = (size_t)p.seg_rows[sgi] * H / 8;
+    const size_t per = (units + nwg - 1) / nwg;
+    const size_t lo = (size_t)wg * per;
+    const size_t hi = lo + per < units ? lo + per : units;
+    if (lo < hi) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(y + (size_t)p.seg_src_row[sgi] * H);
+      u32x4* dst = reinterpret_cast<u32x4*>(bufs.p[p.seg_dest[sgi]] + (size_t)p.seg_dst_row[sgi] * H);
+      copy_units(src, dst, lo, hi, tid, kConsumerThreads);
+    }
+  }
+  if (tid == 0 && s_reserve[0] != 0) s_abort = 2;   // keeps the LDS reservation alive
+}
+
+// baseline: all remote segments after the producer, on all CUs
+__global__ __launch_bounds__(256) void k_bulk_copy(const uint16_t* __restrict__ y, BufPtrs bufs,
+                                                    moe_plan_t p, int H) {
+  const int n_seg = p.meta[META_NSEG];
+  const int nwg = gridDim.x, wg = blockIdx.x;
+  for (int sgi = 0; sgi < n_seg; ++sgi) {
+    const size_t units = (size_t)p.seg_rows[sgi] * H / 8;
+    const size_t per = (units + nwg - 1) / nwg;
+    const size_t lo = (size_t)wg * per;
+    const size_t hi = lo + per < units ? lo + per : units;
+    if (lo >= hi) continue;
+    const u32x4* src = reinterpret_cast<const u32x4*>(y + (size_t)p.seg_src_row[sgi] * H);
+    u32x4* dst = reinterpret_cast<u32x4*>(bufs.p[p.seg_dest[sgi]] + (size_t)p.seg_dst_row[sgi] * H);
+    copy_units(src, dst, lo, hi, threadIdx.x, 256);
+  }
+}
+
+hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
+                           const uint32_t* flags, uint32_t epoch, int n_wg, hipStream_t st) {
+  hipLaunchKernelGGL(k_consumer, dim3(n_wg), dim3(kConsumerThreads), 0, st, y, bufs, p, flags,
+                     epoch, g.tiles2, g.H);
+  return hipGetLastError();
+}
+
+hipError_t launch_bulk_copy(const Geometry& g, const uint16_t* y, BufPtrs bufs,
+                            const moe_plan_t& p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL(k_bulk_copy, dim3(grid), dim3(256), 0, st, y, bufs, p, g.H);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,270 @@
+// Expert problem construction of the tile-signalling overlap paper
+// (sec. 3.2): the remote-owner-aligned row layout (sec. 3.2.1, Algorithm 1),
+// the remote-first row-band schedule (sec. 3.2.2), the combine plan
+// (sec. 3.2.3) and the transfer segments (sec. 3.3.2, Fig. 3(b)); then the
+// gather of every routed row into its packed position (the dispatch,
+// modelled on one GPU) and the zero fill of the padding rows.
+//
+// Layout: for each local expert, owner groups in ascending remote rank, the
+// local rank last; a remote group is padded with zero rows to a multiple of
+// tb_m; rows inside a group follow the owner's token order. Experts sit in
+// one buffer at tb_m-aligned bases. Band schedule: experts ordered by
+// (remote band count desc, remote rows desc, id asc), their remote bands in
+// layout order, then all local bands by expert id. Segments per (expert,
+// destination) group: 1 band, middle segments of mgb bands, 1 band.
+#include "common.hpp"
+
+namespace moe {
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int nseg_of(int nb, int mgb) {
+  return nb <= 2 ? nb : 2 + ceil_div(nb - 2, mgb);
+}
+
+constexpr int kPlanMaxEl = 256;
+constexpr int kPlanMaxGroups = 2048;  // E_l * R limit (checked on the host)
+
+// single workgroup: everything here is O(E_l * R) metadata
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ counts, moe_plan_t p,
+                                                int R, int El, int r_self, int tb, int mgb) {
+  __shared__ int s_cnt[kPlanMaxGroups];
+  __shared__ int s_rel[kPlanMaxGroups];      // group start relative to its expert base
+  __shared__ int s_bandoff[kPlanMaxGroups];  // first band index of the group (schedule order)
+  __shared__ int s_segoff[kPlanMaxGroups];   // first segment index (remote groups)
+  __shared__ int s_base[kPlanMaxEl + 1];
+  __shared__ int s_alg[kPlanMaxEl];          // tb-aligned rows of expert e
+  __shared__ int s_nrb[kPlanMaxEl], s_nrr[kPlanMaxEl], s_nlb[kPlanMaxEl], s_order[kPlanMaxEl];
+  const int tid = threadIdx.x;
+  const int G = El * R;
+  for (int i = tid; i < G; i += blockDim.x) s_cnt[i] = counts[i];
+  __syncthreads();
+
+  for (int e = tid; e < El; e += blockDim.x) {
+    int rel = 0, nrb = 0, nrr = 0;
+    for (int q = 0; q < R; ++q) {           // remote owners ascending, then the local owner
+      const int s = (q < R - 1) ? (q < r_self ? q : q + 1) : r_self;
+      const int c = s_cnt[e * R + s];
+      s_rel[e * R + s] = rel;
+      if (s != r_self) {
+        const int nb = ceil_div(c, tb);
+        rel += nb * tb;
+        nrb += nb;
+        nrr += c;
+      } else {
+        rel += c;
+      }
+    }
+    s_alg[e] = ceil_div(rel, tb) * tb;
+    s_nrb[e] = nrb;
+    s_nrr[e] = nrr;
+    s_nlb[e] = ceil_div(s_cnt[e * R + r_self], tb);
+  }
+  __syncthreads();
+  // rule (ii): rank of expert e under (remote bands desc, remote rows desc, id asc)
+  for (int e = tid; e < El; e += blockDim.x) {
+    int rank = 0;
+    for (int f = 0; f < El; ++f) {
+      const bool before = s_nrb[f] > s_nrb[e] ||
+                          (s_nrb[f] == s_nrb[e] && (s_nrr[f] > s_nrr[e] ||
+                                                    (s_nrr[f] == s_nrr[e] && f < e)));
+      rank += before ? 1 : 0;
+    }
+    s_order[rank] = e;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < El; ++e) { s_base[e] = acc; acc += s_alg[e]; }
+    s_base[El] = acc;
+    // remote bands: experts in rule-(ii) order, groups in layout order
+    int band = 0, seg = 0;
+    for (int o = 0; o < El; ++o) {
+      const int e = s_order[o];
+      for (int q = 0; q < R - 1; ++q) {
+        const int s = q < r_self ? q : q + 1;
+        const int nb = ceil_div(s_cnt[e * R + s], tb);
+        s_bandoff[e * R + s] = band;
+        s_segoff[e * R + s] = seg;
+        band += nb;
+        seg += nseg_of(nb, mgb);
+      }
+    }
+    const int n_remote = band;
+    for (int e = 0; e < El; ++e) {             // rule (i): local bands last, by expert id
+      s_bandoff[e * R + r_self] = band;
+      s_segoff[e * R + r_self] = -1;
+      band += s_nlb[e];
+    }
+    p.meta[META_MPAD] = acc;
+    p.meta[META_NBANDS] = band;
+    p.meta[META_NREMOTE] = n_remote;
+    p.meta[META_NSEG] = seg;
+    p.meta[META_STATUS] = 0;
+  }
+  __syncthreads();
+  for (int e = tid; e <= El; e += blockDim.x) p.expert_base[e] = s_base[e];
+  for (int s = tid; s < R; s += blockDim.x) {   // receive offsets: (expert, token) order
+    int acc = 0;
+    for (int e = 0; e < El; ++e) { p.recv_off[s * El + e] = acc; acc += s_cnt[e * R + s]; }
+  }
+  for (int i = tid; i < G; i += blockDim.x) {
+    const int e = i / R, s = i % R;
+    const int c = s_cnt[i];
+    const int row0 = s_base[e] + s_rel[i];
+    p.group_row[i] = row0;
+    const int nb = ceil_div(c, tb);
+    const int b0 = s_bandoff[i];
+    int recv0 = 0;
+    if (s != r_self) {
+      for (int f = 0; f < e; ++f) recv0 += s_cnt[f * R + s];
+    }
+    for (int j = 0; j < nb; ++j) {
+      const int b = b0 + j;
+      p.band_row0[b] = row0 + j * tb;
+      p.band_expert[b] = e;
+      p.band_dest[b] = s;
+      p.band_recv0[b] = (s != r_self) ? recv0 + j * tb : -1;
+      p.band_valid[b] = min(tb, c - j * tb);
+    }
+    if (s != r_self && nb > 0) {
+      int sidx = s_segoff[i];
+      int j = 0;
+      const int ns = nseg_of(nb, mgb);
+      for (int q = 0; q < ns; ++q) {
+        int sz;
+        if (q == 0 || q == ns - 1) sz = 1;
+        else sz = min(mgb, nb - 1 - j);
+        const int rows = min(c - j * tb, sz * tb);
+        p.seg_band0[sidx] = b0 + j;
+        p.seg_nbands[sidx] = sz;
+        p.seg_dest[sidx] = s;
+        p.seg_src_row[sidx] = row0 + j * tb;
+        p.seg_dst_row[sidx] = recv0 + j * tb;
+        p.seg_rows[sidx] = rows;
+        ++sidx;
+        j += sz;
+      }
+    }
+  }
+}
+
+// gather: every local (token, slot) -> its packed row; also row_src and recv_row.
+// One block per routing chunk (<= 256 tokens of one source rank); thread = token.
+// Rank inside the (expert, owner) group = rows of earlier chunks + rows of
+// earlier waves of this chunk + earlier lanes of this wave (ballot prefix).
+__global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ x,
+                                                 const int32_t* __restrict__ ids,
+                                                 uint16_t* __restrict__ x_perm, moe_plan_t p,
+                                                 int R, int T, int H, int k, int El,
+                                                 int first_local, int r_self,
+                                                 int chunks_per_rank) {
+  __shared__ int s_wcnt[4][kPlanMaxEl];
+  __shared__ int s_rows[kChunk * 16];
+  __shared__ int s_toks[kChunk * 16];
+  __shared__ int s_n;
+  const int chunk = blockIdx.x;
+  const int s = chunk / chunks_per_rank;
+  const int t0 = (chunk % chunks_per_rank) * kChunk;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t = t0 + tid;
+  const bool active = t < T;
+  const int g = s * T + (active ? t : 0);
+  int my[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) my[j] = (active && j < k) ? ids[g * k + j] - first_local : -1;
+  if (tid == 0) s_n = 0;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int e = 0; e < El; ++e) {
+    bool has = false;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) has |= (my[j] == e);
+    const uint64_t m = __ballot(has);
+    if (lane == 0) s_wcnt[wave][e] = __popcll(m);
+  }
+  __syncthreads();
+  for (int e = tid; e < El; e += blockDim.x) {   // exclusive prefix over the 4 waves
+    int acc = 0;
+    for (int w = 0; w < 4; ++w) { const int c = s_wcnt[w][e]; s_wcnt[w][e] = acc; acc += c; }
+  }
+  __syncthreads();
+  for (int e = 0; e < El; ++e) {
+    int slot = -1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) slot = (my[j] == e) ? j : slot;
+    const uint64_t m = __ballot(slot >= 0);
+    if (slot >= 0) {
+      const int rank = p.chunk_base[chunk * El + e] + s_wcnt[wave][e] + __popcll(m & lt);
+      const int row = p.group_row[e * R + s] + rank;
+      p.row_src[row] = g;
+      p.recv_row[g * k + slot] = (s == r_self) ? row : p.recv_off[s * El + e] + rank;
+      const int q = atomicAdd(&s_n, 1);
+      s_rows[q] = row;
+      s_toks[q] = g;
+    }
+  }
+  // slots whose expert is not local
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (active && j < k && (my[j] < 0 || my[j] >= El)) p.recv_row[g * k + j] = -1;
+  __syncthreads();
+  // copy rows: one wave per row, 16-byte vectors
+  const int n = s_n;
+  const int nv = H / 8;
+  for (int q = wave; q < n; q += 4) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(s_toks[q]) * H);
+    u32x4* dst = reinterpret_cast<u32x4*>(x_perm + static_cast<size_t>(s_rows[q]) * H);
+    for (int v = lane; v < nv; v += 64) dst[v] = src[v];
+  }
+}
+
+// zero rows: owner-boundary padding of remote groups and the gap after each expert
+__global__ __launch_bounds__(256) void k_padzero(uint16_t* __restrict__ x_perm,
+                                                  const int32_t* __restrict__ counts,
+                                                  moe_plan_t p, int R, int H, int El,
+                                                  int r_self, int tb) {
+  const int e = blockIdx.x;
+  const int nv = H / 8;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  // remote groups: rows [row0 + count, row0 + roundup(count))
+  for (int s = 0; s < R; ++s) {
+    const int c = counts[e * R + s];
+    int lo, hi;
+    if (s != r_self) {
+      lo = p.group_row[e * R + s] + c;
+      hi = p.group_row[e * R + s] + ceil_div(c, tb) * tb;
+    } else {
+      lo = p.group_row[e * R + s] + c;   // end of X_e
+      hi = p.expert_base[e + 1];         // next expert's aligned base
+    }
+    for (int r = lo; r < hi; ++r) {
+      if (threadIdx.x == 0) p.row_src[r] = -1;
+      u32x4* dst = reinterpret_cast<u32x4*>(x_perm + static_cast<size_t>(r) * H);
+      for (int v = threadIdx.x; v < nv; v += blockDim.x) dst[v] = z;
+    }
+  }
+}
+
+hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, counts, p, g.R, g.El, g.r_self, g.tb_m,
+                     g.mgb);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
+                         uint16_t* x_perm, const moe_plan_t& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_gather, dim3(g.n_chunks), dim3(256), 0, st, x, ids, x_perm, p, g.R, g.T,
+                     g.H, g.k, g.El, g.r_self * g.El, g.r_self, g.chunks_per_rank);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return hipSuccess;
+}
+
+hipError_t launch_padzero(const Geometry& g, uint16_t* x_perm, const int32_t* counts,
+                          const moe_plan_t& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_padzero, dim3(g.El), dim3(256), 0, st, x_perm, counts, p, g.R, g.H, g.El,
+                     g.r_self, g.tb_m);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,159 @@
+"""One EP rank's MoE-layer share on one GPU: buffer ownership + call order.
+
+MoEShare allocates every device buffer the C ABI needs for one shape and runs
+route -> permute -> (partition) -> expert forward (overlap or sequential) ->
+combine, all through the HIP library. PyTorch only provides device memory,
+streams and events.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _abi
+from . import ops
+
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bit patterns (numpy) -> bf16 device tensor with the same bits."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+@dataclasses.dataclass
+class ShareBuffers:
+    logits: torch.Tensor
+    x: torch.Tensor
+    w1: torch.Tensor
+    w3: Optional[torch.Tensor]
+    w2: torch.Tensor
+    topk_ids: torch.Tensor
+    gates: torch.Tensor
+    counts: torch.Tensor
+    ws: torch.Tensor
+    x_perm: torch.Tensor
+    h: torch.Tensor
+    y_perm: torch.Tensor
+    combine: list
+    flags: torch.Tensor
+    y_share: torch.Tensor
+
+
+class MoEShare:
+    """Buffers and launch sequence for rank r_self's share of one MoE layer."""
+
+    def __init__(self, R, T, H, F, E, k, gated, gate_kind, r_self=0, tb_m=128, mgb=1,
+                 device="cuda:0"):
+        self.device = torch.device(device)
+        self.shape = ops.make_shape(R, T, H, F, E, k, r_self, gated, gate_kind, tb_m, mgb)
+        self.sizes = ops.moe_query_sizes(self.shape)
+        self.R, self.T, self.H, self.F, self.E, self.k = R, T, H, F, E, k
+        self.El = E // R
+        self.r_self = r_self
+        self.gated = bool(gated)
+        self.ctx = ops.Context()
+        self.consumer_stream = torch.cuda.Stream(device=self.device)
+        self.epoch = 0
+        self.buf: Optional[ShareBuffers] = None
+
+    # ------------------------------------------------------------ buffers
+    def allocate(self, logits: torch.Tensor, x: torch.Tensor, w1, w3, w2) -> ShareBuffers:
+        d, s = self.device, self.sizes
+        R, T, H, F, k, El = self.R, self.T, self.H, self.F, self.k, self.El
+        mp = int(s.m_pad_max)
+        ws = torch.empty(int(s.ws_bytes) + 256, dtype=torch.uint8, device=d)
+        off = (-ws.data_ptr()) % 256
+        ws = ws[off:off + int(s.ws_bytes)]
+        combine = [None if q == self.r_self else
+                   torch.empty((max(1, s.recv_rows_max), H), dtype=torch.bfloat16, device=d)
+                   for q in range(R)]
+        self.buf = ShareBuffers(
+            logits=logits, x=x, w1=w1, w3=w3, w2=w2,
+            topk_ids=torch.empty((R * T, k), dtype=torch.int32, device=d),
+            gates=torch.empty((R * T, k), dtype=torch.float32, device=d),
+            counts=torch.empty((El, R), dtype=torch.int32, device=d),
+            ws=ws,
+            x_perm=torch.empty((mp, H), dtype=torch.bfloat16, device=d),
+            h=torch.empty((mp, F), dtype=torch.bfloat16, device=d),
+            y_perm=torch.empty((mp, H), dtype=torch.bfloat16, device=d),
+            combine=combine,
+            flags=torch.zeros(max(1, s.max_flags), dtype=torch.int32, device=d),
+            y_share=torch.empty((R, T, H), dtype=torch.bfloat16, device=d),
+        )
+        return self.buf
+
+    def set_routing(self, tb_m: Optional[int] = None, mgb: Optional[int] = None):
+        """Changes the band height / segment size (the buffers were sized for the
+        tb_m given at construction: only equal or smaller tb_m fit)."""
+        sh = self.shape
+        if tb_m is not None:
+            new = ops.make_shape(sh.R, sh.T, sh.H, sh.F, sh.E, sh.k, sh.r_self, sh.gated,
+                                 sh.gate_kind, tb_m, sh.mgb)
+            if ops.moe_query_sizes(new).ws_bytes > self.sizes.ws_bytes:
+                raise ValueError("buffers too small for this tb_m")
+            sh.tb_m = tb_m
+        if mgb is not None:
+            sh.mgb = mgb
+
+    # ------------------------------------------------------------ steps
+    def route(self, stream=None):
+        b = self.buf
+        ops.moe_route(self.shape, b.logits, b.topk_ids, b.gates, b.counts, b.ws, stream)
+
+    def permute(self, stream=None):
+        b = self.buf
+        ops.moe_permute(self.shape, b.x, b.topk_ids, b.counts, b.x_perm, b.ws, stream)
+
+    def partition(self, calib=None):
+        cnt = self.buf.counts.cpu().numpy()
+        return ops.moe_plan_partition(self.shape, cnt, calib)
+
+    def expert_forward(self, mode=_abi.MOE_MODE_OVERLAP, n_consumer_cu=8, stream=None):
+        b = self.buf
+        self.epoch = (self.epoch % 0xFFFFFFF0) + 1
+        ops.moe_expert_forward_overlap(self.ctx, self.shape, b.x_perm, b.w1, b.w3, b.w2, b.ws, b.h,
+                                       b.y_perm, b.combine, b.flags, self.epoch, n_consumer_cu,
+                                       mode, stream, self.consumer_stream)
+
+    def combine(self, stream=None):
+        b = self.buf
+        ops.moe_combine(self.shape, b.combine, b.y_perm, b.gates, b.ws, b.y_share, stream)
+
+    def forward(self, mode=_abi.MOE_MODE_OVERLAP, n_consumer_cu=8, stream=None):
+        self.route(stream)
+        self.permute(stream)
+        self.expert_forward(mode, n_consumer_cu, stream)
+        self.combine(stream)
+
+    def status(self, stream=None) -> int:
+        return ops.moe_read_status(self.shape, self.buf.ws, stream)
+
+    # ------------------------------------------------------------ inspection
+    def plan_arrays(self) -> dict:
+        """Copies the plan arrays of the workspace to host numpy arrays."""
+        torch.cuda.synchronize(self.device)
+        v = ops.moe_plan_view(self.shape, self.buf.ws)
+        base = self.buf.ws.data_ptr()
+        ws_i32 = self.buf.ws.view(torch.int32)
+
+        def arr(name, n):
+            o = (v[name] - base) // 4
+            return ws_i32[o:o + n].cpu().numpy().copy()
+        meta = arr("meta", 8)
+        m_pad, n_bands, n_remote, n_seg = (int(meta[i]) for i in range(4))
+        El, R = self.El, self.R
+        out = dict(meta=meta, m_pad=m_pad, n_bands=n_bands, n_remote=n_remote, n_seg=n_seg,
+                   status=int(meta[_abi.META_STATUS]))
+        out["group_row"] = arr("group_row", El * R).reshape(El, R)
+        out["expert_base"] = arr("expert_base", El + 1)
+        out["recv_off"] = arr("recv_off", R * El).reshape(R, El)
+        for f in ("band_row0", "band_expert", "band_dest", "band_recv0", "band_valid"):
+            out[f] = arr(f, n_bands)
+        for f in ("seg_band0", "seg_nbands", "seg_dest", "seg_src_row", "seg_dst_row", "seg_rows"):
+            out[f] = arr(f, n_seg)
+        out["row_src"] = arr("row_src", m_pad)
+        out["recv_row"] = arr("recv_row", self.R * self.T * self.k).reshape(self.R * self.T, self.k)
+        return out

@@ -1,0 +1,252 @@
+/*
+ * moe_overlap.h -- C ABI of the MI355X (gfx950) library for one
+ * expert-parallel rank's MoE-layer share with tile-signalled combine overlap.
+ *
+ * Method: "Fine-grained Computation-Communication Overlap via Tile-level
+ * Signaling and Scheduling for Mixture-of-Experts" (arXiv 2607.19539),
+ * cited as [TLS] below; the per-layer producer/consumer split follows the
+ * cost-model idea in the abstract of "Weave: Fine-Grained Dynamic SM
+ * Scheduling in an MoE Megakernel for Compute-Communication Overlap"
+ * (arXiv 2609.21483), cited as [Weave].
+ *
+ * One call sequence computes rank r_self's share of an MoE layer
+ * ([TLS] sec. 2.1, steps 1-5, with the two all-to-alls modelled on one GPU):
+ *
+ *   moe_route       top-k routing, gates, per-(local expert, source rank) counts
+ *   moe_plan_partition (optional, host) consumer CU count / segment size
+ *   moe_permute     remote-owner-aligned row layout, band schedule, combine
+ *                   plan, transfer segments, gather of the routed rows
+ *   moe_expert_forward_overlap
+ *                   expert FFN as a persistent grouped GEMM; its output
+ *                   projection raises one ready flag per tile while a
+ *                   consumer kernel on a few CUs copies each ready segment
+ *                   into its source rank's combine buffer
+ *   moe_combine     gate-weighted reduction of the returned rows
+ *
+ * Conventions
+ *  - Every tensor argument is a DEVICE pointer allocated and owned by the
+ *    caller; the library never allocates device memory on these paths and
+ *    never frees caller memory. bf16 tensors are passed as uint16_t bit
+ *    patterns; all matrices are row-major and densely packed.
+ *  - Every call except moe_query_sizes, moe_plan_partition, moe_error_string
+ *    and moe_ctx_* only enqueues work on the given HIP stream (passed as
+ *    void*, NULL = the default stream) and returns without synchronising.
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code. Argument and
+ *    shape errors are detected on the host before any HIP call.
+ *  - No global state: everything persistent lives in caller memory (the
+ *    workspace) or in a moe_ctx_t.
+ */
+#ifndef MOE_OVERLAP_H
+#define MOE_OVERLAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG (-1)  /* null pointer, bad size, inconsistent shape  */
+#define MOE_ERR_UNSUPPORTED (-2)  /* shape/tile outside the compiled tile table  */
+#define MOE_ERR_WORKSPACE   (-3)  /* workspace pointer misaligned                */
+#define MOE_ERR_HIP         (-4)  /* a HIP runtime call failed                   */
+#define MOE_ERR_TIMEOUT     (-5)  /* device watchdog: a flag wait exceeded budget */
+#define MOE_ERR_DEVICE      (-6)  /* device-side consistency check failed         */
+
+#define MOE_MAX_RANKS 16          /* R limit: combine buffer pointers go by value */
+
+enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 };
+enum { MOE_MODE_OVERLAP = 0, MOE_MODE_SEQUENTIAL = 1 };
+
+/* Problem shape of one rank's share ([TLS] sec. 3.2, Algorithm 1 inputs).
+ *  R        simulated ranks (1..MOE_MAX_RANKS)
+ *  T        tokens per rank (>= 1)
+ *  H        hidden size (multiple of 256)
+ *  F        expert FFN width (multiple of 128)
+ *  E        experts in total; E % R == 0; rank r owns experts [r*E/R, (r+1)*E/R)
+ *  k        top-k, 1 <= k <= min(E, 16)
+ *  r_self   the rank whose share is computed, 0 <= r_self < R
+ *  gated    1: y = (SiLU(x W1^T) * (x W3^T)) W2^T;  0: y = SiLU(x W1^T) W2^T
+ *  gate_kind MOE_GATE_SOFTMAX: softmax over the k selected logits;
+ *           MOE_GATE_SIGMOID: sigmoid of the k selected logits, normalised to sum 1
+ *  tb_m     GEMM tile height = row-band height ([TLS] sec. 3.2.1): 64, 128 or 256
+ *  mgb      row bands per middle transfer segment ([TLS] sec. 3.3.2, Fig. 3(b)), >= 1
+ */
+typedef struct {
+  int32_t R, T, H, F, E, k, r_self;
+  int32_t gated, gate_kind;
+  int32_t tb_m, mgb;
+} moe_shape_t;
+
+/* Buffer sizes for a shape. Rows of x_perm / h / y_perm are bounded by
+ * m_pad_max = min(R*T*k, R*T*E/R) + (E/R)*R*(tb_m-1) (each remote owner group is
+ * padded by < tb_m rows and each expert's rows are placed tb_m-aligned). */
+typedef struct {
+  size_t  ws_bytes;       /* workspace bytes (256-byte aligned pointer required) */
+  int64_t m_pad_max;      /* rows to allocate for x_perm [.,H], h [.,F], y_perm [.,H] */
+  int32_t max_bands;      /* = m_pad_max / tb_m */
+  int32_t max_flags;      /* uint32 ready flags the overlapped forward may write */
+  int32_t recv_rows_max;  /* rows to allocate per combine buffer: T*min(k, E/R) */
+  int32_t bn_out;         /* tile width of the output projection (flags per band) */
+} moe_sizes_t;
+
+/* Read-only device views into a workspace after moe_permute (for inspection
+ * and tests). Arrays indexed by band / segment are in schedule order. */
+typedef struct {
+  int32_t* meta;          /* [0]=m_pad [1]=n_bands [2]=n_remote_bands [3]=n_segments
+                             [4]=device status (0 or MOE_ERR_*)                      */
+  int32_t* group_row;     /* [E_l*R] first packed row of group (e, s)                */
+  int32_t* expert_base;   /* [E_l+1] first packed row of expert e, tb_m-aligned      */
+  int32_t* recv_off;      /* [R*E_l] first row of (e, s) in rank s's combine buffer */
+  int32_t* band_row0;     /* [max_bands] first packed row of the band                */
+  int32_t* band_expert;   /* [max_bands] local expert                                 */
+  int32_t* band_dest;     /* [max_bands] owner rank (r_self for local bands)          */
+  int32_t* band_recv0;    /* [max_bands] first combine-buffer row, -1 if local        */
+  int32_t* band_valid;    /* [max_bands] non-padding rows                             */
+  int32_t* seg_band0;     /* [max_bands] first band (schedule index) of the segment   */
+  int32_t* seg_nbands;    /* [max_bands]                                              */
+  int32_t* seg_dest;      /* [max_bands]                                              */
+  int32_t* seg_src_row;   /* [max_bands] first y_perm row                             */
+  int32_t* seg_dst_row;   /* [max_bands] first combine-buffer row                     */
+  int32_t* seg_rows;      /* [max_bands] valid rows copied                            */
+  int32_t* row_src;       /* [m_pad_max] token s*T+t of each packed row, -1 = zero row */
+  int32_t* recv_row;      /* [R*T*k] combine-buffer row (s != r_self) or y_perm row
+                             (s == r_self) of slot j of token g; -1 if not local      */
+  int32_t* chunk_base;    /* [n_chunks*E_l] internal: per-chunk row offsets           */
+  int32_t* chunk_counts;  /* [n_chunks*E_l] internal: per-chunk local counts          */
+} moe_plan_t;
+
+/* Calibration of the partition cost model (measured on the device). */
+typedef struct {
+  double gemm_flops_per_cu;   /* sustained bf16 FLOP/s of one producer CU, large M */
+  double gemm_m_half;         /* rows per expert at which GEMM efficiency halves    */
+  double copy_bw_per_cu;      /* bytes/s one consumer CU moves (large segments)     */
+  double copy_bw_max;         /* bytes/s ceiling of the copy (HBM)                  */
+  double seg_latency_s;       /* fixed cost per transfer segment, seconds           */
+  int32_t n_cu;               /* CUs on the device (256 on MI355X)                  */
+  int32_t c_min, c_max;       /* consumer CU range considered                       */
+} moe_calib_t;
+
+typedef struct moe_ctx moe_ctx_t;
+
+/* Human-readable name of an MOE_* code (static string, never NULL). */
+const char* moe_error_string(int code);
+
+/* Validates the shape and reports buffer sizes. Host only; no HIP call. */
+int moe_query_sizes(const moe_shape_t* shape, moe_sizes_t* out);
+
+/* Fills device views into a workspace of ws_bytes at ws. Host only. */
+int moe_plan_view(const moe_shape_t* shape, void* ws, moe_plan_t* out);
+
+/* Creates a context for the current HIP device: two events used to order the
+ * producer and consumer streams, and the device's CU count. Returns MOE_OK and
+ * sets *out, or MOE_ERR_HIP. Destroy with moe_ctx_destroy. */
+int moe_ctx_create(moe_ctx_t** out);
+int moe_ctx_destroy(moe_ctx_t* ctx);
+int moe_ctx_num_cus(const moe_ctx_t* ctx);
+
+/* Phase timing of moe_expert_forward_overlap with HIP events recorded on the
+ * streams the kernels run on (off by default; enabling creates 5 events).
+ * moe_ctx_timings waits for the last timed call and writes, in ms:
+ *   ms[0] first projection (all CUs)
+ *   ms[1] output projection (producer) from its start to its end
+ *   ms[2] from the output projection's start to the consumer's end
+ *         (SEQUENTIAL: to the end of the bulk copy)
+ *   ms[3] whole call
+ *   ms[4] exposed transfer: consumer end minus producer end, >= 0
+ *         (SEQUENTIAL: the bulk copy's duration)
+ * Returns MOE_ERR_INVALID_ARG if timing is off or nothing was timed. */
+int moe_ctx_set_timing(moe_ctx_t* ctx, int enable);
+int moe_ctx_timings(moe_ctx_t* ctx, float* ms);
+
+/* Step 1, routing ([TLS] sec. 2.1 step 1). Per token g of R*T (g = s*T + t):
+ * the k experts with the highest logits, highest first, equal logits to the
+ * lower expert id; gates per gate_kind (they sum to 1).
+ *   logits   [R*T, E] fp32 (in)
+ *   topk_ids [R*T, k] int32 global expert ids (out)
+ *   gates    [R*T, k] fp32 (out)
+ *   counts   [E_l, R] int32 (out): count[e][s] = slots of rank s's tokens
+ *            routed to local expert r_self*E_l + e (the rows the dispatch delivers)
+ *   ws       workspace (per-chunk counts are left there for moe_permute) */
+int moe_route(const moe_shape_t* shape, const float* logits, int32_t* topk_ids,
+              float* gates, int32_t* counts, void* ws, void* stream);
+
+/* Steps 3-4: remote-owner-aligned row layout, remote-first band schedule and
+ * combine plan ([TLS] sec. 3.2.1-3.2.3, Algorithm 1), transfer segments
+ * ([TLS] sec. 3.3.2, Fig. 3(b)), and the gather of the routed rows (the
+ * dispatch, modelled locally).
+ *   x       [R, T, H] bf16: every rank's tokens (in)
+ *   topk_ids, counts: from moe_route (in)
+ *   x_perm  [m_pad_max, H] bf16 (out): row i = x of token row_src[i]; zero
+ *           rows for owner-boundary padding and between experts. Rows beyond
+ *           m_pad are not written.
+ *   ws      workspace: plan arrays written (see moe_plan_t). */
+int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_ids,
+                const int32_t* counts, uint16_t* x_perm, void* ws, void* stream);
+
+/* Picks the consumer CU count c (and segment size) for one layer from the
+ * routing counts ([Weave] abstract: split compute/communication workers to
+ * match the layer's communication/computation ratio; [TLS] sec. 4.3.4 on the
+ * cost of a wrong split). Host-only pure function.
+ *   counts_host [E_l, R] int32 (host memory)
+ *   calib       NULL = built-in MI355X defaults
+ *   n_consumer_cu (out) c in [calib->c_min, calib->c_max]
+ *   mgb         (out, may be NULL) bands per middle segment
+ *   predicted_s (out, may be NULL) model time of the overlapped expert phase */
+int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
+                       const moe_calib_t* calib, int32_t* n_consumer_cu, int32_t* mgb,
+                       double* predicted_s);
+
+/* Step 3+4: expert FFN + combine transfer ([TLS] sec. 3.3).
+ *   x_perm   [m_pad_max, H] bf16 from moe_permute
+ *   w1, w3   [E_l, F, H] bf16 (nn.Linear [out, in]); w3 NULL iff !gated
+ *   w2       [E_l, H, F] bf16
+ *   h        [m_pad_max, F] bf16 scratch (the activated first projection)
+ *   y_perm   [m_pad_max, H] bf16 (out): expert outputs in packed row order
+ *   combine_buf host array of R device pointers; combine_buf[s] for s != r_self
+ *            is [recv_rows_max, H] bf16 (out): rows returned to rank s;
+ *            combine_buf[r_self] is ignored (may be NULL)
+ *   flags    [max_flags] uint32, zero-initialised once by the caller and then
+ *            reused: tile t is ready when flags[t] == epoch
+ *   epoch    nonzero, different from the previous call's epoch on these flags
+ *   n_consumer_cu  c, 1..64 and < device CUs (ignored in SEQUENTIAL mode)
+ *   mode     MOE_MODE_OVERLAP: first projection on all CUs; then the output
+ *            projection on (CUs - c) persistent workgroups raising a flag per
+ *            tile, concurrently with the consumer on c workgroups that copies
+ *            every segment once all its tiles are flagged.
+ *            MOE_MODE_SEQUENTIAL (baseline, [TLS] sec. 4.1.3): both projections
+ *            on all CUs, then one bulk copy of all remote rows on all CUs.
+ *   producer_stream  all work is ordered after prior work on this stream and
+ *            completes before later work on it (the consumer is joined back)
+ *   consumer_stream  second stream for the consumer (OVERLAP only; must differ
+ *            from producer_stream)
+ * Calls that overlap in time on the same flags/workspace race. */
+int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape,
+                               const uint16_t* x_perm, const uint16_t* w1,
+                               const uint16_t* w3, const uint16_t* w2, void* ws,
+                               uint16_t* h, uint16_t* y_perm, uint16_t* const* combine_buf,
+                               uint32_t* flags, uint32_t epoch, int32_t n_consumer_cu,
+                               int32_t mode, void* producer_stream, void* consumer_stream);
+
+/* Step 5, weighted reduction ([TLS] sec. 2.1 step 5): for every token (s, t),
+ * y_share[s, t] = sum over slots j ascending whose expert is local of
+ * gates[s*T+t, j] * row, with row = combine_buf[s][recv_row] for s != r_self
+ * and y_perm[recv_row] for s == r_self; fp32 accumulation, bf16 (RNE) out;
+ * zero when no slot is local.
+ *   combine_buf host array of R device pointers (as above)
+ *   y_perm   [m_pad_max, H] bf16, gates [R*T, k] fp32
+ *   y_share  [R, T, H] bf16 (out) */
+int moe_combine(const moe_shape_t* shape, uint16_t* const* combine_buf,
+                const uint16_t* y_perm, const float* gates, void* ws,
+                uint16_t* y_share, void* stream);
+
+/* Copies the device status word of the workspace to *status (host) and
+ * synchronises the stream. Returns *status (MOE_OK, MOE_ERR_TIMEOUT, ...)
+ * or MOE_ERR_HIP. */
+int moe_read_status(const moe_shape_t* shape, void* ws, int32_t* status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_OVERLAP_H */

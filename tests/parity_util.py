@@ -1,0 +1,90 @@
+"""Helpers for GPU-vs-oracle parity tests (imported by the -m gpu tests only)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from oracle import moe_share as om
+from synth import Workload, make_share_inputs
+
+# Tolerance for floating-point outputs (bf16 storage, fp32 accumulation):
+# per-token relative distance ||y - y_ref|| / ||y_ref|| and mean absolute
+# error against the bf16-rounded reference.
+REL_TOL = 2e-2
+MEAN_ABS_TOL = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to even), returned as float64."""
+    f = np.asarray(a, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def widen(t) -> np.ndarray:
+    """bf16 torch tensor -> float64 numpy (exact)."""
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).__lshift__(16) \
+        .view(np.float32).astype(np.float64)
+
+
+def bits(t) -> np.ndarray:
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_rows(got: np.ndarray, ref: np.ndarray, what: str):
+    """Per-row relative distance and mean abs error vs bf16(ref)."""
+    got = got.reshape(-1, got.shape[-1])
+    ref = ref.reshape(-1, ref.shape[-1])
+    nr = np.linalg.norm(ref, axis=1)
+    zero = nr == 0
+    assert np.all(got[zero] == 0), f"{what}: rows with zero reference are not exactly zero"
+    rel = np.linalg.norm(got - ref, axis=1)[~zero] / nr[~zero]
+    mae = float(np.mean(np.abs(got - bf16_round(ref))))
+    mx = float(rel.max()) if rel.size else 0.0
+    say(f"  {what}: max per-row rel {mx:.3e}, mean abs err {mae:.3e}")
+    assert mx <= REL_TOL, f"{what}: max per-row relative distance {mx} > {REL_TOL}"
+    assert mae <= MEAN_ABS_TOL, f"{what}: mean abs err {mae} > {MEAN_ABS_TOL}"
+    return mx, mae
+
+
+def make_gpu_share(w: Workload, r_self: int, tb_m: int, mgb: int, inp=None, device="cuda:0"):
+    import torch
+    from combine_overlap_amd.share import MoEShare, bf16_tensor
+    if inp is None:
+        inp = make_share_inputs(w, r_self)
+    sh = MoEShare(w.R, w.T, w.H, w.F, w.E, w.k, w.gated, w.gate_kind, r_self=r_self, tb_m=tb_m,
+                  mgb=mgb, device=device)
+    d = sh.device
+    sh.allocate(torch.from_numpy(inp.logits).to(d), bf16_tensor(inp.x, d), bf16_tensor(inp.W1, d),
+                bf16_tensor(inp.W3, d) if inp.W3 is not None else None, bf16_tensor(inp.W2, d))
+    return sh, inp
+
+
+def oracle_plan_arrays(res: om.ShareResult) -> dict:
+    lay, b, sg = res.layout, res.bands, res.segs
+    return dict(
+        m_pad=lay.m_pad, n_bands=len(b.row0), n_remote=b.n_remote, n_seg=len(sg.band0),
+        group_row=lay.group_row, expert_base=lay.expert_base, recv_off=lay.recv_off,
+        band_row0=b.row0, band_expert=b.expert, band_dest=b.dest, band_recv0=b.recv0,
+        band_valid=b.valid, seg_band0=sg.band0, seg_nbands=sg.nbands, seg_dest=sg.dest,
+        seg_src_row=sg.src_row, seg_dst_row=sg.dst_row, seg_rows=sg.rows,
+        row_src=lay.row_src, recv_row=lay.recv_row)
+
+
+def assert_plan_equal(got: dict, want: dict):
+    for key, v in want.items():
+        g = got[key]
+        if np.isscalar(v) or isinstance(v, int):
+            assert int(g) == int(v), f"{key}: {g} != {v}"
+        else:
+            g = np.asarray(g).reshape(np.shape(v))
+            assert np.array_equal(g, np.asarray(v)), f"plan field {key} differs"

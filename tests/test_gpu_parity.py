@@ -1,0 +1,128 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer work (routing ids, counts, layout, schedule, plan, segments, row
+maps) and byte copies (x_perm, combine buffers) must match bit-exactly;
+floating-point outputs must satisfy the per-row relative distance and mean
+absolute error bounds of parity_util.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_share as om
+from synth import Workload, WORKLOADS, make_share_inputs
+from parity_util import (assert_plan_equal, bits, check_rows, make_gpu_share, oracle_plan_arrays,
+                         say, widen)
+
+pytestmark = pytest.mark.gpu
+
+# (id, workload, r_self, tb_m, mgb, consumer CUs, layer)
+CASES = [
+    ("tiny_full_tb64", WORKLOADS[1], 0, 64, 1, 4, 0),
+    ("tiny_full_tb128_r2", WORKLOADS[1], 2, 128, 2, 2, 0),
+    ("mixtral_mini_tb128", Workload("mixtral_mini", 4, 512, 1024, 2048, 8, 2, True, "softmax",
+                                    "normal", w_std="fan_in"), 0, 128, 1, 8, 0),
+    ("zipf_mini_tb256", Workload("zipf_mini", 4, 512, 1024, 1024, 8, 2, True, "softmax", "zipf",
+                                 w_std="fan_in"), 0, 256, 2, 8, 0),
+    ("fine_mini_tb64", Workload("fine_mini", 8, 256, 512, 256, 64, 8, True, "sigmoid"), 3, 64, 1, 16, 0),
+    ("dyn_mini_tb64_l2", Workload("dyn_mini", 4, 512, 512, 384, 32, 8, True, "softmax", "layered",
+                                  layers=16), 0, 64, 2, 6, 2),
+    ("ragged_T300_R3", Workload("ragged", 3, 300, 256, 128, 6, 3, True, "softmax"), 1, 64, 1, 3, 0),
+    ("single_rank", Workload("single", 1, 100, 256, 256, 4, 2, False, "softmax"), 0, 64, 1, 2, 0),
+    ("k_equals_E", Workload("kE", 2, 64, 256, 128, 4, 4, True, "sigmoid"), 1, 128, 1, 2, 0),
+]
+
+
+def _inputs(w, r_self, layer):
+    from synth import make_logits, make_x, make_local_weights
+    from synth.workloads import ShareInputs
+    W1, W3, W2 = make_local_weights(w, r_self)
+    return ShareInputs(w, r_self, make_logits(w, layer), make_x(w), W1, W3, W2)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_share_parity(case):
+    import torch
+    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL
+    name, w, r_self, tb, mgb, c, layer = case
+    say(f"[parity] {name}: R={w.R} T={w.T} H={w.H} F={w.F} E={w.E} k={w.k} r_self={r_self} "
+        f"tb_m={tb} mgb={mgb} c={c}")
+    inp = _inputs(w, r_self, layer)
+    ref = om.oracle_share(inp.logits, inp.x, inp.W1, inp.W3, inp.W2, R=w.R, T=w.T, E=w.E, k=w.k,
+                          gate_kind=w.gate_kind, r_self=r_self, tb_m=tb, mgb=mgb)
+    sh, _ = make_gpu_share(w, r_self, tb, mgb, inp)
+    b = sh.buf
+
+    # step 1: routing
+    sh.route()
+    torch.cuda.synchronize()
+    assert np.array_equal(b.topk_ids.cpu().numpy(), ref.ids), "topk ids differ"
+    assert np.array_equal(b.counts.cpu().numpy(), ref.layout.counts), "counts differ"
+    g = b.gates.cpu().numpy().astype(np.float64)
+    assert np.allclose(g, ref.gates, rtol=2e-6, atol=1e-7), f"gates differ {np.abs(g - ref.gates).max()}"
+
+    # steps 3-4: layout, schedule, plan, segments, gather
+    sh.permute()
+    plan = sh.plan_arrays()
+    assert plan["status"] == 0
+    assert_plan_equal(plan, oracle_plan_arrays(ref))
+    m_pad = plan["m_pad"]
+    assert np.array_equal(widen(b.x_perm[:m_pad]), ref.x_perm), "x_perm differs"
+
+    # expert FFN + overlapped transfer
+    for s in range(w.R):
+        if b.combine[s] is not None:
+            b.combine[s].fill_(float("nan"))
+    b.y_perm.fill_(float("nan"))
+    sh.expert_forward(MOE_MODE_OVERLAP, n_consumer_cu=c)
+    torch.cuda.synchronize()
+    assert sh.status() == 0
+    y_gpu = widen(b.y_perm[:m_pad])
+    check_rows(y_gpu, ref.y_perm, f"{name} y_perm")
+    y_bits = bits(b.y_perm[:m_pad])
+    comb = {s: bits(b.combine[s]) for s in range(w.R) if s != r_self}
+    for i in range(len(ref.bands.row0)):
+        if i >= ref.bands.n_remote:
+            break
+        s, r0, rc, n = (int(ref.bands.dest[i]), int(ref.bands.row0[i]), int(ref.bands.recv0[i]),
+                        int(ref.bands.valid[i]))
+        assert np.array_equal(comb[s][rc:rc + n], y_bits[r0:r0 + n]), f"combine buf band {i} differs"
+    for s in comb:
+        check_rows(widen(b.combine[s][:int(ref.layout.recv_rows[s])]), ref.bufs[s], f"{name} combine[{s}]")
+
+    # weighted reduction
+    sh.combine()
+    torch.cuda.synchronize()
+    y_share_ovl = bits(b.y_share).copy()
+    check_rows(widen(b.y_share), ref.y_share, f"{name} y_share")
+
+    # the non-overlapped baseline gives bit-identical results
+    for s in range(w.R):
+        if b.combine[s] is not None:
+            b.combine[s].fill_(float("nan"))
+    sh.expert_forward(MOE_MODE_SEQUENTIAL)
+    sh.combine()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits), "sequential y_perm differs from overlap"
+    assert np.array_equal(bits(b.y_share), y_share_ovl), "sequential y_share differs from overlap"
+
+
+def test_repeated_overlap_calls_are_deterministic():
+    import torch
+    from combine_overlap_amd import MOE_MODE_OVERLAP
+    w = Workload("rep", 4, 512, 1024, 1024, 8, 2, True, "softmax", "zipf", w_std="fan_in")
+    say("[parity] repeated overlap calls, epochs 1..6, c in 1,2,4,8,16,32")
+    sh, inp = make_gpu_share(w, 0, 128, 1)
+    sh.route()
+    sh.permute()
+    outs = []
+    for c in (1, 2, 4, 8, 16, 32):
+        for s in range(w.R):
+            if sh.buf.combine[s] is not None:
+                sh.buf.combine[s].fill_(float("nan"))
+        sh.expert_forward(MOE_MODE_OVERLAP, n_consumer_cu=c)
+        sh.combine()
+        torch.cuda.synchronize()
+        assert sh.status() == 0
+        outs.append(bits(sh.buf.y_share).copy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
