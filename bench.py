@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--tb", type=int, default=0, help="band height (0 = per-workload default)")
     ap.add_argument("--c", type=int, default=0, help="consumer CUs (0 = cost model)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sequential-only", action="store_true",
+                    help="run only the non-overlapped path (for counter collection, which "
+                         "serialises kernels and so cannot run the concurrent consumer)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
 
