@@ -113,19 +113,13 @@ def main():
     log(f"[bench] device CUs {n_cu}; buffers ready")
 
     def step(mode):
-        sh.route()
-        c, mgb, _ = sh.partition()
-        if args.c:
-            c = args.c
-        sh.shape.mgb = mgb
-        sh.permute()
-        sh.expert_forward(mode, n_consumer_cu=c)
-        sh.combine()
-        return c, mgb
+        c = sh.layer(mode, n_consumer_cu=args.c or None)
+        return c, sh.shape.mgb
 
+    main_mode = MOE_MODE_SEQUENTIAL if args.sequential_only else MOE_MODE_OVERLAP
     # warmup + sanity
     for _ in range(max(1, args.warmup)):
-        c_used, mgb_used = step(MOE_MODE_OVERLAP)
+        c_used, mgb_used = step(main_mode)
     torch.cuda.synchronize()
     if sh.status() != 0:
         raise RuntimeError(f"device status {sh.status()} after warmup")
@@ -148,17 +142,20 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / k
 
-    t_ovl = timed(MOE_MODE_OVERLAP, args.steps)
-    log(f"[bench] overlap layer step {t_ovl * 1e3:.3f} ms")
-    for _ in range(args.warmup):
-        step(MOE_MODE_SEQUENTIAL)
+    t_ovl = None
+    if not args.sequential_only:
+        t_ovl = timed(MOE_MODE_OVERLAP, args.steps)
+        log(f"[bench] overlap layer step {t_ovl * 1e3:.3f} ms")
+        for _ in range(args.warmup):
+            step(MOE_MODE_SEQUENTIAL)
     t_seq = timed(MOE_MODE_SEQUENTIAL, args.steps)
     log(f"[bench] sequential layer step {t_seq * 1e3:.3f} ms")
 
     # per-phase device timings (HIP events on the kernels' own streams)
     sh.ctx.set_timing(True)
-    ph = {MOE_MODE_OVERLAP: [], MOE_MODE_SEQUENTIAL: []}
-    for mode in (MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL):
+    modes = (MOE_MODE_SEQUENTIAL,) if args.sequential_only else (MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL)
+    ph = {m: [] for m in modes}
+    for mode in modes:
         for _ in range(max(3, args.steps)):
             sh.expert_forward(mode, n_consumer_cu=c_used)
             ph[mode].append(sh.ctx.timings())
@@ -166,18 +163,24 @@ def main():
 
     def med(mode, key):
         return float(np.median([d[key] for d in ph[mode]]))
-    g1 = med(MOE_MODE_OVERLAP, "gemm1")
-    prod = med(MOE_MODE_OVERLAP, "producer")
-    ovl_total = med(MOE_MODE_OVERLAP, "total")
-    exposed = med(MOE_MODE_OVERLAP, "exposed")
+    seq_g1 = med(MOE_MODE_SEQUENTIAL, "gemm1")
     seq_g2 = med(MOE_MODE_SEQUENTIAL, "producer")
     seq_copy = med(MOE_MODE_SEQUENTIAL, "exposed")
     seq_total = med(MOE_MODE_SEQUENTIAL, "total")
-    log(f"[bench] overlap: gemm1 {g1:.3f} ms, producer {prod:.3f} ms, expert phase {ovl_total:.3f} ms, "
-        f"exposed copy {exposed * 1e3:.1f} us")
-    log(f"[bench] sequential: gemm2 {seq_g2:.3f} ms, bulk copy {seq_copy * 1e3:.1f} us, "
-        f"expert phase {seq_total:.3f} ms")
+    log(f"[bench] sequential: gemm1 {seq_g1:.3f} ms, gemm2 {seq_g2:.3f} ms, bulk copy "
+        f"{seq_copy * 1e3:.1f} us, expert phase {seq_total:.3f} ms")
+    if args.sequential_only:
+        g1, prod, ovl_total, exposed, t_main = seq_g1, seq_g2, seq_total, seq_copy, t_seq
+    else:
+        g1 = med(MOE_MODE_OVERLAP, "gemm1")
+        prod = med(MOE_MODE_OVERLAP, "producer")
+        ovl_total = med(MOE_MODE_OVERLAP, "total")
+        exposed = med(MOE_MODE_OVERLAP, "exposed")
+        t_main = t_ovl
+        log(f"[bench] overlap: gemm1 {g1:.3f} ms, producer {prod:.3f} ms, expert phase "
+            f"{ovl_total:.3f} ms, exposed copy {exposed * 1e3:.1f} us")
     ach1 = flops1 / (g1 * 1e-3) / 1e12
+    t_ovl = t_main
 
     out = {
         "metric": "MoE-layer TFLOP/s per EP rank (overlapped combine), % of bf16 MFMA peak",

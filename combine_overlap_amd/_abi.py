@@ -40,7 +40,7 @@ class MoeSizes(C.Structure):
 PLAN_FIELDS = ("meta", "group_row", "expert_base", "recv_off", "band_row0", "band_expert",
                "band_dest", "band_recv0", "band_valid", "seg_band0", "seg_nbands", "seg_dest",
                "seg_src_row", "seg_dst_row", "seg_rows", "row_src", "recv_row", "chunk_base",
-               "chunk_counts")
+               "chunk_counts", "tile_ctr", "slot_valid")
 
 
 class MoePlan(C.Structure):
@@ -55,7 +55,7 @@ class MoeCalib(C.Structure):
 
 
 EXPORTS = ("moe_error_string", "moe_query_sizes", "moe_plan_view", "moe_ctx_create",
-           "moe_ctx_destroy", "moe_ctx_num_cus", "moe_ctx_set_timing", "moe_ctx_timings", "moe_route", "moe_permute",
+           "moe_ctx_destroy", "moe_ctx_num_cus", "moe_ctx_set_timing", "moe_ctx_timings", "moe_ctx_set_trace", "moe_route", "moe_permute",
            "moe_plan_partition", "moe_expert_forward_overlap", "moe_combine", "moe_read_status")
 
 _lib = None
@@ -80,6 +80,7 @@ def lib() -> C.CDLL:
     L.moe_ctx_num_cus.argtypes = [vp]
     L.moe_ctx_set_timing.argtypes = [vp, C.c_int]
     L.moe_ctx_timings.argtypes = [vp, C.POINTER(C.c_float)]
+    L.moe_ctx_set_trace.argtypes = [vp, pshape, vp, C.c_int64]
     L.moe_route.argtypes = [pshape, vp, vp, vp, vp, vp, vp]
     L.moe_permute.argtypes = [pshape, vp, vp, vp, vp, vp, vp]
     L.moe_plan_partition.argtypes = [pshape, pi32, C.POINTER(MoeCalib), pi32, pi32,

@@ -36,37 +36,47 @@ def _run(cmd):
     return r.returncode, out
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 8, defines=(), out: str = OUT, build_dir: str = BUILD) -> str:
+    """Compiles and links the library; `defines` are extra -D flags (e.g. for
+    tuning variants built to another `out` path)."""
+    os.makedirs(build_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     cmds = []
     objs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        cmds.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src + ".o")
+        cmds.append([HIPCC, *HIP_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        cmds.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src + ".o")
+        cmds.append(["g++", *CXX_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(_run, cmds))
     failed = False
-    for cmd, (rc, out) in zip(cmds, results):
-        if out.strip() and (verbose or rc != 0):
-            print(out, file=sys.stderr)
+    for cmd, (rc, log) in zip(cmds, results):
+        if log.strip() and (verbose or rc != 0):
+            print(log, file=sys.stderr)
         if rc != 0:
             failed = True
             print(f"FAILED: {' '.join(cmd)}", file=sys.stderr)
     if failed:
         raise RuntimeError("HIP build failed")
-    tmp = OUT + ".tmp"
-    rc, out = _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    tmp = out + ".tmp"
+    rc, log = _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     if rc != 0:
-        print(out, file=sys.stderr)
+        print(log, file=sys.stderr)
         raise RuntimeError("link failed")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("-D", action="append", default=[], help="extra preprocessor define")
+    ap.add_argument("--out", default=OUT)
+    ap.add_argument("--build-dir", default=BUILD)
+    a = ap.parse_args()
+    print(build(verbose=a.v, defines=a.D, out=a.out, build_dir=a.build_dir))

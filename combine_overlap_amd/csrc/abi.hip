@@ -13,6 +13,8 @@ struct moe_ctx {
   int timed;                // a timed call has been enqueued
   int timed_mode;
   hipEvent_t tev[5];        // start, first projection end, producer end, consumer end, join
+  uint64_t* trace;          // device timeline (see moe_ctx_set_trace) or null
+  int32_t trace_flags;      // max_flags of the shape the trace was sized for
 };
 
 namespace moe {
@@ -83,6 +85,8 @@ WsLayout ws_layout(const Geometry& g) {
   L.seg_src_row = take(mb); L.seg_dst_row = take(mb); L.seg_rows = take(mb);
   L.row_src = take((size_t)g.m_pad_max);
   L.recv_row = take((size_t)g.R * g.T * g.k);
+  L.tile_ctr = take(kCtrWords);
+  L.slot_valid = take(mb);
   L.total = off;
   return L;
 }
@@ -103,6 +107,8 @@ void plan_from_ws(const Geometry& g, void* ws, moe_plan_t* p) {
   p->recv_row = at(L.recv_row);
   p->chunk_base = at(L.chunk_base);
   p->chunk_counts = at(L.chunk_counts);
+  p->tile_ctr = at(L.tile_ctr);
+  p->slot_valid = at(L.slot_valid);
 }
 
 static inline bool ws_ok(const void* ws) {
@@ -160,6 +166,8 @@ int moe_ctx_create(moe_ctx_t** out) {
   moe_ctx* c = new moe_ctx();
   c->timing = 0;
   c->timed = 0;
+  c->trace = nullptr;
+  c->trace_flags = 0;
   if (hipGetDevice(&c->device) != hipSuccess ||
       hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess ||
       hipEventCreateWithFlags(&c->ev_producer, hipEventDisableTiming) != hipSuccess) {
@@ -210,6 +218,21 @@ int moe_ctx_timings(moe_ctx_t* ctx, float* ms) {
   return MOE_OK;
 }
 
+int moe_ctx_set_trace(moe_ctx_t* ctx, const moe_shape_t* shape, uint64_t* trace, int64_t words) {
+  if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
+  if (trace == nullptr) {
+    ctx->trace = nullptr;
+    return MOE_OK;
+  }
+  Geometry g;
+  const int rc = make_geometry(shape, &g);
+  if (rc != MOE_OK) return rc;
+  if (words < 8 + (int64_t)g.max_flags + 3 * (int64_t)g.max_bands) return MOE_ERR_INVALID_ARG;
+  ctx->trace = trace;
+  ctx->trace_flags = g.max_flags;
+  return MOE_OK;
+}
+
 int moe_ctx_destroy(moe_ctx_t* ctx) {
   if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
   if (ctx->timing) (void)moe_ctx_set_timing(ctx, 0);
@@ -247,7 +270,6 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
   plan_from_ws(g, ws, &p);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((rc = hip_rc(launch_plan(g, counts, p, st))) != MOE_OK) return rc;
-  if ((rc = hip_rc(launch_padzero(g, x_perm, counts, p, st))) != MOE_OK) return rc;
   return hip_rc(launch_gather(g, x, topk_ids, x_perm, p, st));
 }
 
@@ -286,7 +308,8 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
   if ((rc = hip_rc(launch_gemm1(g, x_perm, w1, w3, h, p, ncu, ps))) != MOE_OK) return rc;
   if ((rc = rec(1, ps)) != MOE_OK) return rc;
   if (mode == MOE_MODE_SEQUENTIAL) {
-    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ncu, ps))) != MOE_OK) return rc;
+    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu, ps))) != MOE_OK)
+      return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
     if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 2 * ncu, ps))) != MOE_OK) return rc;
     if ((rc = rec(3, ps)) != MOE_OK) return rc;
@@ -297,10 +320,12 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
   }
   if ((rc = hip_rc(hipEventRecord(ctx->ev_producer, ps))) != MOE_OK) return rc;
   if ((rc = hip_rc(hipStreamWaitEvent(cs, ctx->ev_producer, 0))) != MOE_OK) return rc;
-  if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ncu - n_consumer_cu, ps))) != MOE_OK)
+  if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu - n_consumer_cu,
+                                ps))) != MOE_OK)
     return rc;
   if ((rc = rec(2, ps)) != MOE_OK) return rc;
-  if ((rc = hip_rc(launch_consumer(g, y_perm, bufs, p, flags, epoch, n_consumer_cu, cs))) != MOE_OK)
+  if ((rc = hip_rc(launch_consumer(g, y_perm, bufs, p, flags, epoch, ctx->trace, n_consumer_cu, cs))) !=
+      MOE_OK)
     return rc;
   if ((rc = rec(3, cs)) != MOE_OK) return rc;
   if ((rc = hip_rc(hipEventRecord(ctx->ev_consumer, cs))) != MOE_OK) return rc;

@@ -18,6 +18,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kChunk = 256;
 // meta words in the workspace
 enum { META_MPAD = 0, META_NBANDS = 1, META_NREMOTE = 2, META_NSEG = 3, META_STATUS = 4, META_WORDS = 64 };
+// per-XCD tile queues of the two GEMM launches: counter (phase, xcd) at tile_ctr[(phase*8 + xcd) * 32]
+constexpr int kXcds = 8;
+constexpr int kCtrStride = 32;
+constexpr int kCtrWords = 2 * kXcds * kCtrStride;
 
 struct Geometry {
   int32_t R, T, H, F, E, k, r_self, gated, gate_kind, tb_m, mgb;
@@ -40,7 +44,7 @@ struct WsLayout {
   size_t meta, chunk_counts, chunk_base, group_row, expert_base, recv_off;
   size_t band_row0, band_expert, band_dest, band_recv0, band_valid;
   size_t seg_band0, seg_nbands, seg_dest, seg_src_row, seg_dst_row, seg_rows;
-  size_t row_src, recv_row, total;
+  size_t row_src, recv_row, tile_ctr, slot_valid, total;
 };
 
 int make_geometry(const moe_shape_t* s, Geometry* g);
@@ -55,18 +59,17 @@ hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, fl
                         const moe_plan_t& p, hipStream_t st);
 hipError_t launch_count(const Geometry& g, int32_t* counts, const moe_plan_t& p, hipStream_t st);
 hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, hipStream_t st);
-hipError_t launch_padzero(const Geometry& g, uint16_t* x_perm, const int32_t* counts,
-                          const moe_plan_t& p, hipStream_t st);
 hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
                          uint16_t* x_perm, const moe_plan_t& p, hipStream_t st);
 hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_t* w1,
                         const uint16_t* w3, uint16_t* h, const moe_plan_t& p, int grid,
                         hipStream_t st);
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
-                        const moe_plan_t& p, uint32_t* flags, uint32_t epoch, int grid,
-                        hipStream_t st);
+                        const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
+                        int grid, hipStream_t st);
 hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
-                           const uint32_t* flags, uint32_t epoch, int n_wg, hipStream_t st);
+                           const uint32_t* flags, uint32_t epoch, uint64_t* trace, int n_wg,
+                           hipStream_t st);
 hipError_t launch_bulk_copy(const Geometry& g, const uint16_t* y, BufPtrs bufs,
                             const moe_plan_t& p, int grid, hipStream_t st);
 hipError_t launch_combine(const Geometry& g, BufPtrs bufs, const uint16_t* y, const float* gates,

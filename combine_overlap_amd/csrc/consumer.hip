@@ -3,7 +3,9 @@
 // in schedule order, waits until every tile of a segment's row bands carries
 // the current epoch flag (acquire loads at agent scope), and then moves the
 // segment's valid rows with one contiguous copy into the combine buffer of
-// the owner rank. On one GPU the owner's receive buffer is a buffer in local
+// the owner rank. Flags and rows are read with device-scope loads, which
+// pair with the producer's device-scope stores and completion wait (see the
+// output-projection epilogue); no L2 invalidate is issued per segment. On one GPU the owner's receive buffer is a buffer in local
 // HBM; the copy is split evenly across the c consumer workgroups.
 //
 // Each consumer workgroup (1024 threads) also reserves enough LDS that no
@@ -23,27 +25,44 @@ constexpr uint64_t kWaitTicks = 200000000ull;   // 2 s at 100 MHz
 constexpr int kConsumerThreads = 1024;
 constexpr int kConsumerLdsBytes = 80 * 1024;
 
+#ifndef MOE_DEVICE_SCOPE_PUBLISH
+#define MOE_DEVICE_SCOPE_PUBLISH 1
+#endif
+
+// plain 16-byte loads (non-temporal loads halve the per-CU rate), streaming stores
+template <bool DEVICE_SCOPE>
 __device__ __forceinline__ void copy_units(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                            size_t lo, size_t hi, int tid, int nthr) {
+  auto ld = [&](size_t i) -> u32x4 {
+    if constexpr (DEVICE_SCOPE) {
+      // device-scope (sc1) loads miss in this XCD's L2 unless the line is coherent
+      const uint64_t* s64 = reinterpret_cast<const uint64_t*>(src + i);
+      const uint64_t x = __hip_atomic_load(s64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t y = __hip_atomic_load(s64 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return u32x4{(uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32)};
+    } else {
+      return src[i];
+    }
+  };
   size_t i = lo + tid;
   for (; i + 3 * (size_t)nthr < hi; i += 4 * (size_t)nthr) {
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + nthr);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * (size_t)nthr);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * (size_t)nthr);
+    const u32x4 a = ld(i);
+    const u32x4 b = ld(i + nthr);
+    const u32x4 c = ld(i + 2 * (size_t)nthr);
+    const u32x4 d = ld(i + 3 * (size_t)nthr);
     __builtin_nontemporal_store(a, dst + i);
     __builtin_nontemporal_store(b, dst + i + nthr);
     __builtin_nontemporal_store(c, dst + i + 2 * (size_t)nthr);
     __builtin_nontemporal_store(d, dst + i + 3 * (size_t)nthr);
   }
-  for (; i < hi; i += nthr) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  for (; i < hi; i += nthr) __builtin_nontemporal_store(ld(i), dst + i);
 }
 
 __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* __restrict__ y,
                                                                 BufPtrs bufs, moe_plan_t p,
                                                                 const uint32_t* flags,
-                                                                uint32_t epoch, int tiles2,
-                                                                int H) {
+                                                                uint32_t epoch, uint64_t* trace,
+                                                                int trace_seg, int tiles2, int H) {
   __shared__ int s_abort;
   __shared__ __attribute__((aligned(16))) uint32_t s_reserve[kConsumerLdsBytes / 4];
   const int tid = threadIdx.x;
@@ -51,9 +70,12 @@ __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* _
   __syncthreads();
   const int n_seg = p.meta[META_NSEG];
   const int nwg = gridDim.x, wg = blockIdx.x;
+  const bool tr = trace != nullptr && wg == 0 && tid == 0;
+  if (tr) trace[1] = wall_clock64();
   for (int sgi = 0; sgi < n_seg; ++sgi) {
     const int b0 = p.seg_band0[sgi];
     const int nb = p.seg_nbands[sgi];
+    if (tr) trace[trace_seg + 3 * sgi] = wall_clock64();
     if (tid < 64) {
       const uint32_t* f = flags + (size_t)b0 * tiles2;
       const int nf = nb * tiles2;
@@ -61,7 +83,8 @@ __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* _
       while (true) {
         bool ok = true;
         for (int i = tid; i < nf; i += 64)
-          ok &= (__hip_atomic_load(f + i, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == epoch);
+          ok &= (__hip_atomic_load(f + i, MOE_DEVICE_SCOPE_PUBLISH ? __ATOMIC_RELAXED : __ATOMIC_ACQUIRE,
+                                   __HIP_MEMORY_SCOPE_AGENT) == epoch);
         if (__ballot(!ok) == 0ull) break;
         if (wall_clock64() - t_start > kWaitTicks) {
           if (tid == 0) {
@@ -78,7 +101,8 @@ __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* _
     }
     __syncthreads();
     if (s_abort) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!MOE_DEVICE_SCOPE_PUBLISH) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (tr) trace[trace_seg + 3 * sgi + 1] = wall_clock64();
     const size_t units = (size_t)p.seg_rows[sgi] * H / 8;
     const size_t per = (units + nwg - 1) / nwg;
     const size_t lo = (size_t)wg * per;
@@ -86,7 +110,11 @@ __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* _
     if (lo < hi) {
       const u32x4* src = reinterpret_cast<const u32x4*>(y + (size_t)p.seg_src_row[sgi] * H);
       u32x4* dst = reinterpret_cast<u32x4*>(bufs.p[p.seg_dest[sgi]] + (size_t)p.seg_dst_row[sgi] * H);
-      copy_units(src, dst, lo, hi, tid, kConsumerThreads);
+      copy_units<MOE_DEVICE_SCOPE_PUBLISH != 0>(src, dst, lo, hi, tid, kConsumerThreads);
+    }
+    if (trace != nullptr && wg == 0) {
+      __syncthreads();
+      if (tid == 0) trace[trace_seg + 3 * sgi + 2] = wall_clock64();
     }
   }
   if (tid == 0 && s_reserve[0] != 0) s_abort = 2;   // keeps the LDS reservation alive
@@ -105,14 +133,15 @@ __global__ __launch_bounds__(256) void k_bulk_copy(const uint16_t* __restrict__ 
     if (lo >= hi) continue;
     const u32x4* src = reinterpret_cast<const u32x4*>(y + (size_t)p.seg_src_row[sgi] * H);
     u32x4* dst = reinterpret_cast<u32x4*>(bufs.p[p.seg_dest[sgi]] + (size_t)p.seg_dst_row[sgi] * H);
-    copy_units(src, dst, lo, hi, threadIdx.x, 256);
+    copy_units<false>(src, dst, lo, hi, threadIdx.x, 256);
   }
 }
 
 hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
-                           const uint32_t* flags, uint32_t epoch, int n_wg, hipStream_t st) {
+                           const uint32_t* flags, uint32_t epoch, uint64_t* trace, int n_wg,
+                           hipStream_t st) {
   hipLaunchKernelGGL(k_consumer, dim3(n_wg), dim3(kConsumerThreads), 0, st, y, bufs, p, flags,
-                     epoch, g.tiles2, g.H);
+                     epoch, trace, 8 + g.max_flags, g.tiles2, g.H);
   return hipGetLastError();
 }
 

@@ -1,44 +1,78 @@
 // Producer: the rank-wide persistent grouped GEMM of the tile-signalling
 // overlap paper (sec. 3.3.1). One launch covers every local expert through
 // one tile worklist: tile t = (row band t / tiles_n, column tile t % tiles_n)
-// with bands in the remote-first schedule order (sec. 3.2.2); workgroup i
-// takes tiles i, i+g, i+2g, ... The expert of a band selects the weight
-// pointer; no matrices are concatenated and nothing is relaunched per expert.
+// with bands in the remote-first schedule order (sec. 3.2.2). The expert of
+// a band selects the weight pointer; no matrices are concatenated and
+// nothing is relaunched per expert.
 //
-// gfx950 mapping: 256 threads = 4 waves in a 2x2 (or 1x4 / 2x2 for 64-row
-// tiles) grid; v_mfma_f32_32x32x16_bf16 with fp32 accumulators; the k-loop
-// stages 64-wide slices of A and B through two LDS buffers (register
-// prefetch of the next slice while MFMAs run on the current one), with a
-// 16-byte-chunk XOR swizzle so MFMA fragment reads are bank-conflict free.
+// gfx950 mapping
+//  * Tile queues per XCD: tile t belongs to XCD t % 8, so each XCD's L2 sees
+//    a fixed subset of column tiles (weight slices) and the bands in schedule
+//    order. A workgroup reads its XCD from HW_REG_XCC_ID and takes the next
+//    tile of that XCD's queue with one atomic; when the queue is empty it
+//    steals from the other queues. Any grid size and any placement of the
+//    consumer's CUs therefore keeps every producer CU busy.
+//  * 4 or 8 waves per workgroup in a WM x WN grid (8 = two waves per SIMD);
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
+//  * The k-loop streams BK-wide slices of A and B straight from global memory
+//    into an NS-stage LDS ring with global_load_lds_dwordx4 (no VGPR staging).
+//    Each lane fetches the 16-byte chunk that belongs at its LDS slot under an
+//    XOR swizzle that keeps MFMA fragment reads free of bank conflicts. One
+//    barrier per k-step: wait for this wave's copies of stage kt, barrier,
+//    issue stage kt+NS-1 into the slot freed by stage kt-1, run the MFMAs.
 //
 // Epilogues:
-//   EPI_PLAIN  C = A B^T (output projection y = h W2^T). With flags, after
-//              the tile's stores every thread issues an agent-scope release
-//              fence, the workgroup synchronises and one lane stores
-//              flags[t] = epoch with release semantics (sec. 3.3.1:
-//              store, fence, publish).
-//   EPI_SILU   h = SiLU(x W1^T)                       (non-gated FFN)
+//   EPI_PLAIN  C = A B^T (output projection y = h W2^T). With flags the tile
+//              is published as in sec. 3.3.1 (store, fence, flag): its rows go
+//              out with device-scope (sc1) stores, which write through this
+//              XCD's L2 to the device coherence point; s_waitcnt vmcnt(0)
+//              waits until every one of them has completed; the workgroup
+//              synchronises; one lane stores flags[t] = epoch (device scope).
+//              The consumer polls with device-scope loads and reads the rows
+//              with device-scope loads, so it sees the completed stores. This
+//              is the ordering an agent-scope release/acquire pair provides,
+//              without the whole-L2 writeback (producer) and invalidate
+//              (consumer) those need for ordinary cached accesses, which cost
+//              ~15% of the producer's time when issued once per tile.
+//              (Build with -DMOE_DEVICE_SCOPE_PUBLISH=0 for the fence-based
+//              release/acquire form.)
+//   EPI_SILU   h = SiLU(x W1^T)                        (non-gated FFN)
 //   EPI_GATED  h = SiLU(x W1^T) * (x W3^T); the B tile interleaves 32-row
-//              blocks of W1 and W3 so each wave holds u and v of the same
-//              h columns in registers.
+//              blocks of W1 and W3 so each wave holds u and v of the same h
+//              columns in registers.
 #include "common.hpp"
+
+#ifndef MOE_DEVICE_SCOPE_PUBLISH
+#define MOE_DEVICE_SCOPE_PUBLISH 1
+#endif
 
 namespace moe {
 
 enum { EPI_PLAIN = 0, EPI_SILU = 1, EPI_GATED = 2 };
 
-template <int BM, int BN>
+#define LDS_AS __attribute__((address_space(3)))
+
+template <int BM, int BN, int BK, int NS, int WM, int WN>
 struct Tile {
-  static constexpr int BK = 64;
-  static constexpr int WN = (BM >= 128) ? 2 : ((BN / 64) < 4 ? (BN / 64) : 4);
-  static constexpr int WM = 4 / WN;
-  static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int A_LOADS = BM / 32, B_LOADS = BN / 32;   // 16-byte chunks per thread
-  static constexpr int STAGE = (BM + BN) * BK;                 // bf16 elements per stage
-  // at least 96 KiB so that one producer workgroup owns a CU
-  static constexpr int LDS_ELEMS = (2 * STAGE > 49152) ? 2 * STAGE : 49152;
-  static_assert(WM * WN == 4 && FM >= 1 && FN >= 1, "wave tiling");
+  static constexpr int NW = WM * WN;                   // waves per workgroup (4 or 8)
+  static constexpr int NT = NW * 64;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
+  static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 MFMA blocks per wave
+  static constexpr int CPR = BK / 8;          // 16-byte chunks per LDS row
+  static constexpr int RPI = 64 / CPR;        // rows covered by one wave-wide DMA instruction
+  static constexpr int A_PW = BM / RPI / NW;  // DMA instructions per wave per stage (A)
+  static constexpr int B_PW = BN / RPI / NW;  // (B)
+  static constexpr int LPW = A_PW + B_PW;
+  static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
+  static constexpr int RING = NS * STAGE;
+  static constexpr int EPI_ROW = BN + 8;        // padded LDS row of the staged output tile
+  static constexpr int LDS_ELEMS = RING > BM * EPI_ROW ? RING : BM * EPI_ROW;
+  static_assert((NW == 4 || NW == 8) && FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0,
+                "wave tiling");
+  static_assert(A_PW >= 1 && B_PW >= 1 && (BM / RPI) % NW == 0 && (BN / RPI) % NW == 0, "dma split");
+  static_assert(NS >= 2 && (NS - 1) * LPW <= 63, "vmcnt range");
+  static_assert(BK % 32 == 0, "even number of k16 substeps per stage");
+  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS");
 };
 
 struct GemmArgs {
@@ -49,128 +83,260 @@ struct GemmArgs {
   const int32_t* meta;
   const int32_t* band_row0;
   const int32_t* band_expert;
+  int32_t* my_ctr;             // this launch's 8 per-XCD queue counters
+  int32_t* other_ctr;          // the other launch's counters (zeroed here)
   uint32_t* flags;             // output projection in overlap mode, else null
+  uint64_t* trace;             // optional timeline: [0] start, [8 + t] tile t done
   uint32_t epoch;
-  int K, Nw, Nout, tiles_n, bn_out;
+  int K, Nw, Nout, tiles_n;
+  int xb, xn;                  // XCD grid: xcd = (band % xb) * xn + (column tile % xn)
+  int gp, gq;                  // blocks of gp bands x gq column tiles inside an XCD queue
 };
 
+// Queue index i of XCD x -> tile (band-major schedule index * tiles_n + column tile).
+// XCD x owns bands b = bx + k*xb and column tiles t = nx + l*xn; its queue walks
+// blocks of gp bands x gq column tiles (bands in schedule order, so remote bands
+// still finish first) so that the ~32 tiles an XCD runs at once share A bands
+// and weight columns in its L2. Returns -1 past the end of the queue.
+__device__ __forceinline__ int queue_tile(const GemmArgs& a, int n_bands, int x, int i) {
+  const int bx = x / a.xn, nx = x - (x / a.xn) * a.xn;
+  if (bx >= n_bands || nx >= a.tiles_n) return -1;
+  const int nb = (n_bands - bx + a.xb - 1) / a.xb;      // bands of this XCD
+  const int nn = (a.tiles_n - nx + a.xn - 1) / a.xn;    // column tiles of this XCD
+  if (i >= nb * nn) return -1;
+  const int per_group = a.gp * nn;
+  const int g = i / per_group;
+  const int pg = min(a.gp, nb - g * a.gp);              // bands in this group
+  const int rem = i - g * per_group;
+  const int h = rem / (pg * a.gq);
+  const int qh = min(a.gq, nn - h * a.gq);              // column tiles in this block
+  const int rem2 = rem - h * pg * a.gq;
+  const int k = g * a.gp + rem2 / qh;
+  const int l = h * a.gq + rem2 % qh;
+  return (bx + k * a.xb) * a.tiles_n + (nx + l * a.xn);
+}
+
 // physical 16-byte chunk of logical chunk c in LDS row r
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (CPR == 8) return c ^ (r & 7) ^ ((r >> 3) & 1);
+  else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+}
 
-__device__ __forceinline__ float silu_f32(float u) { return u / (1.0f + __expf(-u)); }
+__device__ __forceinline__ float silu_f32(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
+}
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
-  using C = Tile<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  // lgkmcnt(0): this wave's LDS reads of the slot about to be refilled have completed
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One wave-wide 16-byte-per-lane copy global -> LDS: lane l reads gbase +
+// lane_off (gbase wave-uniform, in SGPRs) and lands at lds_byte + 16 l.
+// Issued through asm so the compiler does not add a full vmcnt wait before every
+// later LDS read; the k-loop waits for exactly the stage it consumes instead.
+// The instruction has no VGPR result (the inline-asm load hazard does not apply).
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t lane_off, uint32_t lds_byte) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(lane_off), "s"(gbase), "s"(lds_byte)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const LDS_AS void*)p));
+}
+
+__device__ __forceinline__ int xcc_id() {
+  int v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & (kXcds - 1);
+}
+
+template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
+  using C = Tile<BM, BN, BK, NS, WM, WN>;
+  static_assert(EPI != EPI_GATED || C::FN % 2 == 0, "gated tiles pair W1/W3 32-column blocks per wave");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  __shared__ int s_tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int n_tiles = a.meta[META_NBANDS] * a.tiles_n;
+  const int wm = wave / WN, wn = wave % WN;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int K = a.K;
-  const int nk = K / C::BK;
-  const int cc = tid & 7;    // logical 16-byte chunk this thread loads
-  const int rr = tid >> 3;   // first row this thread loads (rows rr + 32 i)
+  const int nk = K / BK;
 
-  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int band = tile / a.tiles_n;
-    const int tn = tile - band * a.tiles_n;
+  if (blockIdx.x == 0 && tid < kXcds) a.other_ctr[tid * kCtrStride] = 0;
+  if (a.trace != nullptr && blockIdx.x == 0 && tid == 0) a.trace[0] = wall_clock64();
+
+  // DMA lane geometry: lane -> (row inside the instruction, physical chunk).
+  // The swizzle depends on the tile row modulo 2*RPI, so one byte offset per
+  // parity of the instruction's row block covers every DMA of A and of B.
+  const int d_row = lane / C::CPR;
+  const int d_pch = lane % C::CPR;
+  uint32_t lane_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    lane_off[par] = (uint32_t)(d_row * K * 2 + swz<C::CPR>(par * C::RPI + d_row, d_pch) * 16);
+  // MFMA fragment geometry: rows (lane & 31) + 32 i; logical chunk 2 kk + (lane >> 5)
+  int a_off[C::CPR / 2], b_off[C::CPR / 2];
+  {
+    const int ra = wm * C::WTM + (lane & 31), rb = wn * C::WTN + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < C::CPR / 2; ++kk) {
+      const int lc = kk * 2 + (lane >> 5);
+      a_off[kk] = ra * BK + swz<C::CPR>(ra, lc) * 8;
+      b_off[kk] = BM * BK + rb * BK + swz<C::CPR>(rb, lc) * 8;
+    }
+  }
+
+  const int n_bands = a.meta[META_NBANDS];
+  int q = xcc_id(), tried = 0;
+  while (true) {
+    if (tid == 0) {
+      int t = -1;
+      while (tried < kXcds) {
+        const int i = __hip_atomic_fetch_add(a.my_ctr + q * kCtrStride, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        const int cand = queue_tile(a, n_bands, q, i);
+        if (cand >= 0) { t = cand; break; }
+        q = (q + 1) & (kXcds - 1);
+        ++tried;
+      }
+      s_tile = t;
+    }
+    __syncthreads();
+    const int tile = s_tile;
+    if (tile < 0) break;
+    __syncthreads();   // everyone has read s_tile before thread 0 may overwrite it
+
+    const int tile_u = __builtin_amdgcn_readfirstlane(tile);
+    const int band = tile_u / a.tiles_n;
+    const int tn = tile_u - band * a.tiles_n;
     const int row0 = a.band_row0[band];
     const int e = a.band_expert[band];
-    const uint16_t* asrc = a.A + (size_t)(row0 + rr) * K + cc * 8;
-    const uint16_t* bsrc[C::B_LOADS];
-#pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i) {
-      int wrow;
-      const uint16_t* base;
-      if constexpr (EPI == EPI_GATED) {
-        base = ((i & 1) ? a.B1 : a.B0) + (size_t)e * a.Nw * K;
-        wrow = tn * (BN / 2) + (i >> 1) * 32 + rr;
-      } else {
-        base = a.B0 + (size_t)e * a.Nw * K;
-        wrow = tn * BN + i * 32 + rr;
-      }
-      bsrc[i] = base + (size_t)wrow * K + cc * 8;
-    }
 
-    u32x4 ra[C::A_LOADS], rb[C::B_LOADS];
+    // wave-uniform global bases of this wave's DMA instructions (k offset added per stage)
+    const char* abase[C::A_PW];
+    const char* bbase[C::B_PW];
+#pragma unroll
+    for (int i = 0; i < C::A_PW; ++i) {
+      const int r = (wave_u * C::A_PW + i) * C::RPI;
+      abase[i] = reinterpret_cast<const char*>(a.A) + ((size_t)(row0 + r) * K) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PW; ++i) {
+      const int r = (wave_u * C::B_PW + i) * C::RPI;   // first B-tile row of the instruction
+      int wrow;
+      const uint16_t* w;
+      if constexpr (EPI == EPI_GATED) {
+        w = ((r >> 5) & 1) ? a.B1 : a.B0;                // 32-row blocks alternate W1 / W3
+        wrow = tn * (BN / 2) + (r >> 6) * 32 + (r & 31);
+      } else {
+        w = a.B0;
+        wrow = tn * BN + r;
+      }
+      bbase[i] = reinterpret_cast<const char*>(w) + ((size_t)e * a.Nw * K + (size_t)wrow * K) * 2;
+    }
+    const uint32_t lds0 = lds_addr(lds);
+    auto issue = [&](int kt) {
+      const uint32_t st = lds0 + (uint32_t)((kt % NS) * C::STAGE * 2);
+      const size_t ko = (size_t)kt * BK * 2;
+#pragma unroll
+      for (int i = 0; i < C::A_PW; ++i) {
+        const int blk = wave_u * C::A_PW + i;
+        dma16(abase[i] + ko, lane_off[blk & 1], st + (uint32_t)(blk * C::RPI * BK * 2));
+      }
+#pragma unroll
+      for (int i = 0; i < C::B_PW; ++i) {
+        const int blk = wave_u * C::B_PW + i;
+        dma16(bbase[i] + ko, lane_off[blk & 1], st + (uint32_t)((BM + blk * C::RPI) * BK * 2));
+      }
+    };
+
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    auto gload = [&](int kt) {
-      const size_t ko = (size_t)kt * C::BK;
+    // k-loop, software-pipelined:
+    //  * all NS ring slots are in flight: stage kt+NS is issued into stage kt's
+    //    slot as soon as every wave has finished reading stage kt;
+    //  * MFMA fragments are double-buffered: substep kk+1's fragments load
+    //    while substep kk's MFMAs run;
+    //  * the stage barrier sits before the last substep's MFMAs (whose
+    //    fragments are already in registers), so stage kt+1's first
+    //    fragments load while they run.
+    constexpr int KK = BK / 16;
+    bf16x8 fa[2][C::FM], fb[2][C::FN];
+    auto load_frags = [&](int kt, int kk, int buf) {
+      const uint16_t* st = lds + (kt % NS) * C::STAGE;
 #pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i)
-        ra[i] = *reinterpret_cast<const u32x4*>(asrc + (size_t)i * 32 * K + ko);
+      for (int i = 0; i < C::FM; ++i)
+        fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + a_off[kk] + i * 32 * BK);
 #pragma unroll
-      for (int i = 0; i < C::B_LOADS; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bsrc[i] + ko);
+      for (int j = 0; j < C::FN; ++j)
+        fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + b_off[kk] + j * 32 * BK);
     };
-    auto sstore = [&](int buf) {
-      uint16_t* As = lds + buf * C::STAGE;
-      uint16_t* Bs = As + BM * C::BK;
+    auto mfmas = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i) {
-        const int r = rr + 32 * i;
-        *reinterpret_cast<u32x4*>(As + r * C::BK + swz(r, cc) * 8) = ra[i];
-      }
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int i = 0; i < C::B_LOADS; ++i) {
-        const int r = rr + 32 * i;
-        *reinterpret_cast<u32x4*>(Bs + r * C::BK + swz(r, cc) * 8) = rb[i];
-      }
+        for (int j = 0; j < C::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
     };
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
+    // previous tile's stores must not be counted by the stage waits below
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (s < nk) issue(s);
+    if (nk >= NS) wait_vm_barrier<(NS - 1) * C::LPW>();
+    else wait_vm_barrier<0>();
+    load_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
-      const uint16_t* As = lds + cur * C::STAGE;
-      const uint16_t* Bs = As + BM * C::BK;
 #pragma unroll
-      for (int kk = 0; kk < C::BK / 16; ++kk) {
-        const int ch = kk * 2 + (lane >> 5);
-        bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-          const int r = wm * C::WTM + i * 32 + (lane & 31);
-          af[i] = *reinterpret_cast<const bf16x8*>(As + r * C::BK + swz(r, ch) * 8);
-        }
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const int r = wn * C::WTN + j * 32 + (lane & 31);
-          bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + r * C::BK + swz(r, ch) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int kk = 0; kk + 1 < KK; ++kk) {
+        load_frags(kt, kk + 1, (kk + 1) & 1);
+        mfmas(kk & 1);
       }
-      if (kt + 1 < nk) sstore(cur ^ 1);
-      __syncthreads();
+      if (kt + 1 < nk) {
+        if (kt + NS <= nk) wait_vm_barrier<(NS - 2) * C::LPW>();
+        else wait_vm_barrier<0>();
+        if (kt + NS < nk) issue(kt + NS);
+        load_frags(kt + 1, 0, 0);
+      }
+      mfmas((KK - 1) & 1);
     }
 
-    // epilogue: 32x32 accumulator layout: lane l holds column l%32, rows
-    // 8*(q/4) + 4*(l/32) + q%4 for q = 0..15
+    // epilogue. 32x32 accumulator layout: lane l holds column l%32 and rows
+    // 8*(r/4) + 4*(l/32) + r%4, r = 0..15. The bf16 tile is staged in LDS
+    // (row stride OUTW + 8 keeps the two row groups of a store on disjoint
+    // banks) and leaves as 16-byte row chunks.
+    constexpr int OUTW = (EPI == EPI_GATED) ? BN / 2 : BN;
+    constexpr int LROW = OUTW + 8;
     const int ncol = lane & 31;
     const int mrow = (lane >> 5) * 4;
+    __syncthreads();   // every wave is done reading the ring
     if constexpr (EPI == EPI_GATED) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int p = 0; p < C::FN / 2; ++p) {
-          const int col = tn * (BN / 2) + wn * (C::WTN / 2) + p * 32 + ncol;
+          const int c = wn * (C::WTN / 2) + p * 32 + ncol;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int m = wm * C::WTM + i * 32 + (q >> 2) * 8 + mrow + (q & 3);
-            const float u = acc[i][2 * p][q], v = acc[i][2 * p + 1][q];
-            a.C[(size_t)(row0 + m) * a.Nout + col] = f32_to_bf16_rne(silu_f32(u) * v);
+          for (int r = 0; r < 16; ++r) {
+            const int m = wm * C::WTM + i * 32 + (r >> 2) * 8 + mrow + (r & 3);
+            lds[m * LROW + c] = f32_to_bf16_rne(silu_f32(acc[i][2 * p][r]) * acc[i][2 * p + 1][r]);
           }
         }
     } else {
@@ -178,39 +344,85 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs a) {
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
-          const int col = tn * BN + wn * C::WTN + j * 32 + ncol;
+          const int c = wn * C::WTN + j * 32 + ncol;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int m = wm * C::WTM + i * 32 + (q >> 2) * 8 + mrow + (q & 3);
-            float v = acc[i][j][q];
+          for (int r = 0; r < 16; ++r) {
+            const int m = wm * C::WTM + i * 32 + (r >> 2) * 8 + mrow + (r & 3);
+            float v = acc[i][j][r];
             if constexpr (EPI == EPI_SILU) v = silu_f32(v);
-            a.C[(size_t)(row0 + m) * a.Nout + col] = f32_to_bf16_rne(v);
+            lds[m * LROW + c] = f32_to_bf16_rne(v);
           }
         }
-      if (a.flags != nullptr) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (tid == 0)
-          __hip_atomic_store(a.flags + tile, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    constexpr int CH = OUTW / 8;   // 16-byte chunks per output row
+    uint16_t* cbase = a.C + (size_t)row0 * a.Nout + (size_t)tn * OUTW;
+    const bool signal = (EPI == EPI_PLAIN) && a.flags != nullptr;
+#pragma unroll 4
+    for (int q = tid; q < BM * CH; q += C::NT) {
+      const int m = q / CH, cc = q - (q / CH) * CH;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + m * LROW + cc * 8);
+      uint16_t* dst = cbase + (size_t)m * a.Nout + cc * 8;
+#if MOE_DEVICE_SCOPE_PUBLISH
+      if (signal) {
+        // device-scope (sc1) stores write through this XCD's L2
+        uint64_t* d64 = reinterpret_cast<uint64_t*>(dst);
+        __hip_atomic_store(d64, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(d64 + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        continue;
       }
+#endif
+      *reinterpret_cast<u32x4*>(dst) = v;
+    }
+    if (signal) {
+#if MOE_DEVICE_SCOPE_PUBLISH
+      // all of this thread's device-scope stores have completed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(a.flags + tile, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(a.flags + tile, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+#endif
+    }
+    if (EPI == EPI_PLAIN && a.trace != nullptr) {
+      if (!signal) __syncthreads();
+      if (tid == 0) a.trace[8 + tile] = wall_clock64();
     }
   }
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI>
 static hipError_t launch_t(const GemmArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm<BM, BN, EPI>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI>), dim3(grid), dim3(WM * WN * 64), 0, st, a);
   return hipGetLastError();
 }
 
+// XCD grid and block shape for a launch with tiles_n column tiles
+static inline void set_xcd_grid(GemmArgs& a) {
+  a.xn = a.tiles_n >= 32 ? 8 : (a.tiles_n >= 8 ? 4 : (a.tiles_n >= 2 ? 2 : 1));
+  a.xb = kXcds / a.xn;
+  const int nn = (a.tiles_n + a.xn - 1) / a.xn;
+  a.gq = nn < 4 ? nn : 4;
+  a.gp = 32 / a.gq;
+}
+
+// per-shape tile table (tile height = band height tb_m; BN from the geometry).
+// 8 waves (two per SIMD) let one wave's MFMAs cover the other's LDS and DMA
+// waits; measured on MI355X for the Mixtral-shaped projections.
 template <int EPI>
-static hipError_t dispatch(const GemmArgs& a, int bm, int bn, int grid, hipStream_t st) {
-  if (bm == 256 && bn == 256) return launch_t<256, 256, EPI>(a, grid, st);
-  if (bm == 256 && bn == 128) return launch_t<256, 128, EPI>(a, grid, st);
-  if (bm == 128 && bn == 256) return launch_t<128, 256, EPI>(a, grid, st);
-  if (bm == 128 && bn == 128) return launch_t<128, 128, EPI>(a, grid, st);
-  if (bm == 64 && bn == 256) return launch_t<64, 256, EPI>(a, grid, st);
-  if (bm == 64 && bn == 128) return launch_t<64, 128, EPI>(a, grid, st);
+static hipError_t dispatch(GemmArgs a, int bm, int bn, int grid, hipStream_t st) {
+  set_xcd_grid(a);
+  if (bm == 256 && bn == 256) return launch_t<256, 256, 64, 2, 2, 4, EPI>(a, grid, st);
+  if (bm == 256 && bn == 128) return launch_t<256, 128, 64, 3, 4, 2, EPI>(a, grid, st);
+  if (bm == 128 && bn == 256) return launch_t<128, 256, 64, 3, 2, 4, EPI>(a, grid, st);
+  if (bm == 128 && bn == 128) return launch_t<128, 128, 64, 4, 4, 2, EPI>(a, grid, st);
+  if (bm == 64 && bn == 256) return launch_t<64, 256, 64, 3, 2, 4, EPI>(a, grid, st);
+  if (bm == 64 && bn == 128) return launch_t<64, 128, 64, 4, 2, 2, EPI>(a, grid, st);
   return hipErrorInvalidValue;
 }
 
@@ -225,20 +437,22 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_
   a.meta = p.meta;
   a.band_row0 = p.band_row0;
   a.band_expert = p.band_expert;
+  a.my_ctr = p.tile_ctr;
+  a.other_ctr = p.tile_ctr + kXcds * kCtrStride;
   a.flags = nullptr;
+  a.trace = nullptr;
   a.epoch = 0;
   a.K = g.H;
   a.Nw = g.F;
   a.Nout = g.F;
   a.tiles_n = g.tiles1;
-  a.bn_out = g.bn1_out;
   return g.gated ? dispatch<EPI_GATED>(a, g.tb_m, g.bn1, grid, st)
                  : dispatch<EPI_SILU>(a, g.tb_m, g.bn1, grid, st);
 }
 
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
-                        const moe_plan_t& p, uint32_t* flags, uint32_t epoch, int grid,
-                        hipStream_t st) {
+                        const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
+                        int grid, hipStream_t st) {
   GemmArgs a{};
   a.A = h;
   a.B0 = w2;
@@ -247,13 +461,15 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
   a.meta = p.meta;
   a.band_row0 = p.band_row0;
   a.band_expert = p.band_expert;
+  a.my_ctr = p.tile_ctr + kXcds * kCtrStride;
+  a.other_ctr = p.tile_ctr;
   a.flags = flags;
+  a.trace = trace;
   a.epoch = epoch;
   a.K = g.F;
   a.Nw = g.H;
   a.Nout = g.H;
   a.tiles_n = g.tiles2;
-  a.bn_out = g.bn2;
   return dispatch<EPI_PLAIN>(a, g.tb_m, g.bn2, grid, st);
 }
 

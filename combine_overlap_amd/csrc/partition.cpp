@@ -6,25 +6,39 @@
 // tile-signalling paper (sec. 4.3.4, Fig. 9) shows that too few consumer SMs
 // leave a long transfer tail and too many slow the GEMM.
 //
-// Model (the form is not given on the pages; this is the plainest one that
-// uses only the routing counts and two measured rates):
-//   P(c)  = n_cu - c producer CUs
-//   T_g   = sum_e flops2_e / (rate(M_e) * P(c))      overlapped output projection
-//           flops2_e = 2 * H * F * padded rows of expert e,
-//           rate(M) = gemm_flops_per_cu * M / (M + gemm_m_half)
-//   BW(c) = min(c * copy_bw_per_cu, copy_bw_max)       bytes moved per second
-//   T_c   = remote_bytes / BW(c) + n_seg * seg_latency
-//   t_1   = first band ready: one tile of the output projection on one CU
-//   t_end = last segment (one band) after the producer finishes
-//   T(c)  = max(T_g, t_1 + T_c) + band_bytes / BW(c)
-// c = argmin T(c) over [c_min, c_max] (smallest c on ties). mgb = 2 when a
-// single band moves less than half a MiB (the bandwidth curve of the
-// tile-signalling paper, Fig. 3(a), saturates only at MiB-scale transfers),
-// else 1.
+// Model (its form is not given on the pages; this is the plainest one that
+// uses only the routing counts and measured rates). For c consumer CUs:
+//  * the output projection runs on P = n_cu - c CUs; every tile (tb_m x 256
+//    columns, K = F) takes t_tile = 2 tb_m 256 F / rate(M_e) on one CU, with
+//    rate(M) = gemm_flops_per_cu * M / (M + gemm_m_half) for an expert of M
+//    rows; tiles run in waves of P in schedule order (remote bands first,
+//    experts by remote band count, then rows, then id), so band b is ready when
+//    the wave holding its last tile ends; a partial last wave of n tiles lasts
+//    max(n / P, 1/3) of a full one (fewer tiles share the memory bandwidth);
+//  * the consumer copies the segments in order, each when its bands are ready
+//    and the previous copy is done, at BW(c) = min(c * copy_bw_per_cu,
+//    copy_bw_max) plus seg_latency_s per segment;
+//  * T(c) = max(producer end, consumer end).
+// c = argmin T(c) over [c_min, c_max] (smallest c on ties). mgb = 2 when one
+// band moves less than half a MiB (transfer bandwidth saturates only at
+// MiB-scale transfers, tile-signalling paper Fig. 3(a)), else 1.
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "moe_overlap.h"
+
+namespace {
+
+struct Band {
+  int expert;
+  int rows;        // valid rows
+  bool group_end;  // last band of its (expert, owner) group
+};
+
+}  // namespace
 
 extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, const moe_calib_t* calib,
                                   int32_t* n_consumer_cu, int32_t* mgb, double* predicted_s) {
@@ -33,10 +47,13 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
       s->r_self >= s->R || s->H < 1 || s->F < 1 || s->tb_m < 1)
     return MOE_ERR_INVALID_ARG;
   moe_calib_t c0;
-  c0.gemm_flops_per_cu = 2.5e15 / 256.0 * 0.6;
+  // measured on MI355X (output projection of the Mixtral-shaped share; consumer
+  // copy while the producer runs): ~3.4 TFLOP/s per producer CU, ~10 GB/s moved
+  // per consumer CU under the producer's memory traffic
+  c0.gemm_flops_per_cu = 3.4e12;
   c0.gemm_m_half = 64.0;
-  c0.copy_bw_per_cu = 60e9;
-  c0.copy_bw_max = 2.5e12;
+  c0.copy_bw_per_cu = 10e9;
+  c0.copy_bw_max = 1.0e12;
   c0.seg_latency_s = 2e-6;
   c0.n_cu = 256;
   c0.c_min = 2;
@@ -46,44 +63,102 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
       k.copy_bw_per_cu <= 0 || k.copy_bw_max <= 0 || k.gemm_m_half < 0 || k.seg_latency_s < 0)
     return MOE_ERR_INVALID_ARG;
 
-  const int El = s->E / s->R, R = s->R, tb = s->tb_m;
-  double flops_work = 0.0;   // sum_e flops2_e / rate(M_e)   (CU-seconds)
-  double remote_rows = 0.0;
-  long n_seg_bands = 0;
-  for (int e = 0; e < El; ++e) {
-    long m = 0;
+  const int El = s->E / s->R, R = s->R, tb = s->tb_m, self = s->r_self;
+  std::vector<long> m_e(El, 0), rb(El, 0), rr(El, 0);
+  for (int e = 0; e < El; ++e)
     for (int q = 0; q < R; ++q) {
       const long c = counts[e * R + q];
       if (c < 0) return MOE_ERR_INVALID_ARG;
-      if (q != s->r_self) {
-        m += (c + tb - 1) / tb * tb;
-        remote_rows += (double)c;
-        n_seg_bands += (c + tb - 1) / tb;
+      if (q != self) {
+        m_e[e] += (c + tb - 1) / tb * tb;
+        rb[e] += (c + tb - 1) / tb;
+        rr[e] += c;
       } else {
-        m += c;
+        m_e[e] += c;
       }
     }
-    const long mp = (m + tb - 1) / tb * tb;
-    if (mp == 0) continue;
-    const double fl = 2.0 * s->H * (double)s->F * (double)mp;
-    const double rate = k.gemm_flops_per_cu * (double)m / ((double)m + k.gemm_m_half);
-    flops_work += fl / rate;
+  std::vector<int> order(El);
+  for (int e = 0; e < El; ++e) order[e] = e;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    if (rb[a] != rb[b]) return rb[a] > rb[b];
+    if (rr[a] != rr[b]) return rr[a] > rr[b];
+    return a < b;
+  });
+  std::vector<Band> bands;
+  for (int e : order)
+    for (int q = 0; q < R; ++q) {
+      if (q == self) continue;
+      const long c = counts[e * R + q];
+      const long nb = (c + tb - 1) / tb;
+      for (long i = 0; i < nb; ++i) bands.push_back(Band{e, (int)std::min<long>(tb, c - i * tb), i == nb - 1});
+    }
+  const size_t n_remote = bands.size();
+  for (int e = 0; e < El; ++e) {
+    const long c = counts[e * R + self];
+    const long nb = (c + tb - 1) / tb;
+    for (long i = 0; i < nb; ++i) bands.push_back(Band{e, (int)std::min<long>(tb, c - i * tb), i == nb - 1});
   }
+
   const double band_bytes = 2.0 * tb * (double)s->H;
   const int g = band_bytes < 0.5 * 1048576.0 ? 2 : 1;
-  const double remote_bytes = 2.0 * (double)s->H * remote_rows;
-  // segments: 1 + ceil((nb-2)/g) + 1 per group, approximated from the band total
-  const double n_seg = g == 1 ? (double)n_seg_bands : 0.5 * (double)n_seg_bands + 1.0;
-  const double t_tile = 2.0 * tb * 256.0 * (double)s->F / k.gemm_flops_per_cu;
+  const int tiles2 = (s->H + 255) / 256;
+  std::vector<double> t_tile(El);
+  for (int e = 0; e < El; ++e) {
+    const double m = (double)std::max<long>(m_e[e], 1);
+    t_tile[e] = 2.0 * tb * 256.0 * (double)s->F / (k.gemm_flops_per_cu * m / (m + k.gemm_m_half));
+  }
+
   double best_t = INFINITY;
   int best_c = k.c_min;
+  std::vector<double> ready(bands.size(), 0.0);
+  std::vector<size_t> pending;
   for (int c = k.c_min; c <= k.c_max; ++c) {
-    const double bw = fmin(c * k.copy_bw_per_cu, k.copy_bw_max);
-    const double tg = flops_work / (double)(k.n_cu - c);
-    const double tc = remote_bytes / bw + n_seg * k.seg_latency_s;
-    const double tail = remote_rows > 0 ? band_bytes / bw : 0.0;
-    const double t = fmax(tg, (remote_rows > 0 ? t_tile : 0.0) + tc) + tail;
-    if (t < best_t) { best_t = t; best_c = c; }
+    const long P = k.n_cu - c;
+    // producer: waves of P tiles in schedule order; a wave lasts as long as its slowest tile
+    double t = 0.0, wave_len = 0.0;
+    long in_wave = 0;
+    pending.clear();
+    for (size_t b = 0; b < bands.size(); ++b) {
+      for (int j = 0; j < tiles2; ++j) {
+        wave_len = std::max(wave_len, t_tile[bands[b].expert]);
+        if (++in_wave == P) {
+          t += wave_len;
+          for (size_t q : pending) ready[q] = t;
+          pending.clear();
+          in_wave = 0;
+          wave_len = 0.0;
+          if (j == tiles2 - 1) ready[b] = t;
+        }
+      }
+      if (in_wave != 0) pending.push_back(b);
+    }
+    if (in_wave > 0) {
+      t += wave_len * std::max((double)in_wave / (double)P, 1.0 / 3.0);
+      for (size_t q : pending) ready[q] = t;
+    }
+    const double t_prod = t;
+    // consumer: segments of 1, g, ..., g, 1 bands per group, copied in order
+    const double bw = std::min(c * k.copy_bw_per_cu, k.copy_bw_max);
+    double tc = 0.0;
+    size_t b = 0;
+    while (b < n_remote) {
+      size_t last = b;
+      while (last < n_remote && !bands[last].group_end) ++last;
+      const size_t nb = last - b + 1;
+      for (size_t p = b, idx = 0; p <= last; ++idx) {
+        const size_t sz = (idx == 0 || nb <= 2 || p == last) ? 1 : std::min<size_t>(g, last - p);
+        double rows = 0.0, rdy = 0.0;
+        for (size_t q = p; q < p + sz; ++q) {
+          rows += bands[q].rows;
+          rdy = std::max(rdy, ready[q]);
+        }
+        tc = std::max(tc, rdy) + 2.0 * rows * (double)s->H / bw + k.seg_latency_s;
+        p += sz;
+      }
+      b = last + 1;
+    }
+    const double total = std::max(t_prod, tc);
+    if (total < best_t) { best_t = total; best_c = c; }
   }
   *n_consumer_cu = best_c;
   if (mgb) *mgb = g;

@@ -102,6 +102,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
     p.meta[META_STATUS] = 0;
   }
   __syncthreads();
+  for (int i = tid; i < kCtrWords; i += blockDim.x) p.tile_ctr[i] = 0;
   for (int e = tid; e <= El; e += blockDim.x) p.expert_base[e] = s_base[e];
   for (int s = tid; s < R; s += blockDim.x) {   // receive offsets: (expert, token) order
     int acc = 0;
@@ -125,6 +126,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
       p.band_dest[b] = s;
       p.band_recv0[b] = (s != r_self) ? recv0 + j * tb : -1;
       p.band_valid[b] = min(tb, c - j * tb);
+      p.slot_valid[(row0 + j * tb) / tb] = min(tb, c - j * tb);
     }
     if (s != r_self && nb > 0) {
       int sidx = s_segoff[i];
@@ -148,20 +150,14 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
   }
 }
 
-// gather: every local (token, slot) -> its packed row; also row_src and recv_row.
+// index: every local (token, slot) -> its packed row; writes row_src and recv_row.
 // One block per routing chunk (<= 256 tokens of one source rank); thread = token.
 // Rank inside the (expert, owner) group = rows of earlier chunks + rows of
 // earlier waves of this chunk + earlier lanes of this wave (ballot prefix).
-__global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ x,
-                                                 const int32_t* __restrict__ ids,
-                                                 uint16_t* __restrict__ x_perm, moe_plan_t p,
-                                                 int R, int T, int H, int k, int El,
-                                                 int first_local, int r_self,
-                                                 int chunks_per_rank) {
+__global__ __launch_bounds__(256) void k_gather_index(const int32_t* __restrict__ ids, moe_plan_t p,
+                                                       int R, int T, int k, int El, int first_local,
+                                                       int r_self, int chunks_per_rank) {
   __shared__ int s_wcnt[4][kPlanMaxEl];
-  __shared__ int s_rows[kChunk * 16];
-  __shared__ int s_toks[kChunk * 16];
-  __shared__ int s_n;
   const int chunk = blockIdx.x;
   const int s = chunk / chunks_per_rank;
   const int t0 = (chunk % chunks_per_rank) * kChunk;
@@ -172,7 +168,6 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ x,
   int my[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) my[j] = (active && j < k) ? ids[g * k + j] - first_local : -1;
-  if (tid == 0) s_n = 0;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int e = 0; e < El; ++e) {
     bool has = false;
@@ -197,49 +192,37 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ x,
       const int row = p.group_row[e * R + s] + rank;
       p.row_src[row] = g;
       p.recv_row[g * k + slot] = (s == r_self) ? row : p.recv_off[s * El + e] + rank;
-      const int q = atomicAdd(&s_n, 1);
-      s_rows[q] = row;
-      s_toks[q] = g;
     }
   }
-  // slots whose expert is not local
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < 16; ++j)   // slots whose expert is not local
     if (active && j < k && (my[j] < 0 || my[j] >= El)) p.recv_row[g * k + j] = -1;
-  __syncthreads();
-  // copy rows: one wave per row, 16-byte vectors
-  const int n = s_n;
-  const int nv = H / 8;
-  for (int q = wave; q < n; q += 4) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(s_toks[q]) * H);
-    u32x4* dst = reinterpret_cast<u32x4*>(x_perm + static_cast<size_t>(s_rows[q]) * H);
-    for (int v = lane; v < nv; v += 64) dst[v] = src[v];
-  }
 }
 
-// zero rows: owner-boundary padding of remote groups and the gap after each expert
-__global__ __launch_bounds__(256) void k_padzero(uint16_t* __restrict__ x_perm,
-                                                  const int32_t* __restrict__ counts,
-                                                  moe_plan_t p, int R, int H, int El,
-                                                  int r_self, int tb) {
-  const int e = blockIdx.x;
+// copy: row r of [0, m_pad) gets x of token row_src[r] when it is one of the
+// valid rows of its band slot, else zeros (owner-boundary padding, or the
+// aligned gap after an expert), and row_src[r] = -1. One wave per row,
+// 16-byte vectors, grid-stride over rows.
+__global__ __launch_bounds__(256) void k_gather_copy(const uint16_t* __restrict__ x,
+                                                      uint16_t* __restrict__ x_perm, moe_plan_t p,
+                                                      int H, int tb) {
+  const int m_pad = p.meta[META_MPAD];
+  const int lane = threadIdx.x & 63;
   const int nv = H / 8;
   const u32x4 z = {0u, 0u, 0u, 0u};
-  // remote groups: rows [row0 + count, row0 + roundup(count))
-  for (int s = 0; s < R; ++s) {
-    const int c = counts[e * R + s];
-    int lo, hi;
-    if (s != r_self) {
-      lo = p.group_row[e * R + s] + c;
-      hi = p.group_row[e * R + s] + ceil_div(c, tb) * tb;
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < m_pad; r += gridDim.x * 4) {
+    u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (size_t)r * H);
+    if ((r % tb) < p.slot_valid[r / tb]) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)p.row_src[r] * H);
+      int v = lane;
+      for (; v + 192 < nv; v += 256) {
+        const u32x4 a = src[v], b = src[v + 64], c = src[v + 128], d = src[v + 192];
+        dst[v] = a; dst[v + 64] = b; dst[v + 128] = c; dst[v + 192] = d;
+      }
+      for (; v < nv; v += 64) dst[v] = src[v];
     } else {
-      lo = p.group_row[e * R + s] + c;   // end of X_e
-      hi = p.expert_base[e + 1];         // next expert's aligned base
-    }
-    for (int r = lo; r < hi; ++r) {
-      if (threadIdx.x == 0) p.row_src[r] = -1;
-      u32x4* dst = reinterpret_cast<u32x4*>(x_perm + static_cast<size_t>(r) * H);
-      for (int v = threadIdx.x; v < nv; v += blockDim.x) dst[v] = z;
+      if (lane == 0) p.row_src[r] = -1;
+      for (int v = lane; v < nv; v += 64) dst[v] = z;
     }
   }
 }
@@ -253,17 +236,14 @@ hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_
 
 hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
                          uint16_t* x_perm, const moe_plan_t& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_gather, dim3(g.n_chunks), dim3(256), 0, st, x, ids, x_perm, p, g.R, g.T,
-                     g.H, g.k, g.El, g.r_self * g.El, g.r_self, g.chunks_per_rank);
+  hipLaunchKernelGGL(k_gather_index, dim3(g.n_chunks), dim3(256), 0, st, ids, p, g.R, g.T, g.k, g.El,
+                     g.r_self * g.El, g.r_self, g.chunks_per_rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return hipSuccess;
-}
-
-hipError_t launch_padzero(const Geometry& g, uint16_t* x_perm, const int32_t* counts,
-                          const moe_plan_t& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_padzero, dim3(g.El), dim3(256), 0, st, x_perm, counts, p, g.R, g.H, g.El,
-                     g.r_self, g.tb_m);
+  // grid-stride over at most m_pad_max rows, four rows per block
+  const int64_t blocks = (g.m_pad_max + 3) / 4;
+  const int grid = (int)(blocks < 4096 ? blocks : 4096);
+  hipLaunchKernelGGL(k_gather_copy, dim3(grid), dim3(256), 0, st, x, x_perm, p, g.H, g.tb_m);
   return hipGetLastError();
 }
 

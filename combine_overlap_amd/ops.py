@@ -65,6 +65,11 @@ class Context:
         return dict(gemm1=ms[0], producer=ms[1], producer_start_to_consumer_end=ms[2], total=ms[3],
                     exposed=ms[4])
 
+    def set_trace(self, shape, trace=None):
+        """Device timeline buffer (uint64 words; see moe_ctx_set_trace) or None to stop."""
+        n = 0 if trace is None else trace.numel()
+        check("moe_ctx_set_trace", lib().moe_ctx_set_trace(self.handle, C.byref(shape), _ptr(trace), n))
+
     def close(self):
         if self.handle:
             check("moe_ctx_destroy", lib().moe_ctx_destroy(self.handle))

@@ -45,10 +45,10 @@ class ShareBuffers:
 class MoEShare:
     """Buffers and launch sequence for rank r_self's share of one MoE layer."""
 
-    def __init__(self, R, T, H, F, E, k, gated, gate_kind, r_self=0, tb_m=128, mgb=1,
+    def __init__(self, R, T, H, F, E, k, gated, gate_kind, r_self=0, tb_m=128, mgb=None,
                  device="cuda:0"):
         self.device = torch.device(device)
-        self.shape = ops.make_shape(R, T, H, F, E, k, r_self, gated, gate_kind, tb_m, mgb)
+        self.shape = ops.make_shape(R, T, H, F, E, k, r_self, gated, gate_kind, tb_m, mgb or 1)
         self.sizes = ops.moe_query_sizes(self.shape)
         self.R, self.T, self.H, self.F, self.E, self.k = R, T, H, F, E, k
         self.El = E // R
@@ -58,6 +58,11 @@ class MoEShare:
         self.consumer_stream = torch.cuda.Stream(device=self.device)
         self.epoch = 0
         self.buf: Optional[ShareBuffers] = None
+        self.counts_host = torch.empty((self.El, R), dtype=torch.int32, pin_memory=True)
+        self.counts_ready = torch.cuda.Event()
+        # the segment size depends on the shape only; the CU split needs the counts
+        self.shape.mgb = ops.moe_plan_partition(self.shape, np.zeros((self.El, R), np.int32))[1] \
+            if mgb is None else mgb
 
     # ------------------------------------------------------------ buffers
     def allocate(self, logits: torch.Tensor, x: torch.Tensor, w1, w3, w2) -> ShareBuffers:
@@ -127,6 +132,25 @@ class MoEShare:
         self.permute(stream)
         self.expert_forward(mode, n_consumer_cu, stream)
         self.combine(stream)
+
+    def layer(self, mode=_abi.MOE_MODE_OVERLAP, n_consumer_cu: Optional[int] = None, calib=None,
+              stream=None) -> int:
+        """The whole share with the per-layer CU split: route; counts to pinned
+        host memory (async); permute runs on the GPU while the host waits for the
+        counts and evaluates the partition model; expert phase; combine.
+        Returns the consumer CU count used."""
+        s = torch.cuda.current_stream(self.device) if stream is None else stream
+        self.route(s)
+        with torch.cuda.stream(s):
+            self.counts_host.copy_(self.buf.counts, non_blocking=True)
+        self.counts_ready.record(s)
+        self.permute(s)
+        if n_consumer_cu is None:
+            self.counts_ready.synchronize()
+            n_consumer_cu = ops.moe_plan_partition(self.shape, self.counts_host.numpy(), calib)[0]
+        self.expert_forward(mode, n_consumer_cu, s)
+        self.combine(s)
+        return n_consumer_cu
 
     def status(self, stream=None) -> int:
         return ops.moe_read_status(self.shape, self.buf.ws, stream)

@@ -115,6 +115,8 @@ typedef struct {
                              (s == r_self) of slot j of token g; -1 if not local      */
   int32_t* chunk_base;    /* [n_chunks*E_l] internal: per-chunk row offsets           */
   int32_t* chunk_counts;  /* [n_chunks*E_l] internal: per-chunk local counts          */
+  int32_t* tile_ctr;      /* internal: per-XCD tile queue counters of the two GEMMs   */
+  int32_t* slot_valid;    /* [max_bands] valid rows of the band starting at row tb_m*i */
 } moe_plan_t;
 
 /* Calibration of the partition cost model (measured on the device). */
@@ -159,6 +161,17 @@ int moe_ctx_num_cus(const moe_ctx_t* ctx);
  * Returns MOE_ERR_INVALID_ARG if timing is off or nothing was timed. */
 int moe_ctx_set_timing(moe_ctx_t* ctx, int enable);
 int moe_ctx_timings(moe_ctx_t* ctx, float* ms);
+
+/* Device timeline of the overlapped expert phase (off when trace is NULL).
+ * trace: caller device buffer of uint64 words, stamps of the 100 MHz constant
+ * clock (wall_clock64), written by later moe_expert_forward_overlap calls:
+ *   [0]                          output projection start (workgroup 0)
+ *   [1]                          consumer start (workgroup 0)
+ *   [8 + t]                      output-projection tile t stored and flagged
+ *   [8 + max_flags + 3 s + 0/1/2] consumer workgroup 0, segment s: wait begins,
+ *                                all its flags seen, its share of the copy done
+ * words >= 8 + max_flags + 3 * max_bands (moe_sizes_t), else MOE_ERR_INVALID_ARG. */
+int moe_ctx_set_trace(moe_ctx_t* ctx, const moe_shape_t* shape, uint64_t* trace, int64_t words);
 
 /* Step 1, routing ([TLS] sec. 2.1 step 1). Per token g of R*T (g = s*T + t):
  * the k experts with the highest logits, highest first, equal logits to the
