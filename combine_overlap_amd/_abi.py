@@ -24,7 +24,7 @@ MOE_GATE_SIGMOID = 1
 MOE_MODE_OVERLAP = 0
 MOE_MODE_SEQUENTIAL = 1
 
-META_MPAD, META_NBANDS, META_NREMOTE, META_NSEG, META_STATUS = range(5)
+META_MPAD, META_NBANDS, META_NREMOTE, META_NSEG, META_STATUS, META_NUNITS = range(6)
 
 
 class MoeShape(C.Structure):
@@ -40,7 +40,7 @@ class MoeSizes(C.Structure):
 PLAN_FIELDS = ("meta", "group_row", "expert_base", "recv_off", "band_row0", "band_expert",
                "band_dest", "band_recv0", "band_valid", "seg_band0", "seg_nbands", "seg_dest",
                "seg_src_row", "seg_dst_row", "seg_rows", "row_src", "recv_row", "chunk_base",
-               "chunk_counts", "tile_ctr", "slot_valid")
+               "chunk_counts", "tile_ctr", "slot_valid", "seg_unit0")
 
 
 class MoePlan(C.Structure):
@@ -51,7 +51,7 @@ class MoeCalib(C.Structure):
     _fields_ = [("gemm_flops_per_cu", C.c_double), ("gemm_m_half", C.c_double),
                 ("copy_bw_per_cu", C.c_double), ("copy_bw_max", C.c_double),
                 ("seg_latency_s", C.c_double), ("n_cu", C.c_int32), ("c_min", C.c_int32),
-                ("c_max", C.c_int32)]
+                ("c_max", C.c_int32), ("c_step", C.c_int32)]
 
 
 EXPORTS = ("moe_error_string", "moe_query_sizes", "moe_plan_view", "moe_ctx_create",

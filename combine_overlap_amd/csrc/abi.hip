@@ -87,6 +87,7 @@ WsLayout ws_layout(const Geometry& g) {
   L.recv_row = take((size_t)g.R * g.T * g.k);
   L.tile_ctr = take(kCtrWords);
   L.slot_valid = take(mb);
+  L.seg_unit0 = take(mb);
   L.total = off;
   return L;
 }
@@ -109,6 +110,7 @@ void plan_from_ws(const Geometry& g, void* ws, moe_plan_t* p) {
   p->chunk_counts = at(L.chunk_counts);
   p->tile_ctr = at(L.tile_ctr);
   p->slot_valid = at(L.slot_valid);
+  p->seg_unit0 = at(L.seg_unit0);
 }
 
 static inline bool ws_ok(const void* ws) {
@@ -311,7 +313,7 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
     if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu, ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
-    if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 2 * ncu, ps))) != MOE_OK) return rc;
+    if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 4 * ncu, ps))) != MOE_OK) return rc;
     if ((rc = rec(3, ps)) != MOE_OK) return rc;
     if ((rc = rec(4, ps)) != MOE_OK) return rc;
     ctx->timed = tm;

@@ -17,7 +17,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // tokens per routing chunk: a chunk never spans two source ranks
 constexpr int kChunk = 256;
 // meta words in the workspace
-enum { META_MPAD = 0, META_NBANDS = 1, META_NREMOTE = 2, META_NSEG = 3, META_STATUS = 4, META_WORDS = 64 };
+enum { META_MPAD = 0, META_NBANDS = 1, META_NREMOTE = 2, META_NSEG = 3, META_STATUS = 4, META_NUNITS = 5,
+       META_WORDS = 64 };
+// segments are also cut into copy units of this many bytes (the baseline bulk copy)
+constexpr int kCopyUnitBytes = 65536;
 // per-XCD tile queues of the two GEMM launches: counter (phase, xcd) at tile_ctr[(phase*8 + xcd) * 32]
 constexpr int kXcds = 8;
 constexpr int kCtrStride = 32;
@@ -44,7 +47,7 @@ struct WsLayout {
   size_t meta, chunk_counts, chunk_base, group_row, expert_base, recv_off;
   size_t band_row0, band_expert, band_dest, band_recv0, band_valid;
   size_t seg_band0, seg_nbands, seg_dest, seg_src_row, seg_dst_row, seg_rows;
-  size_t row_src, recv_row, tile_ctr, slot_valid, total;
+  size_t row_src, recv_row, tile_ctr, slot_valid, seg_unit0, total;
 };
 
 int make_geometry(const moe_shape_t* s, Geometry* g);

@@ -29,10 +29,16 @@ constexpr int kConsumerLdsBytes = 80 * 1024;
 #define MOE_DEVICE_SCOPE_PUBLISH 1
 #endif
 
-// plain 16-byte loads (non-temporal loads halve the per-CU rate), streaming stores
+#ifndef MOE_COPY_UNROLL
+#define MOE_COPY_UNROLL 8
+#endif
+
+// plain 16-byte loads (non-temporal loads halve the per-CU rate), streaming
+// stores; MOE_COPY_UNROLL loads in flight per thread
 template <bool DEVICE_SCOPE>
 __device__ __forceinline__ void copy_units(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                            size_t lo, size_t hi, int tid, int nthr) {
+  constexpr int U = MOE_COPY_UNROLL;
   auto ld = [&](size_t i) -> u32x4 {
     if constexpr (DEVICE_SCOPE) {
       // device-scope (sc1) loads miss in this XCD's L2 unless the line is coherent
@@ -45,15 +51,12 @@ __device__ __forceinline__ void copy_units(const u32x4* __restrict__ src, u32x4*
     }
   };
   size_t i = lo + tid;
-  for (; i + 3 * (size_t)nthr < hi; i += 4 * (size_t)nthr) {
-    const u32x4 a = ld(i);
-    const u32x4 b = ld(i + nthr);
-    const u32x4 c = ld(i + 2 * (size_t)nthr);
-    const u32x4 d = ld(i + 3 * (size_t)nthr);
-    __builtin_nontemporal_store(a, dst + i);
-    __builtin_nontemporal_store(b, dst + i + nthr);
-    __builtin_nontemporal_store(c, dst + i + 2 * (size_t)nthr);
-    __builtin_nontemporal_store(d, dst + i + 3 * (size_t)nthr);
+  for (; i + (U - 1) * (size_t)nthr < hi; i += U * (size_t)nthr) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld(i + u * (size_t)nthr);
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], dst + i + u * (size_t)nthr);
   }
   for (; i < hi; i += nthr) __builtin_nontemporal_store(ld(i), dst + i);
 }
@@ -120,20 +123,27 @@ __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* _
   if (tid == 0 && s_reserve[0] != 0) s_abort = 2;   // keeps the LDS reservation alive
 }
 
-// baseline: all remote segments after the producer, on all CUs
+// baseline: all remote segments after the producer, on all CUs. The segments
+// are cut into 64 KiB copy units (prefix in seg_unit0); workgroups take units
+// grid-stride and find their segment by binary search.
 __global__ __launch_bounds__(256) void k_bulk_copy(const uint16_t* __restrict__ y, BufPtrs bufs,
                                                     moe_plan_t p, int H) {
   const int n_seg = p.meta[META_NSEG];
-  const int nwg = gridDim.x, wg = blockIdx.x;
-  for (int sgi = 0; sgi < n_seg; ++sgi) {
-    const size_t units = (size_t)p.seg_rows[sgi] * H / 8;
-    const size_t per = (units + nwg - 1) / nwg;
-    const size_t lo = (size_t)wg * per;
-    const size_t hi = lo + per < units ? lo + per : units;
-    if (lo >= hi) continue;
+  const int n_units = p.meta[META_NUNITS];
+  constexpr size_t kUnit16 = kCopyUnitBytes / 16;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    int lo = 0, hi = n_seg - 1;
+    while (lo < hi) {   // last segment whose first unit is <= u
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.seg_unit0[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    const int sgi = lo;
+    const size_t units16 = (size_t)p.seg_rows[sgi] * H / 8;
+    const size_t a = (size_t)(u - p.seg_unit0[sgi]) * kUnit16;
+    const size_t b = a + kUnit16 < units16 ? a + kUnit16 : units16;
     const u32x4* src = reinterpret_cast<const u32x4*>(y + (size_t)p.seg_src_row[sgi] * H);
     u32x4* dst = reinterpret_cast<u32x4*>(bufs.p[p.seg_dest[sgi]] + (size_t)p.seg_dst_row[sgi] * H);
-    copy_units<false>(src, dst, lo, hi, threadIdx.x, 256);
+    copy_units<false>(src, dst, a, b, threadIdx.x, 256);
   }
 }
 

@@ -417,7 +417,7 @@ static inline void set_xcd_grid(GemmArgs& a) {
 template <int EPI>
 static hipError_t dispatch(GemmArgs a, int bm, int bn, int grid, hipStream_t st) {
   set_xcd_grid(a);
-  if (bm == 256 && bn == 256) return launch_t<256, 256, 64, 2, 2, 4, EPI>(a, grid, st);
+  if (bm == 256 && bn == 256) return launch_t<256, 256, 64, 2, 4, 2, EPI>(a, grid, st);
   if (bm == 256 && bn == 128) return launch_t<256, 128, 64, 3, 4, 2, EPI>(a, grid, st);
   if (bm == 128 && bn == 256) return launch_t<128, 256, 64, 3, 2, 4, EPI>(a, grid, st);
   if (bm == 128 && bn == 128) return launch_t<128, 128, 64, 4, 4, 2, EPI>(a, grid, st);

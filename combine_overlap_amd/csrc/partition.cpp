@@ -19,7 +19,10 @@
 //    and the previous copy is done, at BW(c) = min(c * copy_bw_per_cu,
 //    copy_bw_max) plus seg_latency_s per segment;
 //  * T(c) = max(producer end, consumer end).
-// c = argmin T(c) over [c_min, c_max] (smallest c on ties). mgb = 2 when one
+// c = argmin T(c) over c_min, c_min + c_step, ..., <= c_max (smallest c on
+// ties). The step defaults to the XCD count: workgroups are dealt to the 8
+// XCDs in turn, so a consumer of c = 8j CUs and a producer of 256 - c CUs fill
+// every XCD exactly whichever kernel is dispatched first. mgb = 2 when one
 // band moves less than half a MiB (transfer bandwidth saturates only at
 // MiB-scale transfers, tile-signalling paper Fig. 3(a)), else 1.
 #include <math.h>
@@ -47,19 +50,21 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
       s->r_self >= s->R || s->H < 1 || s->F < 1 || s->tb_m < 1)
     return MOE_ERR_INVALID_ARG;
   moe_calib_t c0;
-  // measured on MI355X (output projection of the Mixtral-shaped share; consumer
-  // copy while the producer runs): ~3.4 TFLOP/s per producer CU, ~10 GB/s moved
-  // per consumer CU under the producer's memory traffic
-  c0.gemm_flops_per_cu = 3.4e12;
+  // measured on MI355X over the five synthetic workloads: 3.1-4.1 TFLOP/s per
+  // producer CU on the output projection, 15-25 GB/s moved per consumer CU
+  // while the producer runs
+  c0.gemm_flops_per_cu = 3.5e12;
   c0.gemm_m_half = 64.0;
-  c0.copy_bw_per_cu = 10e9;
+  c0.copy_bw_per_cu = 16e9;
   c0.copy_bw_max = 1.0e12;
   c0.seg_latency_s = 2e-6;
   c0.n_cu = 256;
-  c0.c_min = 2;
-  c0.c_max = 16;
+  c0.c_min = 8;
+  c0.c_max = 48;
+  c0.c_step = 8;
   const moe_calib_t& k = calib ? *calib : c0;
-  if (k.n_cu < 2 || k.c_min < 1 || k.c_max < k.c_min || k.c_max >= k.n_cu || k.gemm_flops_per_cu <= 0 ||
+  if (k.n_cu < 2 || k.c_min < 1 || k.c_max < k.c_min || k.c_max >= k.n_cu || k.c_step < 1 ||
+      k.gemm_flops_per_cu <= 0 ||
       k.copy_bw_per_cu <= 0 || k.copy_bw_max <= 0 || k.gemm_m_half < 0 || k.seg_latency_s < 0)
     return MOE_ERR_INVALID_ARG;
 
@@ -112,7 +117,7 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
   int best_c = k.c_min;
   std::vector<double> ready(bands.size(), 0.0);
   std::vector<size_t> pending;
-  for (int c = k.c_min; c <= k.c_max; ++c) {
+  for (int c = k.c_min; c <= k.c_max; c += k.c_step) {
     const long P = k.n_cu - c;
     // producer: waves of P tiles in schedule order; a wave lasts as long as its slowest tile
     double t = 0.0, wave_len = 0.0;

@@ -26,7 +26,7 @@ constexpr int kPlanMaxGroups = 2048;  // E_l * R limit (checked on the host)
 
 // single workgroup: everything here is O(E_l * R) metadata
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ counts, moe_plan_t p,
-                                                int R, int El, int r_self, int tb, int mgb) {
+                                                int R, int El, int r_self, int tb, int mgb, int H) {
   __shared__ int s_cnt[kPlanMaxGroups];
   __shared__ int s_rel[kPlanMaxGroups];      // group start relative to its expert base
   __shared__ int s_bandoff[kPlanMaxGroups];  // first band index of the group (schedule order)
@@ -34,6 +34,8 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
   __shared__ int s_base[kPlanMaxEl + 1];
   __shared__ int s_alg[kPlanMaxEl];          // tb-aligned rows of expert e
   __shared__ int s_nrb[kPlanMaxEl], s_nrr[kPlanMaxEl], s_nlb[kPlanMaxEl], s_order[kPlanMaxEl];
+  __shared__ int s_nseg;
+  __shared__ int s_usum[1024];
   const int tid = threadIdx.x;
   const int G = El * R;
   for (int i = tid; i < G; i += blockDim.x) s_cnt[i] = counts[i];
@@ -100,6 +102,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
     p.meta[META_NREMOTE] = n_remote;
     p.meta[META_NSEG] = seg;
     p.meta[META_STATUS] = 0;
+    s_nseg = seg;
   }
   __syncthreads();
   for (int i = tid; i < kCtrWords; i += blockDim.x) p.tile_ctr[i] = 0;
@@ -148,6 +151,26 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
       }
     }
   }
+  // copy units: exclusive prefix of ceil(segment bytes / kCopyUnitBytes)
+  __syncthreads();
+  const int n_seg = s_nseg;
+  const int per = (n_seg + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int lo = tid * per, hi = min(n_seg, lo + per);
+  auto units = [&](int sg) {
+    return (int)(((long)p.seg_rows[sg] * H * 2 + kCopyUnitBytes - 1) / kCopyUnitBytes);
+  };
+  int local = 0;
+  for (int sg = lo; sg < hi; ++sg) local += units(sg);
+  s_usum[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int t = 0; t < (int)blockDim.x; ++t) { const int v = s_usum[t]; s_usum[t] = acc; acc += v; }
+    p.meta[META_NUNITS] = acc;
+  }
+  __syncthreads();
+  int acc = s_usum[tid];
+  for (int sg = lo; sg < hi; ++sg) { p.seg_unit0[sg] = acc; acc += units(sg); }
 }
 
 // index: every local (token, slot) -> its packed row; writes row_src and recv_row.
@@ -230,7 +253,7 @@ __global__ __launch_bounds__(256) void k_gather_copy(const uint16_t* __restrict_
 hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p,
                        hipStream_t st) {
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, counts, p, g.R, g.El, g.r_self, g.tb_m,
-                     g.mgb);
+                     g.mgb, g.H);
   return hipGetLastError();
 }
 

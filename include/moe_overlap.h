@@ -95,7 +95,7 @@ typedef struct {
  * and tests). Arrays indexed by band / segment are in schedule order. */
 typedef struct {
   int32_t* meta;          /* [0]=m_pad [1]=n_bands [2]=n_remote_bands [3]=n_segments
-                             [4]=device status (0 or MOE_ERR_*)                      */
+                             [4]=device status (0 or MOE_ERR_*) [5]=64 KiB copy units */
   int32_t* group_row;     /* [E_l*R] first packed row of group (e, s)                */
   int32_t* expert_base;   /* [E_l+1] first packed row of expert e, tb_m-aligned      */
   int32_t* recv_off;      /* [R*E_l] first row of (e, s) in rank s's combine buffer */
@@ -117,6 +117,7 @@ typedef struct {
   int32_t* chunk_counts;  /* [n_chunks*E_l] internal: per-chunk local counts          */
   int32_t* tile_ctr;      /* internal: per-XCD tile queue counters of the two GEMMs   */
   int32_t* slot_valid;    /* [max_bands] valid rows of the band starting at row tb_m*i */
+  int32_t* seg_unit0;     /* [max_bands] internal: first 64 KiB copy unit of each segment */
 } moe_plan_t;
 
 /* Calibration of the partition cost model (measured on the device). */
@@ -128,6 +129,9 @@ typedef struct {
   double seg_latency_s;       /* fixed cost per transfer segment, seconds           */
   int32_t n_cu;               /* CUs on the device (256 on MI355X)                  */
   int32_t c_min, c_max;       /* consumer CU range considered                       */
+  int32_t c_step;             /* candidates c_min, c_min + c_step, ...: a multiple of
+                                 the XCD count (8) keeps both kernels' workgroups
+                                 spread evenly over the XCDs                        */
 } moe_calib_t;
 
 typedef struct moe_ctx moe_ctx_t;
@@ -204,7 +208,8 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
  * cost of a wrong split). Host-only pure function.
  *   counts_host [E_l, R] int32 (host memory)
  *   calib       NULL = built-in MI355X defaults
- *   n_consumer_cu (out) c in [calib->c_min, calib->c_max]
+ *   n_consumer_cu (out) c in {c_min, c_min + c_step, ...} <= c_max
+ *               (defaults 8, 16, ..., 48)
  *   mgb         (out, may be NULL) bands per middle segment
  *   predicted_s (out, may be NULL) model time of the overlapped expert phase */
 int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,

@@ -122,14 +122,14 @@ def test_partition_no_remote_rows_takes_minimum():
     counts = np.zeros((2, 4), dtype=np.int32)
     counts[:, 0] = 5000
     c, g, t = ops.moe_plan_partition(sh, counts)
-    assert c == 2 and t > 0
+    assert c == 8 and t > 0
 
 
 def test_partition_grows_with_copy_share():
     sh = good_shape(R=4, H=4096, F=256, E=8, k=2, gated=1, tb_m=128)
     small = np.full((2, 4), 200, dtype=np.int32)
     big = np.full((2, 4), 20000, dtype=np.int32)
-    cal = _abi.MoeCalib(5e12, 64.0, 20e9, 4e12, 1e-6, 256, 2, 16)
+    cal = _abi.MoeCalib(5e12, 64.0, 20e9, 4e12, 1e-6, 256, 2, 16, 1)
     c_small, _, _ = ops.moe_plan_partition(sh, small, cal)
     c_big, _, _ = ops.moe_plan_partition(sh, big, cal)
     assert 2 <= c_small <= c_big <= 16
@@ -140,11 +140,11 @@ def test_partition_is_argmin_of_its_model_over_range():
     sh = good_shape(R=4, H=4096, F=1536, E=128, k=8, gated=1, tb_m=64)
     rng = np.random.default_rng(0)
     counts = rng.integers(0, 3000, size=(32, 4)).astype(np.int32)
-    cal = _abi.MoeCalib(5e12, 64.0, 40e9, 3e12, 2e-6, 256, 2, 16)
+    cal = _abi.MoeCalib(5e12, 64.0, 40e9, 3e12, 2e-6, 256, 2, 16, 1)
     c_best, _, t_best = ops.moe_plan_partition(sh, counts, cal)
     times = {}
     for c in range(2, 17):
-        one = _abi.MoeCalib(5e12, 64.0, 40e9, 3e12, 2e-6, 256, c, c)
+        one = _abi.MoeCalib(5e12, 64.0, 40e9, 3e12, 2e-6, 256, c, c, 1)
         cc, _, t = ops.moe_plan_partition(sh, counts, one)
         assert cc == c
         times[c] = t
@@ -152,12 +152,21 @@ def test_partition_is_argmin_of_its_model_over_range():
     assert c_best == min(c for c in times if times[c] == t_best)
 
 
+def test_partition_default_candidates_are_xcd_multiples():
+    sh = good_shape(R=4, H=4096, F=1536, E=128, k=8, gated=1, tb_m=64)
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        counts = rng.integers(0, 4000, size=(32, 4)).astype(np.int32)
+        c, _, _ = ops.moe_plan_partition(sh, counts)
+        assert c % 8 == 0 and 8 <= c <= 48
+
+
 def test_partition_rejects_bad_calibration():
     sh = good_shape()
     counts = np.ones((2, 4), dtype=np.int32)
     with pytest.raises(_abi.MoeError):
-        ops.moe_plan_partition(sh, counts, _abi.MoeCalib(0, 64, 1e9, 1e12, 0, 256, 2, 16))
+        ops.moe_plan_partition(sh, counts, _abi.MoeCalib(0, 64, 1e9, 1e12, 0, 256, 2, 16, 1))
     with pytest.raises(_abi.MoeError):
-        ops.moe_plan_partition(sh, counts, _abi.MoeCalib(1e12, 64, 1e9, 1e12, 0, 256, 20, 16))
+        ops.moe_plan_partition(sh, counts, _abi.MoeCalib(1e12, 64, 1e9, 1e12, 0, 256, 20, 16, 1))
     with pytest.raises(_abi.MoeError):
         ops.moe_plan_partition(sh, -counts, None)
