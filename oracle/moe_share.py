@@ -420,21 +420,29 @@ def oracle_share(logits, x_bits, W1b, W3b, W2b, *, R: int, T: int, E: int, k: in
 
 
 def token_rows(res: ShareResult, W1b, W3b, W2b, tokens) -> np.ndarray:
-    """y_share rows of selected tokens only, computed one token at a time from
-    the definition (for sampled checks at sizes where the full share is slow).
-    tokens: iterable of global token indices. Returns float64 [len, H]."""
+    """y_share rows of selected tokens only, from the definition
+    y[g] = sum_j gate_j * FFN_{e_j}(x_g) over the local slots of g (for sampled
+    checks where the full share is too slow). Works one expert at a time so
+    only one expert's weights are widened to float64 at once.
+    tokens: global token indices. Returns float64 [len, H]."""
     lay = res.layout
     H = W2b.shape[1]
     first = lay.r_self * lay.E_l
-    out = []
-    for g in tokens:
-        acc = np.zeros(H, dtype=np.float64)
-        for j in range(res.ids.shape[1]):
-            e = int(res.ids[g, j]) - first
-            if not (0 <= e < lay.E_l):
-                continue
-            x = res.x_perm[np.nonzero(lay.row_src == g)[0][0]][None, :]
-            W3 = widen_bf16(W3b[e]) if W3b is not None else None
-            acc += res.gates[g, j] * expert_ffn(x, widen_bf16(W1b[e]), W3, widen_bf16(W2b[e]))[0]
-        out.append(acc)
-    return np.array(out)
+    tokens = [int(g) for g in tokens]
+    out = np.zeros((len(tokens), H), dtype=np.float64)
+    xrow = {}
+    for q, g in enumerate(tokens):
+        hit = np.nonzero(lay.row_src == g)[0]
+        if hit.size:
+            xrow[g] = res.x_perm[hit[0]]
+    for e in range(lay.E_l):
+        pairs = [(q, j) for q, g in enumerate(tokens) for j in range(res.ids.shape[1])
+                 if int(res.ids[g, j]) - first == e]
+        if not pairs:
+            continue
+        X = np.stack([xrow[tokens[q]] for q, _ in pairs])
+        W3 = widen_bf16(W3b[e]) if W3b is not None else None
+        Y = expert_ffn(X, widen_bf16(W1b[e]), W3, widen_bf16(W2b[e]))
+        for (q, j), y in zip(pairs, Y):
+            out[q] += res.gates[tokens[q], j] * y
+    return out

@@ -97,12 +97,17 @@ def _rng(*key: int) -> np.random.Generator:
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    """Round fp32 values to bf16 (round-to-nearest-even) and return the bit patterns."""
+    """Round fp32 values to bf16 (round-to-nearest-even) and return the bit patterns.
+
+    Works in uint32 (no wider temporaries): for finite inputs the rounding
+    increment cannot overflow 32 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    # keep NaNs quiet NaNs (not expected from normal draws)
+    u = a.view(np.uint32).copy()
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
+    r = u.astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         r[nan] = 0x7FC0
@@ -174,17 +179,27 @@ def make_expert_weights(w: Workload, e_glob: int):
 
 
 def make_local_weights(w: Workload, r_self: int):
-    """Stacked weights of rank r_self's local experts: W1/W3 [E_l,F,H], W2 [E_l,H,F]."""
+    """Stacked weights of rank r_self's local experts: W1/W3 [E_l,F,H], W2 [E_l,H,F].
+
+    Experts are drawn in parallel threads (each has its own stream, so the
+    result does not depend on the thread count)."""
+    import concurrent.futures as cf
+    import os
     El = w.E_local
     W1 = np.empty((El, w.F, w.H), dtype=np.uint16)
     W3 = np.empty((El, w.F, w.H), dtype=np.uint16) if w.gated else None
     W2 = np.empty((El, w.H, w.F), dtype=np.uint16)
-    for e in range(El):
+
+    def one(e):
         a, b, c = make_expert_weights(w, r_self * El + e)
         W1[e] = a
         if W3 is not None:
             W3[e] = b
         W2[e] = c
+
+    workers = max(1, min(El, len(os.sched_getaffinity(0)), 16))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(El)))
     return W1, W3, W2
 
 

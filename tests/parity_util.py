@@ -9,8 +9,11 @@ from oracle import moe_share as om
 from synth import Workload, make_share_inputs
 
 # Tolerance for floating-point outputs (bf16 storage, fp32 accumulation):
-# per-token relative distance ||y - y_ref|| / ||y_ref|| and mean absolute
-# error against the bf16-rounded reference.
+# per-row relative distance ||y - y_ref|| / ||y_ref|| <= REL_TOL for every
+# output; for the layer output (y_share) also the mean absolute error against
+# the bf16-rounded reference <= MEAN_ABS_TOL. Intermediates (per-expert rows,
+# combine buffers) are not gate-weighted, so their magnitude and hence their
+# bf16 rounding floor is larger; they are held to the relative bound only.
 REL_TOL = 2e-2
 MEAN_ABS_TOL = 2e-3
 
@@ -40,8 +43,8 @@ def bits(t) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def check_rows(got: np.ndarray, ref: np.ndarray, what: str):
-    """Per-row relative distance and mean abs error vs bf16(ref)."""
+def check_rows(got: np.ndarray, ref: np.ndarray, what: str, layer_output: bool = True):
+    """Per-row relative distance and (layer output) mean abs error vs bf16(ref)."""
     got = got.reshape(-1, got.shape[-1])
     ref = ref.reshape(-1, ref.shape[-1])
     nr = np.linalg.norm(ref, axis=1)
@@ -52,7 +55,8 @@ def check_rows(got: np.ndarray, ref: np.ndarray, what: str):
     mx = float(rel.max()) if rel.size else 0.0
     say(f"  {what}: max per-row rel {mx:.3e}, mean abs err {mae:.3e}")
     assert mx <= REL_TOL, f"{what}: max per-row relative distance {mx} > {REL_TOL}"
-    assert mae <= MEAN_ABS_TOL, f"{what}: mean abs err {mae} > {MEAN_ABS_TOL}"
+    if layer_output:
+        assert mae <= MEAN_ABS_TOL, f"{what}: mean abs err {mae} > {MEAN_ABS_TOL}"
     return mx, mae
 
 

@@ -1,0 +1,100 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark uses (default band height, partition-model consumer CU count).
+
+Integer work (ids, counts, layout, schedule, plan, segments, row maps) is
+compared bit-exactly with the oracle in full; x_perm and the combine
+buffers are checked bit-exactly (rows against the source tokens / against
+y_perm); expert outputs and the share are compared on sampled rows/tokens
+against the fp64 oracle (one expert's weights widened at a time).
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_share as om
+from synth import WORKLOADS, make_local_weights, make_logits, make_x
+from synth.workloads import ShareInputs
+from parity_util import (assert_plan_equal, bits, check_rows, make_gpu_share, oracle_plan_arrays,
+                         say, widen)
+
+pytestmark = pytest.mark.gpu
+
+# (workload id, layer, band height) -- band heights as in bench.py
+FULL = [(2, 0, 256), (3, 0, 256), (4, 0, 128), (5, 0, 256), (5, 2, 128)]
+
+
+@pytest.mark.parametrize("wid,layer,tb", FULL, ids=[f"cfg{a}_l{b}_tb{c}" for a, b, c in FULL])
+def test_full_size_parity(wid, layer, tb):
+    import torch
+    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL
+    w = WORKLOADS[wid]
+    say(f"[fullsize] {w.name} layer {layer} tb_m={tb}: inputs")
+    W1, W3, W2 = make_local_weights(w, 0)
+    inp = ShareInputs(w, 0, make_logits(w, layer), make_x(w), W1, W3, W2)
+    sh, _ = make_gpu_share(w, 0, tb, None, inp)
+    b = sh.buf
+    mgb = sh.shape.mgb
+    ref = om.oracle_share(inp.logits, inp.x, W1, W3, W2, R=w.R, T=w.T, E=w.E, k=w.k,
+                          gate_kind=w.gate_kind, r_self=0, tb_m=tb, mgb=mgb, with_ffn=False)
+    say(f"[fullsize] {w.name}: route + permute")
+    sh.route()
+    torch.cuda.synchronize()
+    assert np.array_equal(b.topk_ids.cpu().numpy(), ref.ids)
+    assert np.array_equal(b.counts.cpu().numpy(), ref.layout.counts)
+    assert np.allclose(b.gates.cpu().numpy().astype(np.float64), ref.gates, rtol=2e-6, atol=1e-7)
+    c, mgb2, _ = sh.partition()
+    assert mgb2 == mgb
+    sh.permute()
+    plan = sh.plan_arrays()
+    assert plan["status"] == 0
+    assert_plan_equal(plan, oracle_plan_arrays(ref))
+    m_pad = plan["m_pad"]
+    rng = np.random.default_rng(wid * 10 + layer)
+    rows = rng.choice(m_pad, size=min(m_pad, 512), replace=False)
+    assert np.array_equal(widen(b.x_perm[torch.from_numpy(rows).to(sh.device)]), ref.x_perm[rows])
+
+    say(f"[fullsize] {w.name}: overlap c={c}")
+    for s in range(w.R):
+        if b.combine[s] is not None:
+            b.combine[s].fill_(float("nan"))
+    sh.expert_forward(MOE_MODE_OVERLAP, n_consumer_cu=c)
+    sh.combine()
+    torch.cuda.synchronize()
+    assert sh.status() == 0
+    y_bits = bits(b.y_perm[:m_pad])
+    share_bits = bits(b.y_share).copy()
+    # combine buffers hold exact copies of the remote bands' valid rows
+    bd = ref.bands
+    for i in range(bd.n_remote):
+        s, r0, rc, n = int(bd.dest[i]), int(bd.row0[i]), int(bd.recv0[i]), int(bd.valid[i])
+        got = b.combine[s][rc:rc + n].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, y_bits[r0:r0 + n]), f"band {i}"
+    # sampled expert-output rows vs the fp64 FFN
+    valid = np.nonzero(ref.layout.row_src >= 0)[0]
+    pick = rng.choice(valid, size=min(valid.size, 96), replace=False)
+    y_ref = np.zeros((pick.size, w.H))
+    for e in range(w.E_local):
+        lo, hi = ref.layout.expert_base[e], ref.layout.expert_base[e] + ref.layout.M_e[e]
+        sel = np.nonzero((pick >= lo) & (pick < hi))[0]
+        if sel.size:
+            y_ref[sel] = om.expert_ffn(ref.x_perm[pick[sel]], om.widen_bf16(W1[e]),
+                                       om.widen_bf16(W3[e]) if W3 is not None else None,
+                                       om.widen_bf16(W2[e]))
+    y_gpu = y_bits[pick].astype(np.uint32) << 16
+    check_rows(y_gpu.view(np.float32).astype(np.float64), y_ref, f"{w.name} y_perm sample",
+               layer_output=False)
+    # sampled tokens of the share: with 0, 1 and several local slots
+    nloc = ((ref.ids >= 0) & (ref.ids < w.E_local)).sum(axis=1)
+    toks = []
+    for want in sorted(set(nloc.tolist())):
+        cand = np.nonzero(nloc == want)[0]
+        toks += rng.choice(cand, size=min(cand.size, 24), replace=False).tolist()
+    t_ref = om.token_rows(ref, W1, W3, W2, toks)
+    t_gpu = (share_bits.reshape(-1, w.H)[toks].astype(np.uint32) << 16).view(np.float32)
+    check_rows(t_gpu.astype(np.float64), t_ref, f"{w.name} y_share sample")
+
+    say(f"[fullsize] {w.name}: sequential baseline")
+    sh.expert_forward(MOE_MODE_SEQUENTIAL)
+    sh.combine()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits)
+    assert np.array_equal(bits(b.y_share), share_bits)
