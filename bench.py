@@ -23,7 +23,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-DEFAULT_TB = {1: 64, 2: 128, 3: 128, 4: 64, 5: 64}
+# band height per workload: the fastest measured overlapped layer step
+DEFAULT_TB = {1: 64, 2: 256, 3: 256, 4: 128, 5: 256}
+# sources whose change invalidates stored hardware-counter traffic figures
+GEMM_SOURCES = ("combine_overlap_amd/csrc/gemm.hip", "combine_overlap_amd/csrc/common.hpp")
 
 
 def log(*a):
@@ -45,6 +48,36 @@ def parse():
                          "serialises kernels and so cannot run the concurrent consumer)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, tb: int):
+    """HBM-side bytes per launch of the first-projection GEMM from the committed
+    FETCH_SIZE / WRITE_SIZE summary for this workload and band height, or None
+    when there is none or the GEMM sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_gemm1_{workload}_tb{tb}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, inp, tb, target_s):
@@ -131,6 +164,10 @@ def main():
     flops1 = float((4 if w.gated else 2) * w.H * w.F) * M
     plan = sh.plan_arrays()
     m_pad = plan["m_pad"]
+    # compulsory HBM bytes of the first-projection GEMM: x_perm, W1 (+W3) of the
+    # experts that received rows, h
+    n_w = (2 if w.gated else 1) * int((counts.sum(axis=1) > 0).sum())
+    gemm1_bytes = 2 * (m_pad * w.H + n_w * w.F * w.H + m_pad * w.F)
     log(f"[bench] valid rows {M}, remote rows {remote}, padded rows {m_pad}, bands {plan['n_bands']}, "
         f"segments {plan['n_seg']}, c={c_used}, mgb={mgb_used}")
 
@@ -180,6 +217,7 @@ def main():
         log(f"[bench] overlap: gemm1 {g1:.3f} ms, producer {prod:.3f} ms, expert phase "
             f"{ovl_total:.3f} ms, exposed copy {exposed * 1e3:.1f} us")
     ach1 = flops1 / (g1 * 1e-3) / 1e12
+    traffic = stored_traffic(w.name, tb)
     t_ovl = t_main
 
     out = {
@@ -213,7 +251,9 @@ def main():
         },
         "roofline": {"kernel": "k_gemm first projection (x W1^T, x W3^T, SiLU gate)",
                      "bound": "mfma", "achieved": round(ach1, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ach1 / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(ach1 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "traffic_unit": "bytes per launch",
+                     "algorithmic_bytes": gemm1_bytes, "launch_ms": round(g1, 4)},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
