@@ -40,7 +40,7 @@ class MoeSizes(C.Structure):
 PLAN_FIELDS = ("meta", "group_row", "expert_base", "recv_off", "band_row0", "band_expert",
                "band_dest", "band_recv0", "band_valid", "seg_band0", "seg_nbands", "seg_dest",
                "seg_src_row", "seg_dst_row", "seg_rows", "row_src", "recv_row", "chunk_base",
-               "chunk_counts", "tile_ctr", "slot_valid", "seg_unit0")
+               "chunk_counts", "tile_ctr", "slot_valid", "seg_unit0", "partial")
 
 
 class MoePlan(C.Structure):

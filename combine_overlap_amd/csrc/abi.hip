@@ -88,6 +88,7 @@ WsLayout ws_layout(const Geometry& g) {
   L.tile_ctr = take(kCtrWords);
   L.slot_valid = take(mb);
   L.seg_unit0 = take(mb);
+  L.partial = take((size_t)kXcds * kTailSlots * g.tb_m * 256);
   L.total = off;
   return L;
 }
@@ -111,6 +112,7 @@ void plan_from_ws(const Geometry& g, void* ws, moe_plan_t* p) {
   p->tile_ctr = at(L.tile_ctr);
   p->slot_valid = at(L.slot_valid);
   p->seg_unit0 = at(L.seg_unit0);
+  p->partial = reinterpret_cast<float*>(b + L.partial);
 }
 
 static inline bool ws_ok(const void* ws) {
@@ -298,6 +300,8 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
     if (!flags || epoch == 0 || n_consumer_cu < 1 || n_consumer_cu > 64 ||
         n_consumer_cu >= ctx->n_cu || consumer_stream == producer_stream)
       return MOE_ERR_INVALID_ARG;
+  } else if (n_consumer_cu < 0 || n_consumer_cu > 64 || n_consumer_cu >= ctx->n_cu) {
+    return MOE_ERR_INVALID_ARG;
   }
   moe_plan_t p;
   plan_from_ws(g, ws, &p);
@@ -310,7 +314,8 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
   if ((rc = hip_rc(launch_gemm1(g, x_perm, w1, w3, h, p, ncu, ps))) != MOE_OK) return rc;
   if ((rc = rec(1, ps)) != MOE_OK) return rc;
   if (mode == MOE_MODE_SEQUENTIAL) {
-    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu, ps))) != MOE_OK)
+    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu, ncu - n_consumer_cu,
+                                  ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
     if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 4 * ncu, ps))) != MOE_OK) return rc;
@@ -323,7 +328,7 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
   if ((rc = hip_rc(hipEventRecord(ctx->ev_producer, ps))) != MOE_OK) return rc;
   if ((rc = hip_rc(hipStreamWaitEvent(cs, ctx->ev_producer, 0))) != MOE_OK) return rc;
   if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu - n_consumer_cu,
-                                ps))) != MOE_OK)
+                                ncu - n_consumer_cu, ps))) != MOE_OK)
     return rc;
   if ((rc = rec(2, ps)) != MOE_OK) return rc;
   if ((rc = hip_rc(launch_consumer(g, y_perm, bufs, p, flags, epoch, ctx->trace, n_consumer_cu, cs))) !=

@@ -25,6 +25,10 @@ constexpr int kCopyUnitBytes = 65536;
 constexpr int kXcds = 8;
 constexpr int kCtrStride = 32;
 constexpr int kCtrWords = 2 * kXcds * kCtrStride;
+// K-split tail tiles of a GEMM launch: per XCD queue at most kTailSlots chunks,
+// each with a tb_m x 256 fp32 partial tile; word 1 + t of the XCD's counter
+// block counts the arrivals of tail tile t
+constexpr int kTailSlots = kCtrStride - 1;
 
 struct Geometry {
   int32_t R, T, H, F, E, k, r_self, gated, gate_kind, tb_m, mgb;
@@ -47,7 +51,7 @@ struct WsLayout {
   size_t meta, chunk_counts, chunk_base, group_row, expert_base, recv_off;
   size_t band_row0, band_expert, band_dest, band_recv0, band_valid;
   size_t seg_band0, seg_nbands, seg_dest, seg_src_row, seg_dst_row, seg_rows;
-  size_t row_src, recv_row, tile_ctr, slot_valid, seg_unit0, total;
+  size_t row_src, recv_row, tile_ctr, slot_valid, seg_unit0, partial, total;
 };
 
 int make_geometry(const moe_shape_t* s, Geometry* g);
@@ -67,9 +71,11 @@ hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* id
 hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_t* w1,
                         const uint16_t* w3, uint16_t* h, const moe_plan_t& p, int grid,
                         hipStream_t st);
+// split_grid: the producer grid the K-split tail is sized for (the overlapped
+// run's n_cu - c in both modes, so that both compute identical bits)
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
-                        int grid, hipStream_t st);
+                        int grid, int split_grid, hipStream_t st);
 hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
                            const uint32_t* flags, uint32_t epoch, uint64_t* trace, int n_wg,
                            hipStream_t st);

@@ -12,6 +12,14 @@
 //    tile of that XCD's queue with one atomic; when the queue is empty it
 //    steals from the other queues. Any grid size and any placement of the
 //    consumer's CUs therefore keeps every producer CU busy.
+//  * Split tail: an XCD queue of T tiles served by P workgroups runs T / P
+//    full rounds; its last T mod P tiles would leave most of that XCD idle
+//    for a whole tile time, so each of them is cut into s = P / (T mod P)
+//    (at most 4) chunks along K. A chunk stores its fp32 accumulators as a
+//    partial tile (device-scope write-through stores), waits for them to
+//    complete and increments the tile's arrival counter; the chunk that
+//    arrives last adds the other partials (device-scope loads) and runs the
+//    tile's epilogue, flag included.
 //  * 4 or 8 waves per workgroup in a WM x WN grid (8 = two waves per SIMD);
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 //  * The k-loop streams BK-wide slices of A and B straight from global memory
@@ -52,6 +60,9 @@ enum { EPI_PLAIN = 0, EPI_SILU = 1, EPI_GATED = 2 };
 
 #define LDS_AS __attribute__((address_space(3)))
 
+constexpr int kMaxSplit = 4;        // K chunks per split tail tile
+constexpr int kMinSplitSteps = 8;   // k-steps per chunk at least
+
 template <int BM, int BN, int BK, int NS, int WM, int WN>
 struct Tile {
   static constexpr int NW = WM * WN;                   // waves per workgroup (4 or 8)
@@ -85,12 +96,14 @@ struct GemmArgs {
   const int32_t* band_expert;
   int32_t* my_ctr;             // this launch's 8 per-XCD queue counters
   int32_t* other_ctr;          // the other launch's counters (zeroed here)
+  float* partial;              // fp32 partial tiles of split tail tiles, [8 * kTailSlots][BM * BN]
   uint32_t* flags;             // output projection in overlap mode, else null
   uint64_t* trace;             // optional timeline: [0] start, [8 + t] tile t done
   uint32_t epoch;
   int K, Nw, Nout, tiles_n;
   int xb, xn;                  // XCD grid: xcd = (band % xb) * xn + (column tile % xn)
   int gp, gq;                  // blocks of gp bands x gq column tiles inside an XCD queue
+  int px;                      // workgroups per XCD queue the tail split is sized for
 };
 
 // Queue index i of XCD x -> tile (band-major schedule index * tiles_n + column tile).
@@ -114,6 +127,43 @@ __device__ __forceinline__ int queue_tile(const GemmArgs& a, int n_bands, int x,
   const int k = g * a.gp + rem2 / qh;
   const int l = h * a.gq + rem2 % qh;
   return (bx + k * a.xb) * a.tiles_n + (nx + l * a.xn);
+}
+
+// Work item i of XCD queue x, served by px workgroups: the first T - tail
+// items are whole tiles in queue order; the tail's tiles are split into
+// nsplit consecutive K chunks. slot = index among the split items (< kTailSlots),
+// slot / nsplit = the tail tile's arrival counter.
+struct Item {
+  int tile, chunk, nsplit, slot;
+};
+
+__device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_bands, int x, int i, int px, int nk) {
+  Item it{-1, 0, 1, 0};
+  const int bx = x / a.xn, nx = x - (x / a.xn) * a.xn;
+  if (bx >= n_bands || nx >= a.tiles_n) return it;
+  const int nb = (n_bands - bx + a.xb - 1) / a.xb;
+  const int nn = (a.tiles_n - nx + a.xn - 1) / a.xn;
+  const int T = nb * nn;
+  const int tail = T % px;
+  int s = tail > 0 ? px / tail : 1;
+  s = min(s, min(kMaxSplit, nk / kMinSplitSteps));
+  if (tail * s > kTailSlots) s = kTailSlots / tail;
+  if (s < 2) {
+    if (i < T) it.tile = queue_tile(a, n_bands, x, i);
+    return it;
+  }
+  const int full = T - tail;
+  if (i < full) {
+    it.tile = queue_tile(a, n_bands, x, i);
+    return it;
+  }
+  const int j = i - full;
+  if (j >= tail * s) return it;
+  it.tile = queue_tile(a, n_bands, x, full + j / s);
+  it.chunk = j % s;
+  it.nsplit = s;
+  it.slot = j;
+  return it;
 }
 
 // physical 16-byte chunk of logical chunk c in LDS row r
@@ -165,14 +215,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   using C = Tile<BM, BN, BK, NS, WM, WN>;
   static_assert(EPI != EPI_GATED || C::FN % 2 == 0, "gated tiles pair W1/W3 32-column blocks per wave");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
-  __shared__ int s_tile;
+  __shared__ int s_item[5];   // tile, chunk, nsplit, slot, queue
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int K = a.K;
   const int nk = K / BK;
 
-  if (blockIdx.x == 0 && tid < kXcds) a.other_ctr[tid * kCtrStride] = 0;
+  // the other launch's queue and tail counters (this launch's were cleared by it)
+  if (blockIdx.x == 0 && tid < kXcds * kCtrStride) a.other_ctr[tid] = 0;
+  const int px = max(1, a.px);
   if (a.trace != nullptr && blockIdx.x == 0 && tid == 0) a.trace[0] = wall_clock64();
 
   // DMA lane geometry: lane -> (row inside the instruction, physical chunk).
@@ -200,21 +252,29 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   int q = xcc_id(), tried = 0;
   while (true) {
     if (tid == 0) {
-      int t = -1;
+      Item it{-1, 0, 1, 0};
       while (tried < kXcds) {
         const int i = __hip_atomic_fetch_add(a.my_ctr + q * kCtrStride, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-        const int cand = queue_tile(a, n_bands, q, i);
-        if (cand >= 0) { t = cand; break; }
+        it = queue_item(a, n_bands, q, i, px, nk);
+        if (it.tile >= 0) break;
         q = (q + 1) & (kXcds - 1);
         ++tried;
       }
-      s_tile = t;
+      s_item[0] = it.tile; s_item[1] = it.chunk; s_item[2] = it.nsplit; s_item[3] = it.slot;
+      s_item[4] = q;
     }
     __syncthreads();
-    const int tile = s_tile;
+    const int tile = s_item[0];
     if (tile < 0) break;
-    __syncthreads();   // everyone has read s_tile before thread 0 may overwrite it
+    const int chunk = __builtin_amdgcn_readfirstlane(s_item[1]);
+    const int nsplit = __builtin_amdgcn_readfirstlane(s_item[2]);
+    const int slot = __builtin_amdgcn_readfirstlane(s_item[3]);
+    const int iq = __builtin_amdgcn_readfirstlane(s_item[4]);
+    __syncthreads();   // everyone has read s_item before thread 0 may overwrite it
+    // this item's k-steps
+    const int kb = chunk * nk / nsplit;
+    const int nkc = (chunk + 1) * nk / nsplit - kb;
 
     const int tile_u = __builtin_amdgcn_readfirstlane(tile);
     const int band = tile_u / a.tiles_n;
@@ -247,7 +307,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     const uint32_t lds0 = lds_addr(lds);
     auto issue = [&](int kt) {
       const uint32_t st = lds0 + (uint32_t)((kt % NS) * C::STAGE * 2);
-      const size_t ko = (size_t)kt * BK * 2;
+      const size_t ko = (size_t)(kb + kt) * BK * 2;
 #pragma unroll
       for (int i = 0; i < C::A_PW; ++i) {
         const int blk = wave_u * C::A_PW + i;
@@ -299,23 +359,88 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      if (s < nk) issue(s);
-    if (nk >= NS) wait_vm_barrier<(NS - 1) * C::LPW>();
+      if (s < nkc) issue(s);
+    if (nkc >= NS) wait_vm_barrier<(NS - 1) * C::LPW>();
     else wait_vm_barrier<0>();
     load_frags(0, 0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt < nkc; ++kt) {
 #pragma unroll
       for (int kk = 0; kk + 1 < KK; ++kk) {
         load_frags(kt, kk + 1, (kk + 1) & 1);
         mfmas(kk & 1);
       }
-      if (kt + 1 < nk) {
-        if (kt + NS <= nk) wait_vm_barrier<(NS - 2) * C::LPW>();
+      if (kt + 1 < nkc) {
+        if (kt + NS <= nkc) wait_vm_barrier<(NS - 2) * C::LPW>();
         else wait_vm_barrier<0>();
-        if (kt + NS < nk) issue(kt + NS);
+        if (kt + NS < nkc) issue(kt + NS);
         load_frags(kt + 1, 0, 0);
       }
       mfmas((KK - 1) & 1);
+    }
+
+    // split tail tile: publish this chunk's accumulators; the last chunk to
+    // arrive adds the others and finishes the tile
+    if (nsplit > 1) {
+      // lane-native layout: ((wave * FM + i) * FN + j) * 8 + pair, then 64 lanes x 2 floats
+      uint64_t* mine = reinterpret_cast<uint64_t*>(a.partial) +
+                       (size_t)(iq * kTailSlots + slot) * (BM * BN / 2) +
+                       (size_t)wave * (C::FM * C::FN * 512) + lane;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const uint64_t v = (uint64_t)__float_as_uint(acc[i][j][2 * r]) |
+                               ((uint64_t)__float_as_uint(acc[i][j][2 * r + 1]) << 32);
+            __hip_atomic_store(mine + ((i * C::FN + j) * 8 + r) * 64, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+      // same ordering as a tile's publication: the write-through stores have
+      // completed before the arrival is counted (fence-based form: release
+      // before, acquire after the count)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#if !MOE_DEVICE_SCOPE_PUBLISH
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#endif
+      __syncthreads();
+      if (tid == 0)
+        s_item[0] = __hip_atomic_fetch_add(a.my_ctr + iq * kCtrStride + 1 + slot / nsplit, 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const int arrived = s_item[0];
+      __syncthreads();   // s_item is rewritten by the next item
+      if (arrived != nsplit - 1) continue;
+#if !MOE_DEVICE_SCOPE_PUBLISH
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
+      // sum every chunk's partial (this one's included) in chunk order, so the
+      // tile's bits do not depend on which chunk arrived last
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int c2 = 0; c2 < nsplit; ++c2) {
+        const uint64_t* part = reinterpret_cast<const uint64_t*>(a.partial) +
+                               (size_t)(iq * kTailSlots + slot - chunk + c2) * (BM * BN / 2) +
+                               (size_t)wave * (C::FM * C::FN * 512) + lane;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              const uint64_t v = __hip_atomic_load(part + ((i * C::FN + j) * 8 + r) * 64, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+              acc[i][j][2 * r] += __uint_as_float((uint32_t)v);
+              acc[i][j][2 * r + 1] += __uint_as_float((uint32_t)(v >> 32));
+            }
+            // one 32x32 block of loads in flight at a time (the accumulators stay live)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
     }
 
     // epilogue. 32x32 accumulator layout: lane l holds column l%32 and rows
@@ -439,6 +564,7 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_
   a.band_expert = p.band_expert;
   a.my_ctr = p.tile_ctr;
   a.other_ctr = p.tile_ctr + kXcds * kCtrStride;
+  a.partial = p.partial;
   a.flags = nullptr;
   a.trace = nullptr;
   a.epoch = 0;
@@ -446,13 +572,14 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_
   a.Nw = g.F;
   a.Nout = g.F;
   a.tiles_n = g.tiles1;
+  a.px = grid / kXcds;
   return g.gated ? dispatch<EPI_GATED>(a, g.tb_m, g.bn1, grid, st)
                  : dispatch<EPI_SILU>(a, g.tb_m, g.bn1, grid, st);
 }
 
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
-                        int grid, hipStream_t st) {
+                        int grid, int split_grid, hipStream_t st) {
   GemmArgs a{};
   a.A = h;
   a.B0 = w2;
@@ -463,6 +590,7 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
   a.band_expert = p.band_expert;
   a.my_ctr = p.tile_ctr + kXcds * kCtrStride;
   a.other_ctr = p.tile_ctr;
+  a.partial = p.partial;
   a.flags = flags;
   a.trace = trace;
   a.epoch = epoch;
@@ -470,6 +598,7 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
   a.Nw = g.H;
   a.Nout = g.H;
   a.tiles_n = g.tiles2;
+  a.px = split_grid / kXcds;
   return dispatch<EPI_PLAIN>(a, g.tb_m, g.bn2, grid, st);
 }
 

@@ -118,6 +118,7 @@ typedef struct {
   int32_t* tile_ctr;      /* internal: per-XCD tile queue counters of the two GEMMs   */
   int32_t* slot_valid;    /* [max_bands] valid rows of the band starting at row tb_m*i */
   int32_t* seg_unit0;     /* [max_bands] internal: first 64 KiB copy unit of each segment */
+  float*   partial;       /* internal: fp32 partial tiles of the GEMMs' K-split tail tiles */
 } moe_plan_t;
 
 /* Calibration of the partition cost model (measured on the device). */
@@ -228,7 +229,11 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *   flags    [max_flags] uint32, zero-initialised once by the caller and then
  *            reused: tile t is ready when flags[t] == epoch
  *   epoch    nonzero, different from the previous call's epoch on these flags
- *   n_consumer_cu  c, 1..64 and < device CUs (ignored in SEQUENTIAL mode)
+ *   n_consumer_cu  c: OVERLAP 1..64, SEQUENTIAL 0..64, and < device CUs. The
+ *            output projection splits its tail tiles along K for CUs - c
+ *            producers in both modes, so OVERLAP and SEQUENTIAL calls with the
+ *            same c compute bit-identical results (different c may differ in
+ *            the last bits of the split tiles, from the fp32 summation order)
  *   mode     MOE_MODE_OVERLAP: first projection on all CUs; then the output
  *            projection on (CUs - c) persistent workgroups raising a flag per
  *            tile, concurrently with the consumer on c workgroups that copies

@@ -93,7 +93,7 @@ def test_full_size_parity(wid, layer, tb):
     check_rows(t_gpu.astype(np.float64), t_ref, f"{w.name} y_share sample")
 
     say(f"[fullsize] {w.name}: sequential baseline")
-    sh.expert_forward(MOE_MODE_SEQUENTIAL)
+    sh.expert_forward(MOE_MODE_SEQUENTIAL, n_consumer_cu=c)
     sh.combine()
     torch.cuda.synchronize()
     assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits)
