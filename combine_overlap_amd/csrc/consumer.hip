@@ -5,8 +5,10 @@
 // segment's valid rows with one contiguous copy into the combine buffer of
 // the owner rank. Flags and rows are read with device-scope loads, which
 // pair with the producer's device-scope stores and completion wait (see the
-// output-projection epilogue); no L2 invalidate is issued per segment. On one GPU the owner's receive buffer is a buffer in local
-// HBM; the copy is split evenly across the c consumer workgroups.
+// output-projection epilogue); no L2 invalidate is issued per segment. On
+// one GPU the owner's receive buffer is a buffer in local HBM. The segments'
+// rows are cut into 64 KiB copy units, dealt to the c consumer workgroups in
+// batches (see k_consumer).
 //
 // Each consumer workgroup (1024 threads) also reserves enough LDS that no
 // producer workgroup can share its CU, which keeps the two partitions
@@ -29,38 +31,60 @@ constexpr int kConsumerLdsBytes = 80 * 1024;
 #define MOE_DEVICE_SCOPE_PUBLISH 1
 #endif
 
+// 64 KiB copy units per consumer batch (loads in flight per workgroup)
+#ifndef MOE_CONSUMER_BATCH
+#define MOE_CONSUMER_BATCH 4
+#endif
+constexpr int kBatchUnits = MOE_CONSUMER_BATCH;
+
 #ifndef MOE_COPY_UNROLL
 #define MOE_COPY_UNROLL 8
 #endif
 
+// 16-byte load: device-scope (sc1, two 8-byte halves) loads miss in this
+// XCD's L2 unless the line is coherent, so they see the producer's
+// write-through stores; plain loads otherwise
+// (global address space explicitly: generic "flat" atomics would each be
+// preceded by a wait for every earlier memory access of the wave)
+#define GLOBAL_AS __attribute__((address_space(1)))
+template <bool DEVICE_SCOPE>
+__device__ __forceinline__ u32x4 load16(const u32x4* a) {
+  if constexpr (DEVICE_SCOPE) {
+    const GLOBAL_AS uint64_t* s64 = (const GLOBAL_AS uint64_t*)a;
+    const uint64_t x = __hip_atomic_load(s64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t y = __hip_atomic_load(s64 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return u32x4{(uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32)};
+  } else {
+    return *(const GLOBAL_AS u32x4*)a;
+  }
+}
+
+__device__ __forceinline__ void store16_nt(u32x4* a, u32x4 v) {
+  __builtin_nontemporal_store(v, (GLOBAL_AS u32x4*)a);
+}
+
 // plain 16-byte loads (non-temporal loads halve the per-CU rate), streaming
 // stores; MOE_COPY_UNROLL loads in flight per thread
-template <bool DEVICE_SCOPE>
 __device__ __forceinline__ void copy_units(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                            size_t lo, size_t hi, int tid, int nthr) {
   constexpr int U = MOE_COPY_UNROLL;
-  auto ld = [&](size_t i) -> u32x4 {
-    if constexpr (DEVICE_SCOPE) {
-      // device-scope (sc1) loads miss in this XCD's L2 unless the line is coherent
-      const uint64_t* s64 = reinterpret_cast<const uint64_t*>(src + i);
-      const uint64_t x = __hip_atomic_load(s64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t y = __hip_atomic_load(s64 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return u32x4{(uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32)};
-    } else {
-      return src[i];
-    }
-  };
   size_t i = lo + tid;
   for (; i + (U - 1) * (size_t)nthr < hi; i += U * (size_t)nthr) {
     u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld(i + u * (size_t)nthr);
+    for (int u = 0; u < U; ++u) v[u] = src[i + u * (size_t)nthr];
 #pragma unroll
     for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], dst + i + u * (size_t)nthr);
   }
-  for (; i < hi; i += nthr) __builtin_nontemporal_store(ld(i), dst + i);
+  for (; i < hi; i += nthr) __builtin_nontemporal_store(src[i], dst + i);
 }
 
+// Workgroup w copies the batches of kBatchUnits consecutive 64 KiB copy units
+// starting at units (w + i c) kBatchUnits, i = 0, 1, ... (the units of all
+// segments in schedule order). Before a batch it makes sure that every
+// segment up to the batch's last one is ready: it polls the flags of the
+// segments past its own ready frontier, in order. Workgroups therefore never
+// wait for one another, and each keeps a whole batch of loads in flight.
 __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* __restrict__ y,
                                                                 BufPtrs bufs, moe_plan_t p,
                                                                 const uint32_t* flags,
@@ -72,24 +96,36 @@ __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* _
   if (tid == 0) { s_abort = 0; s_reserve[0] = 0; }
   __syncthreads();
   const int n_seg = p.meta[META_NSEG];
+  const int n_units = p.meta[META_NUNITS];
   const int nwg = gridDim.x, wg = blockIdx.x;
   const bool tr = trace != nullptr && wg == 0 && tid == 0;
   if (tr) trace[1] = wall_clock64();
-  for (int sgi = 0; sgi < n_seg; ++sgi) {
-    const int b0 = p.seg_band0[sgi];
-    const int nb = p.seg_nbands[sgi];
-    if (tr) trace[trace_seg + 3 * sgi] = wall_clock64();
+  constexpr size_t kUnit16 = kCopyUnitBytes / 16;                 // 16-byte words per unit
+  constexpr int kPer = (int)(kUnit16 / kConsumerThreads);          // words per thread and unit
+  int ready = 0;     // wave 0: segments [0, ready) are known to be ready
+  int seg = 0;       // segment of the unit being placed (non-decreasing)
+  for (int u0 = wg * kBatchUnits; u0 < n_units; u0 += nwg * kBatchUnits) {
+    const int u1 = min(u0 + kBatchUnits, n_units);
+    int last = seg;    // segment of unit u1 - 1
+    while (last + 1 < n_seg && p.seg_unit0[last + 1] <= u1 - 1) ++last;
     if (tid < 64) {
-      const uint32_t* f = flags + (size_t)b0 * tiles2;
-      const int nf = nb * tiles2;
-      const uint64_t t_start = wall_clock64();
-      while (true) {
-        bool ok = true;
-        for (int i = tid; i < nf; i += 64)
-          ok &= (__hip_atomic_load(f + i, MOE_DEVICE_SCOPE_PUBLISH ? __ATOMIC_RELAXED : __ATOMIC_ACQUIRE,
-                                   __HIP_MEMORY_SCOPE_AGENT) == epoch);
-        if (__ballot(!ok) == 0ull) break;
-        if (wall_clock64() - t_start > kWaitTicks) {
+      for (; ready <= last; ++ready) {
+        const int b0 = p.seg_band0[ready];
+        const uint32_t* f = flags + (size_t)b0 * tiles2;
+        const int nf = p.seg_nbands[ready] * tiles2;
+        const uint64_t t_start = wall_clock64();
+        if (tr) trace[trace_seg + 3 * ready] = t_start;
+        bool timed_out = false;
+        while (true) {
+          bool ok = true;
+          for (int i = tid; i < nf; i += 64)
+            ok &= (__hip_atomic_load(f + i, MOE_DEVICE_SCOPE_PUBLISH ? __ATOMIC_RELAXED : __ATOMIC_ACQUIRE,
+                                     __HIP_MEMORY_SCOPE_AGENT) == epoch);
+          if (__ballot(!ok) == 0ull) break;
+          if (wall_clock64() - t_start > kWaitTicks) { timed_out = true; break; }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (timed_out) {
           if (tid == 0) {
             s_abort = 1;
             int expected = 0;
@@ -99,25 +135,54 @@ __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* _
           }
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        if (tr) trace[trace_seg + 3 * ready + 1] = wall_clock64();
       }
     }
     __syncthreads();
     if (s_abort) return;
     if (!MOE_DEVICE_SCOPE_PUBLISH) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (tr) trace[trace_seg + 3 * sgi + 1] = wall_clock64();
-    const size_t units = (size_t)p.seg_rows[sgi] * H / 8;
-    const size_t per = (units + nwg - 1) / nwg;
-    const size_t lo = (size_t)wg * per;
-    const size_t hi = lo + per < units ? lo + per : units;
-    if (lo < hi) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(y + (size_t)p.seg_src_row[sgi] * H);
-      u32x4* dst = reinterpret_cast<u32x4*>(bufs.p[p.seg_dest[sgi]] + (size_t)p.seg_dst_row[sgi] * H);
-      copy_units<MOE_DEVICE_SCOPE_PUBLISH != 0>(src, dst, lo, hi, tid, kConsumerThreads);
+    // all loads of the batch, then all stores. The loads are unconditional
+    // (indices clamped into the unit; a missing unit reads row 0 of y), so the
+    // compiler keeps them all in flight; only the stores are predicated.
+    u32x4 v[kBatchUnits][kPer];
+    const u32x4* src[kBatchUnits];
+    u32x4* dst[kBatchUnits];
+    size_t lo[kBatchUnits], hi[kBatchUnits], last_ld[kBatchUnits];
+#pragma unroll
+    for (int k = 0; k < kBatchUnits; ++k) {
+      const int u = u0 + k;
+      src[k] = reinterpret_cast<const u32x4*>(y);
+      dst[k] = reinterpret_cast<u32x4*>(bufs.p[0]);
+      lo[k] = 0;
+      hi[k] = 0;
+      last_ld[k] = 0;
+      if (u < u1) {
+        while (seg + 1 < n_seg && p.seg_unit0[seg + 1] <= u) ++seg;
+        const size_t words = (size_t)p.seg_rows[seg] * H / 8;
+        lo[k] = (size_t)(u - p.seg_unit0[seg]) * kUnit16;
+        hi[k] = lo[k] + kUnit16 < words ? lo[k] + kUnit16 : words;
+        last_ld[k] = hi[k] - 1;
+        src[k] = reinterpret_cast<const u32x4*>(y + (size_t)p.seg_src_row[seg] * H);
+        dst[k] = reinterpret_cast<u32x4*>(bufs.p[p.seg_dest[seg]] + (size_t)p.seg_dst_row[seg] * H);
+      }
     }
+#pragma unroll
+    for (int k = 0; k < kBatchUnits; ++k)
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const size_t i = lo[k] + (size_t)q * kConsumerThreads + tid;
+        v[k][q] = load16<MOE_DEVICE_SCOPE_PUBLISH != 0>(src[k] + (i < last_ld[k] ? i : last_ld[k]));
+      }
+#pragma unroll
+    for (int k = 0; k < kBatchUnits; ++k)
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const size_t i = lo[k] + (size_t)q * kConsumerThreads + tid;
+        if (i < hi[k]) store16_nt(dst[k] + i, v[k][q]);
+      }
     if (trace != nullptr && wg == 0) {
       __syncthreads();
-      if (tid == 0) trace[trace_seg + 3 * sgi + 2] = wall_clock64();
+      if (tid == 0) trace[trace_seg + 3 * last + 2] = wall_clock64();
     }
   }
   if (tid == 0 && s_reserve[0] != 0) s_abort = 2;   // keeps the LDS reservation alive
@@ -143,7 +208,7 @@ __global__ __launch_bounds__(256) void k_bulk_copy(const uint16_t* __restrict__ 
     const size_t b = a + kUnit16 < units16 ? a + kUnit16 : units16;
     const u32x4* src = reinterpret_cast<const u32x4*>(y + (size_t)p.seg_src_row[sgi] * H);
     u32x4* dst = reinterpret_cast<u32x4*>(bufs.p[p.seg_dest[sgi]] + (size_t)p.seg_dst_row[sgi] * H);
-    copy_units<false>(src, dst, a, b, threadIdx.x, 256);
+    copy_units(src, dst, a, b, threadIdx.x, 256);
   }
 }
 
