@@ -24,7 +24,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 # band height per workload: the fastest measured overlapped layer step
-DEFAULT_TB = {1: 64, 2: 256, 3: 256, 4: 128, 5: 256}
+DEFAULT_TB = {1: 64, 2: 64, 3: 256, 4: 32, 5: 64}
 # sources whose change invalidates stored hardware-counter traffic figures
 GEMM_SOURCES = ("combine_overlap_amd/csrc/gemm.hip", "combine_overlap_amd/csrc/common.hpp")
 

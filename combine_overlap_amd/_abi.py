@@ -24,7 +24,8 @@ MOE_GATE_SIGMOID = 1
 MOE_MODE_OVERLAP = 0
 MOE_MODE_SEQUENTIAL = 1
 
-META_MPAD, META_NBANDS, META_NREMOTE, META_NSEG, META_STATUS, META_NUNITS = range(6)
+META_MPAD, META_NBANDS, META_NREMOTE, META_NSEG, META_STATUS, META_NUNITS, META_NTILES, \
+    META_NRTILES = range(8)
 
 
 class MoeShape(C.Structure):
@@ -34,13 +35,15 @@ class MoeShape(C.Structure):
 
 class MoeSizes(C.Structure):
     _fields_ = [("ws_bytes", C.c_size_t), ("m_pad_max", C.c_int64), ("max_bands", C.c_int32),
-                ("max_flags", C.c_int32), ("recv_rows_max", C.c_int32), ("bn_out", C.c_int32)]
+                ("max_flags", C.c_int32), ("recv_rows_max", C.c_int32), ("bn_out", C.c_int32),
+                ("tile_m", C.c_int32), ("max_tiles", C.c_int32)]
 
 
 PLAN_FIELDS = ("meta", "group_row", "expert_base", "recv_off", "band_row0", "band_expert",
                "band_dest", "band_recv0", "band_valid", "seg_band0", "seg_nbands", "seg_dest",
                "seg_src_row", "seg_dst_row", "seg_rows", "row_src", "recv_row", "chunk_base",
-               "chunk_counts", "tile_ctr", "slot_valid", "seg_unit0", "partial")
+               "chunk_counts", "tile_ctr", "slot_valid", "seg_unit0", "tile_row0", "tile_expert",
+               "tile_rows", "tile_sched", "seg_tile0", "seg_tile1", "partial")
 
 
 class MoePlan(C.Structure):

@@ -31,7 +31,7 @@ int make_geometry(const moe_shape_t* s, Geometry* g) {
     return MOE_ERR_INVALID_ARG;
   if (s->mgb < 1) return MOE_ERR_INVALID_ARG;
   if (s->H < 256 || s->H % 256 != 0 || s->F < 128 || s->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if (s->tb_m != 64 && s->tb_m != 128 && s->tb_m != 256) return MOE_ERR_UNSUPPORTED;
+  if (s->tb_m != 32 && s->tb_m != 64 && s->tb_m != 128 && s->tb_m != 256) return MOE_ERR_UNSUPPORTED;
   if (s->E > 512) return MOE_ERR_UNSUPPORTED;
   const int El = s->E / s->R;
   if (El > 256 || (int64_t)El * s->R > 2048) return MOE_ERR_UNSUPPORTED;
@@ -47,8 +47,11 @@ int make_geometry(const moe_shape_t* s, Geometry* g) {
   const int64_t m_pad_max = valid_max + (int64_t)El * s->R * (s->tb_m - 1);
   if (m_pad_max * (s->H > s->F ? s->H : s->F) >= (int64_t)1 << 40 || m_pad_max >= (int64_t)1 << 31)
     return MOE_ERR_UNSUPPORTED;
-  g->m_pad_max = ceil_div64(m_pad_max, s->tb_m) * s->tb_m;
-  g->max_bands = (int32_t)(g->m_pad_max / s->tb_m);
+  g->rows = ceil_div64(m_pad_max, s->tb_m) * s->tb_m;
+  g->max_bands = (int32_t)(g->rows / s->tb_m);
+  g->tile_m = kTileM;
+  g->m_pad_max = g->rows + g->tile_m;   // the last tile may read past the last row
+  g->max_tiles = (int32_t)(ceil_div64(g->rows, g->tile_m) + El);
   // per-shape tile table: output projection 256 wide; first projection
   // 256-wide MFMA tiles (128 h columns when gated)
   g->bn2 = 256;
@@ -57,10 +60,12 @@ int make_geometry(const moe_shape_t* s, Geometry* g) {
   else if (s->F % 256 == 0) { g->bn1 = 256; g->bn1_out = 256; }
   else { g->bn1 = 128; g->bn1_out = 128; }
   g->tiles1 = s->F / g->bn1_out;
-  const int64_t flags = (int64_t)g->max_bands * g->tiles2;
+  const int64_t flags = (int64_t)g->max_tiles * g->tiles2;
   if (flags >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   g->max_flags = (int32_t)flags;
   g->recv_rows_max = (int32_t)((int64_t)s->T * (s->k < El ? s->k : El));
+  // the consumer addresses a segment's 16-byte words with 32-bit offsets
+  if ((int64_t)g->recv_rows_max * (s->H / 8) >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -88,7 +93,10 @@ WsLayout ws_layout(const Geometry& g) {
   L.tile_ctr = take(kCtrWords);
   L.slot_valid = take(mb);
   L.seg_unit0 = take(mb);
-  L.partial = take((size_t)kXcds * kTailSlots * g.tb_m * 256);
+  L.partial = take((size_t)kXcds * kTailSlots * g.tile_m * 256);
+  const size_t mt = (size_t)g.max_tiles;
+  L.tile_row0 = take(mt); L.tile_expert = take(mt); L.tile_rows = take(mt); L.tile_sched = take(mt);
+  L.seg_tile0 = take(mb); L.seg_tile1 = take(mb);
   L.total = off;
   return L;
 }
@@ -113,6 +121,8 @@ void plan_from_ws(const Geometry& g, void* ws, moe_plan_t* p) {
   p->slot_valid = at(L.slot_valid);
   p->seg_unit0 = at(L.seg_unit0);
   p->partial = reinterpret_cast<float*>(b + L.partial);
+  p->tile_row0 = at(L.tile_row0); p->tile_expert = at(L.tile_expert); p->tile_rows = at(L.tile_rows);
+  p->tile_sched = at(L.tile_sched); p->seg_tile0 = at(L.seg_tile0); p->seg_tile1 = at(L.seg_tile1);
 }
 
 static inline bool ws_ok(const void* ws) {
@@ -151,6 +161,8 @@ int moe_query_sizes(const moe_shape_t* shape, moe_sizes_t* out) {
   out->max_flags = g.max_flags;
   out->recv_rows_max = g.recv_rows_max;
   out->bn_out = g.bn2;
+  out->tile_m = g.tile_m;
+  out->max_tiles = g.max_tiles;
   return MOE_OK;
 }
 

@@ -18,7 +18,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kChunk = 256;
 // meta words in the workspace
 enum { META_MPAD = 0, META_NBANDS = 1, META_NREMOTE = 2, META_NSEG = 3, META_STATUS = 4, META_NUNITS = 5,
-       META_WORDS = 64 };
+       META_NTILES = 6, META_NRTILES = 7, META_WORDS = 64 };
+// GEMM row-tile height: the producer computes tiles of this many rows over each
+// expert's tb_m-aligned rows, independently of the (possibly smaller) band
+constexpr int kTileM = 256;
 // segments are also cut into copy units of this many bytes (the baseline bulk copy)
 constexpr int kCopyUnitBytes = 65536;
 // per-XCD tile queues of the two GEMM launches: counter (phase, xcd) at tile_ctr[(phase*8 + xcd) * 32]
@@ -37,6 +40,9 @@ struct Geometry {
   int32_t n_chunks;           // R * chunks_per_rank
   int64_t m_pad_max;
   int32_t max_bands;
+  int64_t rows;               // packed-row bound of the band layout
+  int32_t tile_m;             // GEMM row-tile height
+  int32_t max_tiles;          // GEMM row tiles at most
   int32_t bn1;                // first projection: MFMA tile width (u and v columns for gated)
   int32_t bn1_out;            // first projection: h columns per tile
   int32_t bn2;                // output projection tile width
@@ -51,7 +57,8 @@ struct WsLayout {
   size_t meta, chunk_counts, chunk_base, group_row, expert_base, recv_off;
   size_t band_row0, band_expert, band_dest, band_recv0, band_valid;
   size_t seg_band0, seg_nbands, seg_dest, seg_src_row, seg_dst_row, seg_rows;
-  size_t row_src, recv_row, tile_ctr, slot_valid, seg_unit0, partial, total;
+  size_t row_src, recv_row, tile_ctr, slot_valid, seg_unit0, partial;
+  size_t tile_row0, tile_expert, tile_rows, tile_sched, seg_tile0, seg_tile1, total;
 };
 
 int make_geometry(const moe_shape_t* s, Geometry* g);

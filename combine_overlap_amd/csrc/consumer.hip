@@ -24,8 +24,12 @@
 namespace moe {
 
 constexpr uint64_t kWaitTicks = 200000000ull;   // 2 s at 100 MHz
-constexpr int kConsumerThreads = 1024;
+constexpr int kConsumerThreads = 1024;   // CU-partition consumer
 constexpr int kConsumerLdsBytes = 80 * 1024;
+// segment tables staged in the consumer's LDS (the reservation has room):
+// unit0 [kSegLds + 1], then rows, src_row, dst_row, dest, tile0, tile1 [kSegLds]
+constexpr int kSegLds = 2048;
+static_assert((kSegLds + 1 + 6 * kSegLds) * 4 <= kConsumerLdsBytes, "segment tables fit the reservation");
 
 #ifndef MOE_DEVICE_SCOPE_PUBLISH
 #define MOE_DEVICE_SCOPE_PUBLISH 1
@@ -79,40 +83,78 @@ __device__ __forceinline__ void copy_units(const u32x4* __restrict__ src, u32x4*
   for (; i < hi; i += nthr) __builtin_nontemporal_store(src[i], dst + i);
 }
 
-// Workgroup w copies the batches of kBatchUnits consecutive 64 KiB copy units
-// starting at units (w + i c) kBatchUnits, i = 0, 1, ... (the units of all
-// segments in schedule order). Before a batch it makes sure that every
-// segment up to the batch's last one is ready: it polls the flags of the
-// segments past its own ready frontier, in order. Workgroups therefore never
-// wait for one another, and each keeps a whole batch of loads in flight.
-__global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* __restrict__ y,
-                                                                BufPtrs bufs, moe_plan_t p,
-                                                                const uint32_t* flags,
-                                                                uint32_t epoch, uint64_t* trace,
-                                                                int trace_seg, int tiles2, int H) {
+// Workgroup w copies the batches of BATCH consecutive 64 KiB copy units
+// starting at units (w + i c) BATCH, i = 0, 1, ... (the units of all segments
+// in schedule order). Before a batch it makes sure that every segment up to
+// the batch's last one is ready: wave 0 polls the flags of the row tiles of
+// the segments past its own ready frontier, in order (consecutive segments
+// mostly share row tiles, which are polled once). Workgroups therefore never
+// wait for one another; each keeps ROUND 16-byte loads per thread in flight.
+//
+// One workgroup of NT threads per consumer CU; the segment tables are staged
+// in an LDS reservation large enough that no producer workgroup shares the CU.
+template <int NT, int BATCH, int ROUND, bool LDS_TABLES>
+__global__ __launch_bounds__(NT) void k_consumer(const uint16_t* __restrict__ y,
+                                                                    BufPtrs bufs, moe_plan_t p,
+                                                                    const uint32_t* flags,
+                                                                    uint32_t epoch, uint64_t* trace,
+                                                                    int trace_seg, int tiles2, int H) {
+  constexpr size_t kUnit16 = kCopyUnitBytes / 16;                 // 16-byte words per unit
+  constexpr int kPer = (int)(kUnit16 / NT);                        // words per thread and unit
+  constexpr int kSlots = BATCH * kPer;                             // words per thread and batch
+  static_assert(kSlots % ROUND == 0, "rounds split the batch evenly");
   __shared__ int s_abort;
-  __shared__ __attribute__((aligned(16))) uint32_t s_reserve[kConsumerLdsBytes / 4];
+  __shared__ __attribute__((aligned(16))) int s_tab[LDS_TABLES ? kConsumerLdsBytes / 4 : 1];
   const int tid = threadIdx.x;
-  if (tid == 0) { s_abort = 0; s_reserve[0] = 0; }
-  __syncthreads();
   const int n_seg = p.meta[META_NSEG];
   const int n_units = p.meta[META_NUNITS];
+  // segment tables: the first kSegLds segments from LDS, any others from global memory
+  int* t_unit0 = s_tab;
+  int* t_rows = s_tab + kSegLds + 1;
+  int* t_src = t_rows + kSegLds;
+  int* t_dst = t_src + kSegLds;
+  int* t_dest = t_dst + kSegLds;
+  int* t_t0 = t_dest + kSegLds;
+  int* t_t1 = t_t0 + kSegLds;
+  const int n_lds = LDS_TABLES ? min(n_seg, kSegLds) : 0;
+  if constexpr (LDS_TABLES) {
+    for (int i = tid; i < n_lds; i += NT) {
+      t_unit0[i] = p.seg_unit0[i];
+      t_rows[i] = p.seg_rows[i];
+      t_src[i] = p.seg_src_row[i];
+      t_dst[i] = p.seg_dst_row[i];
+      t_dest[i] = p.seg_dest[i];
+      t_t0[i] = p.seg_tile0[i];
+      t_t1[i] = p.seg_tile1[i];
+    }
+    if (tid == 0) t_unit0[n_lds] = n_lds < n_seg ? p.seg_unit0[n_lds] : n_units;
+  }
+  if (tid == 0) s_abort = 0;
+  __syncthreads();
+  auto unit0 = [&](int i) {
+    if (LDS_TABLES && i <= n_lds) return t_unit0[i];
+    return i < n_seg ? p.seg_unit0[i] : n_units;
+  };
+  auto field = [&](const int* lds, const int32_t* glob, int i) {
+    return (LDS_TABLES && i < n_lds) ? lds[i] : glob[i];
+  };
   const int nwg = gridDim.x, wg = blockIdx.x;
   const bool tr = trace != nullptr && wg == 0 && tid == 0;
   if (tr) trace[1] = wall_clock64();
-  constexpr size_t kUnit16 = kCopyUnitBytes / 16;                 // 16-byte words per unit
-  constexpr int kPer = (int)(kUnit16 / kConsumerThreads);          // words per thread and unit
-  int ready = 0;     // wave 0: segments [0, ready) are known to be ready
-  int seg = 0;       // segment of the unit being placed (non-decreasing)
-  for (int u0 = wg * kBatchUnits; u0 < n_units; u0 += nwg * kBatchUnits) {
-    const int u1 = min(u0 + kBatchUnits, n_units);
+  int ready = 0;             // wave 0: segments [0, ready) are known to be ready
+  int kt0 = 1, kt1 = 0;      // wave 0: row tiles [kt0, kt1] seen flagged (empty at first)
+  int seg = 0;               // segment of the unit being placed (non-decreasing)
+  for (int u0 = wg * BATCH; u0 < n_units; u0 += nwg * BATCH) {
+    const int u1 = min(u0 + BATCH, n_units);
     int last = seg;    // segment of unit u1 - 1
-    while (last + 1 < n_seg && p.seg_unit0[last + 1] <= u1 - 1) ++last;
+    while (last + 1 < n_seg && unit0(last + 1) <= u1 - 1) ++last;
     if (tid < 64) {
       for (; ready <= last; ++ready) {
-        const int b0 = p.seg_band0[ready];
-        const uint32_t* f = flags + (size_t)b0 * tiles2;
-        const int nf = p.seg_nbands[ready] * tiles2;
+        // every column tile of the row tiles covering the segment's bands
+        const int t0 = field(t_t0, p.seg_tile0, ready), t1 = field(t_t1, p.seg_tile1, ready);
+        if (t0 >= kt0 && t1 <= kt1) continue;
+        const uint32_t* f = flags + (size_t)t0 * tiles2;
+        const int nf = (t1 - t0 + 1) * tiles2;
         const uint64_t t_start = wall_clock64();
         if (tr) trace[trace_seg + 3 * ready] = t_start;
         bool timed_out = false;
@@ -135,21 +177,20 @@ __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* _
           }
           break;
         }
+        kt0 = t0;
+        kt1 = t1;
         if (tr) trace[trace_seg + 3 * ready + 1] = wall_clock64();
       }
     }
     __syncthreads();
     if (s_abort) return;
     if (!MOE_DEVICE_SCOPE_PUBLISH) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // all loads of the batch, then all stores. The loads are unconditional
-    // (indices clamped into the unit; a missing unit reads row 0 of y), so the
-    // compiler keeps them all in flight; only the stores are predicated.
-    u32x4 v[kBatchUnits][kPer];
-    const u32x4* src[kBatchUnits];
-    u32x4* dst[kBatchUnits];
-    size_t lo[kBatchUnits], hi[kBatchUnits], last_ld[kBatchUnits];
+    // the batch's units (a missing unit reads row 0 of y and stores nothing)
+    const u32x4* src[BATCH];
+    u32x4* dst[BATCH];
+    uint32_t lo[BATCH], hi[BATCH], last_ld[BATCH];   // 16-byte words in the segment
 #pragma unroll
-    for (int k = 0; k < kBatchUnits; ++k) {
+    for (int k = 0; k < BATCH; ++k) {
       const int u = u0 + k;
       src[k] = reinterpret_cast<const u32x4*>(y);
       dst[k] = reinterpret_cast<u32x4*>(bufs.p[0]);
@@ -157,35 +198,42 @@ __global__ __launch_bounds__(kConsumerThreads) void k_consumer(const uint16_t* _
       hi[k] = 0;
       last_ld[k] = 0;
       if (u < u1) {
-        while (seg + 1 < n_seg && p.seg_unit0[seg + 1] <= u) ++seg;
-        const size_t words = (size_t)p.seg_rows[seg] * H / 8;
-        lo[k] = (size_t)(u - p.seg_unit0[seg]) * kUnit16;
-        hi[k] = lo[k] + kUnit16 < words ? lo[k] + kUnit16 : words;
+        while (seg + 1 < n_seg && unit0(seg + 1) <= u) ++seg;
+        const uint32_t words = (uint32_t)field(t_rows, p.seg_rows, seg) * (uint32_t)(H / 8);
+        lo[k] = (uint32_t)(u - unit0(seg)) * (uint32_t)kUnit16;
+        hi[k] = lo[k] + (uint32_t)kUnit16 < words ? lo[k] + (uint32_t)kUnit16 : words;
         last_ld[k] = hi[k] - 1;
-        src[k] = reinterpret_cast<const u32x4*>(y + (size_t)p.seg_src_row[seg] * H);
-        dst[k] = reinterpret_cast<u32x4*>(bufs.p[p.seg_dest[seg]] + (size_t)p.seg_dst_row[seg] * H);
+        src[k] = reinterpret_cast<const u32x4*>(y + (size_t)field(t_src, p.seg_src_row, seg) * H);
+        dst[k] = reinterpret_cast<u32x4*>(bufs.p[field(t_dest, p.seg_dest, seg)] +
+                                          (size_t)field(t_dst, p.seg_dst_row, seg) * H);
       }
     }
+    // rounds of ROUND loads per thread: the loads are unconditional (indices
+    // clamped into the unit) so the compiler keeps them all in flight; only
+    // the stores are predicated
 #pragma unroll
-    for (int k = 0; k < kBatchUnits; ++k)
+    for (int z0 = 0; z0 < kSlots; z0 += ROUND) {
+      u32x4 v[ROUND];
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const size_t i = lo[k] + (size_t)q * kConsumerThreads + tid;
-        v[k][q] = load16<MOE_DEVICE_SCOPE_PUBLISH != 0>(src[k] + (i < last_ld[k] ? i : last_ld[k]));
+      for (int z = 0; z < ROUND; ++z) {
+        const int k = (z0 + z) / kPer, q = (z0 + z) % kPer;
+        const uint32_t i = lo[k] + (uint32_t)(q * NT + tid);
+        v[z] = load16<MOE_DEVICE_SCOPE_PUBLISH != 0>(src[k] + (i < last_ld[k] ? i : last_ld[k]));
       }
 #pragma unroll
-    for (int k = 0; k < kBatchUnits; ++k)
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const size_t i = lo[k] + (size_t)q * kConsumerThreads + tid;
-        if (i < hi[k]) store16_nt(dst[k] + i, v[k][q]);
+      for (int z = 0; z < ROUND; ++z) {
+        const int k = (z0 + z) / kPer, q = (z0 + z) % kPer;
+        const uint32_t i = lo[k] + (uint32_t)(q * NT + tid);
+        if (i < hi[k]) store16_nt(dst[k] + i, v[z]);
       }
+    }
     if (trace != nullptr && wg == 0) {
       __syncthreads();
       if (tid == 0) trace[trace_seg + 3 * last + 2] = wall_clock64();
     }
   }
-  if (tid == 0 && s_reserve[0] != 0) s_abort = 2;   // keeps the LDS reservation alive
+  if constexpr (LDS_TABLES)   // keeps the whole reservation
+    if (tid == 0 && s_tab[kConsumerLdsBytes / 4 - 1] == 0x7fffffff) s_abort = 2;
 }
 
 // baseline: all remote segments after the producer, on all CUs. The segments
@@ -215,8 +263,9 @@ __global__ __launch_bounds__(256) void k_bulk_copy(const uint16_t* __restrict__ 
 hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
                            const uint32_t* flags, uint32_t epoch, uint64_t* trace, int n_wg,
                            hipStream_t st) {
-  hipLaunchKernelGGL(k_consumer, dim3(n_wg), dim3(kConsumerThreads), 0, st, y, bufs, p, flags,
-                     epoch, trace, 8 + g.max_flags, g.tiles2, g.H);
+  hipLaunchKernelGGL((k_consumer<kConsumerThreads, kBatchUnits, 16, true>), dim3(n_wg),
+                     dim3(kConsumerThreads), 0, st, y, bufs, p, flags, epoch, trace, 8 + g.max_flags,
+                     g.tiles2, g.H);
   return hipGetLastError();
 }
 

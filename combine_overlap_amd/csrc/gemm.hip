@@ -1,14 +1,21 @@
 // Producer: the rank-wide persistent grouped GEMM of the tile-signalling
 // overlap paper (sec. 3.3.1). One launch covers every local expert through
-// one tile worklist: tile t = (row band t / tiles_n, column tile t % tiles_n)
-// with bands in the remote-first schedule order (sec. 3.2.2). The expert of
-// a band selects the weight pointer; no matrices are concatenated and
-// nothing is relaunched per expert.
+// one tile worklist: tile t = (row tile at schedule position t / tiles_n,
+// column tile t % tiles_n), row tiles in the remote-first schedule order
+// (sec. 3.2.2). The expert of a row tile selects the weight pointer; no
+// matrices are concatenated and nothing is relaunched per expert.
+//
+// Row tiles are 256 rows of one expert's tb_m-aligned rows, whatever the
+// band height tb_m (the padding and transfer unit of the row layout): the
+// last tile of an expert is shorter and stores only its own rows (the rows
+// past them, read from the next expert or the buffer's slack, are computed
+// and discarded). The paper ties the tile to the band; here a small band
+// keeps the owner-group padding small while the tile stays at the size that
+// runs the MFMA pipes best.
 //
 // gfx950 mapping
-//  * Tile queues per XCD: tile t belongs to XCD t % 8, so each XCD's L2 sees
-//    a fixed subset of column tiles (weight slices) and the bands in schedule
-//    order. A workgroup reads its XCD from HW_REG_XCC_ID and takes the next
+//  * Tile queues per XCD: each XCD's L2 sees a fixed subset of column tiles
+//    (weight slices) and of row tiles, in schedule order. A workgroup reads its XCD from HW_REG_XCC_ID and takes the next
 //    tile of that XCD's queue with one atomic; when the queue is empty it
 //    steals from the other queues. Any grid size and any placement of the
 //    consumer's CUs therefore keeps every producer CU busy.
@@ -92,8 +99,10 @@ struct GemmArgs {
   const uint16_t* B1;          // [El, Nw, K] (gated only)
   uint16_t* C;                 // [rows, Nout]
   const int32_t* meta;
-  const int32_t* band_row0;
-  const int32_t* band_expert;
+  const int32_t* tile_row0;    // row tiles in layout order: first row, expert, rows
+  const int32_t* tile_expert;
+  const int32_t* tile_rows;
+  const int32_t* tile_sched;   // schedule position -> row tile
   int32_t* my_ctr;             // this launch's 8 per-XCD queue counters
   int32_t* other_ctr;          // the other launch's counters (zeroed here)
   float* partial;              // fp32 partial tiles of split tail tiles, [8 * kTailSlots][BM * BN]
@@ -101,25 +110,25 @@ struct GemmArgs {
   uint64_t* trace;             // optional timeline: [0] start, [8 + t] tile t done
   uint32_t epoch;
   int K, Nw, Nout, tiles_n;
-  int xb, xn;                  // XCD grid: xcd = (band % xb) * xn + (column tile % xn)
-  int gp, gq;                  // blocks of gp bands x gq column tiles inside an XCD queue
+  int xb, xn;                  // XCD grid: xcd = (row tile % xb) * xn + (column tile % xn)
+  int gp, gq;                  // blocks of gp row tiles x gq column tiles inside an XCD queue
   int px;                      // workgroups per XCD queue the tail split is sized for
 };
 
-// Queue index i of XCD x -> tile (band-major schedule index * tiles_n + column tile).
-// XCD x owns bands b = bx + k*xb and column tiles t = nx + l*xn; its queue walks
-// blocks of gp bands x gq column tiles (bands in schedule order, so remote bands
-// still finish first) so that the ~32 tiles an XCD runs at once share A bands
+// Queue index i of XCD x -> tile (row-tile schedule position * tiles_n + column tile).
+// XCD x owns row tiles b = bx + k*xb and column tiles t = nx + l*xn; its queue walks
+// blocks of gp row tiles x gq column tiles (in schedule order, so remote rows
+// still finish first) so that the ~32 tiles an XCD runs at once share A rows
 // and weight columns in its L2. Returns -1 past the end of the queue.
-__device__ __forceinline__ int queue_tile(const GemmArgs& a, int n_bands, int x, int i) {
+__device__ __forceinline__ int queue_tile(const GemmArgs& a, int n_rt, int x, int i) {
   const int bx = x / a.xn, nx = x - (x / a.xn) * a.xn;
-  if (bx >= n_bands || nx >= a.tiles_n) return -1;
-  const int nb = (n_bands - bx + a.xb - 1) / a.xb;      // bands of this XCD
+  if (bx >= n_rt || nx >= a.tiles_n) return -1;
+  const int nb = (n_rt - bx + a.xb - 1) / a.xb;         // row tiles of this XCD
   const int nn = (a.tiles_n - nx + a.xn - 1) / a.xn;    // column tiles of this XCD
   if (i >= nb * nn) return -1;
   const int per_group = a.gp * nn;
   const int g = i / per_group;
-  const int pg = min(a.gp, nb - g * a.gp);              // bands in this group
+  const int pg = min(a.gp, nb - g * a.gp);              // row tiles in this group
   const int rem = i - g * per_group;
   const int h = rem / (pg * a.gq);
   const int qh = min(a.gq, nn - h * a.gq);              // column tiles in this block
@@ -137,11 +146,11 @@ struct Item {
   int tile, chunk, nsplit, slot;
 };
 
-__device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_bands, int x, int i, int px, int nk) {
+__device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int x, int i, int px, int nk) {
   Item it{-1, 0, 1, 0};
   const int bx = x / a.xn, nx = x - (x / a.xn) * a.xn;
-  if (bx >= n_bands || nx >= a.tiles_n) return it;
-  const int nb = (n_bands - bx + a.xb - 1) / a.xb;
+  if (bx >= n_rt || nx >= a.tiles_n) return it;
+  const int nb = (n_rt - bx + a.xb - 1) / a.xb;
   const int nn = (a.tiles_n - nx + a.xn - 1) / a.xn;
   const int T = nb * nn;
   const int tail = T % px;
@@ -149,17 +158,17 @@ __device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_bands, int x
   s = min(s, min(kMaxSplit, nk / kMinSplitSteps));
   if (tail * s > kTailSlots) s = kTailSlots / tail;
   if (s < 2) {
-    if (i < T) it.tile = queue_tile(a, n_bands, x, i);
+    if (i < T) it.tile = queue_tile(a, n_rt, x, i);
     return it;
   }
   const int full = T - tail;
   if (i < full) {
-    it.tile = queue_tile(a, n_bands, x, i);
+    it.tile = queue_tile(a, n_rt, x, i);
     return it;
   }
   const int j = i - full;
   if (j >= tail * s) return it;
-  it.tile = queue_tile(a, n_bands, x, full + j / s);
+  it.tile = queue_tile(a, n_rt, x, full + j / s);
   it.chunk = j % s;
   it.nsplit = s;
   it.slot = j;
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     }
   }
 
-  const int n_bands = a.meta[META_NBANDS];
+  const int n_rt = a.meta[META_NTILES];   // row tiles, in schedule positions
   int q = xcc_id(), tried = 0;
   while (true) {
     if (tid == 0) {
@@ -256,7 +265,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       while (tried < kXcds) {
         const int i = __hip_atomic_fetch_add(a.my_ctr + q * kCtrStride, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-        it = queue_item(a, n_bands, q, i, px, nk);
+        it = queue_item(a, n_rt, q, i, px, nk);
         if (it.tile >= 0) break;
         q = (q + 1) & (kXcds - 1);
         ++tried;
@@ -277,10 +286,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     const int nkc = (chunk + 1) * nk / nsplit - kb;
 
     const int tile_u = __builtin_amdgcn_readfirstlane(tile);
-    const int band = tile_u / a.tiles_n;
-    const int tn = tile_u - band * a.tiles_n;
-    const int row0 = a.band_row0[band];
-    const int e = a.band_expert[band];
+    const int st = tile_u / a.tiles_n;           // schedule position of the row tile
+    const int tn = tile_u - st * a.tiles_n;
+    const int rt = a.tile_sched[st];             // row tile (layout order)
+    const int row0 = a.tile_row0[rt];
+    const int e = a.tile_expert[rt];
+    const int vrows = a.tile_rows[rt];           // rows to store (the rest is the next expert's)
+    const int fidx = rt * a.tiles_n + tn;        // flag / trace index
 
     // wave-uniform global bases of this wave's DMA instructions (k offset added per stage)
     const char* abase[C::A_PW];
@@ -484,7 +496,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     uint16_t* cbase = a.C + (size_t)row0 * a.Nout + (size_t)tn * OUTW;
     const bool signal = (EPI == EPI_PLAIN) && a.flags != nullptr;
 #pragma unroll 4
-    for (int q = tid; q < BM * CH; q += C::NT) {
+    for (int q = tid; q < vrows * CH; q += C::NT) {
       const int m = q / CH, cc = q - (q / CH) * CH;
       const u32x4 v = *reinterpret_cast<const u32x4*>(lds + m * LROW + cc * 8);
       uint16_t* dst = cbase + (size_t)m * a.Nout + cc * 8;
@@ -506,17 +518,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       // all of this thread's device-scope stores have completed
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (tid == 0) __hip_atomic_store(a.flags + tile, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(a.flags + fidx, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #else
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __syncthreads();
       if (tid == 0)
-        __hip_atomic_store(a.flags + tile, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.flags + fidx, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 #endif
     }
     if (EPI == EPI_PLAIN && a.trace != nullptr) {
       if (!signal) __syncthreads();
-      if (tid == 0) a.trace[8 + tile] = wall_clock64();
+      if (tid == 0) a.trace[8 + fidx] = wall_clock64();
     }
   }
 }
@@ -536,7 +548,7 @@ static inline void set_xcd_grid(GemmArgs& a) {
   a.gp = 32 / a.gq;
 }
 
-// per-shape tile table (tile height = band height tb_m; BN from the geometry).
+// per-shape tile table (row tiles of kTileM rows; BN from the geometry).
 // 8 waves (two per SIMD) let one wave's MFMAs cover the other's LDS and DMA
 // waits; measured on MI355X for the Mixtral-shaped projections.
 template <int EPI>
@@ -544,10 +556,6 @@ static hipError_t dispatch(GemmArgs a, int bm, int bn, int grid, hipStream_t st)
   set_xcd_grid(a);
   if (bm == 256 && bn == 256) return launch_t<256, 256, 64, 2, 4, 2, EPI>(a, grid, st);
   if (bm == 256 && bn == 128) return launch_t<256, 128, 64, 3, 4, 2, EPI>(a, grid, st);
-  if (bm == 128 && bn == 256) return launch_t<128, 256, 64, 3, 2, 4, EPI>(a, grid, st);
-  if (bm == 128 && bn == 128) return launch_t<128, 128, 64, 4, 4, 2, EPI>(a, grid, st);
-  if (bm == 64 && bn == 256) return launch_t<64, 256, 64, 3, 2, 4, EPI>(a, grid, st);
-  if (bm == 64 && bn == 128) return launch_t<64, 128, 64, 4, 2, 2, EPI>(a, grid, st);
   return hipErrorInvalidValue;
 }
 
@@ -560,8 +568,10 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_
   a.B1 = w3;
   a.C = h;
   a.meta = p.meta;
-  a.band_row0 = p.band_row0;
-  a.band_expert = p.band_expert;
+  a.tile_row0 = p.tile_row0;
+  a.tile_expert = p.tile_expert;
+  a.tile_rows = p.tile_rows;
+  a.tile_sched = p.tile_sched;
   a.my_ctr = p.tile_ctr;
   a.other_ctr = p.tile_ctr + kXcds * kCtrStride;
   a.partial = p.partial;
@@ -573,8 +583,8 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_
   a.Nout = g.F;
   a.tiles_n = g.tiles1;
   a.px = grid / kXcds;
-  return g.gated ? dispatch<EPI_GATED>(a, g.tb_m, g.bn1, grid, st)
-                 : dispatch<EPI_SILU>(a, g.tb_m, g.bn1, grid, st);
+  return g.gated ? dispatch<EPI_GATED>(a, g.tile_m, g.bn1, grid, st)
+                 : dispatch<EPI_SILU>(a, g.tile_m, g.bn1, grid, st);
 }
 
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
@@ -586,8 +596,10 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
   a.B1 = nullptr;
   a.C = y;
   a.meta = p.meta;
-  a.band_row0 = p.band_row0;
-  a.band_expert = p.band_expert;
+  a.tile_row0 = p.tile_row0;
+  a.tile_expert = p.tile_expert;
+  a.tile_rows = p.tile_rows;
+  a.tile_sched = p.tile_sched;
   a.my_ctr = p.tile_ctr + kXcds * kCtrStride;
   a.other_ctr = p.tile_ctr;
   a.partial = p.partial;
@@ -599,7 +611,7 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
   a.Nout = g.H;
   a.tiles_n = g.tiles2;
   a.px = split_grid / kXcds;
-  return dispatch<EPI_PLAIN>(a, g.tb_m, g.bn2, grid, st);
+  return dispatch<EPI_PLAIN>(a, g.tile_m, g.bn2, grid, st);
 }
 
 }  // namespace moe

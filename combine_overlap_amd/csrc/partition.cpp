@@ -8,13 +8,16 @@
 //
 // Model (its form is not given on the pages; this is the plainest one that
 // uses only the routing counts and measured rates). For c consumer CUs:
-//  * the output projection runs on P = n_cu - c CUs; every tile (tb_m x 256
-//    columns, K = F) takes t_tile = 2 tb_m 256 F / rate(M_e) on one CU, with
-//    rate(M) = gemm_flops_per_cu * M / (M + gemm_m_half) for an expert of M
-//    rows; tiles run in waves of P in schedule order (remote bands first,
-//    experts by remote band count, then rows, then id), so band b is ready when
-//    the wave holding its last tile ends; a partial last wave of n tiles lasts
-//    max(n / P, 1/3) of a full one (fewer tiles share the memory bandwidth);
+//  * the output projection runs on P = n_cu - c CUs; every tile (256 rows of
+//    one expert's tb_m-aligned rows x 256 columns, K = F; a short last row
+//    tile costs a full one) takes t_tile = 2 256 256 F / rate(M_e) on one CU,
+//    with rate(M) = gemm_flops_per_cu * M / (M + gemm_m_half) for an expert of
+//    M rows; tiles run in waves of P in schedule order (row tiles holding a
+//    remote band first, experts by remote band count, then rows, then id; then
+//    the other row tiles by expert), so a band is ready when the wave holding
+//    the last column tile of its row tile ends; a partial last wave of n tiles
+//    lasts max(n / P, 1/3) of a full one (fewer tiles share the memory
+//    bandwidth);
 //  * the consumer copies the segments in order, each when its bands are ready
 //    and the previous copy is done, at BW(c) = min(c * copy_bw_per_cu,
 //    copy_bw_max) plus seg_latency_s per segment;
@@ -35,8 +38,11 @@
 
 namespace {
 
+constexpr int kTileRows = 256;   // GEMM row-tile height
+
 struct Band {
   int expert;
+  long rel;        // first row relative to the expert's base
   int rows;        // valid rows
   bool group_end;  // last band of its (expert, owner) group
 };
@@ -89,20 +95,40 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
     if (rr[a] != rr[b]) return rr[a] > rr[b];
     return a < b;
   });
+  // remote bands in schedule order (the consumer's order)
   std::vector<Band> bands;
-  for (int e : order)
+  for (int e : order) {
+    long rel = 0;
     for (int q = 0; q < R; ++q) {
       if (q == self) continue;
       const long c = counts[e * R + q];
       const long nb = (c + tb - 1) / tb;
-      for (long i = 0; i < nb; ++i) bands.push_back(Band{e, (int)std::min<long>(tb, c - i * tb), i == nb - 1});
+      for (long i = 0; i < nb; ++i)
+        bands.push_back(Band{e, rel + i * tb, (int)std::min<long>(tb, c - i * tb), i == nb - 1});
+      rel += nb * tb;
     }
-  const size_t n_remote = bands.size();
-  for (int e = 0; e < El; ++e) {
-    const long c = counts[e * R + self];
-    const long nb = (c + tb - 1) / tb;
-    for (long i = 0; i < nb; ++i) bands.push_back(Band{e, (int)std::min<long>(tb, c - i * tb), i == nb - 1});
   }
+  const size_t n_remote = bands.size();
+  // row tiles in schedule order: those reaching into the remote groups first
+  // (experts in band order), then the rest by expert id
+  std::vector<int> t_exp, t_idx;
+  std::vector<long> t_first(El + 1, 0);
+  for (int e = 0; e < El; ++e) {
+    const long alg = (m_e[e] + tb - 1) / tb * tb;
+    t_first[e + 1] = t_first[e] + (alg + kTileRows - 1) / kTileRows;
+  }
+  std::vector<long> remote_rows(El, 0);
+  for (int e = 0; e < El; ++e) remote_rows[e] = rb[e] * tb;
+  for (int e : order)
+    for (long j = 0; j < (remote_rows[e] + kTileRows - 1) / kTileRows; ++j) {
+      t_exp.push_back(e);
+      t_idx.push_back((int)j);
+    }
+  for (int e = 0; e < El; ++e)
+    for (long j = (remote_rows[e] + kTileRows - 1) / kTileRows; j < t_first[e + 1] - t_first[e]; ++j) {
+      t_exp.push_back(e);
+      t_idx.push_back((int)j);
+    }
 
   const double band_bytes = 2.0 * tb * (double)s->H;
   const int g = band_bytes < 0.5 * 1048576.0 ? 2 : 1;
@@ -110,12 +136,12 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
   std::vector<double> t_tile(El);
   for (int e = 0; e < El; ++e) {
     const double m = (double)std::max<long>(m_e[e], 1);
-    t_tile[e] = 2.0 * tb * 256.0 * (double)s->F / (k.gemm_flops_per_cu * m / (m + k.gemm_m_half));
+    t_tile[e] = 2.0 * kTileRows * 256.0 * (double)s->F / (k.gemm_flops_per_cu * m / (m + k.gemm_m_half));
   }
+  std::vector<double> tile_done((size_t)t_first[El], 0.0);
 
   double best_t = INFINITY;
   int best_c = k.c_min;
-  std::vector<double> ready(bands.size(), 0.0);
   std::vector<size_t> pending;
   for (int c = k.c_min; c <= k.c_max; c += k.c_step) {
     const long P = k.n_cu - c;
@@ -123,23 +149,24 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
     double t = 0.0, wave_len = 0.0;
     long in_wave = 0;
     pending.clear();
-    for (size_t b = 0; b < bands.size(); ++b) {
+    for (size_t r = 0; r < t_exp.size(); ++r) {
+      const size_t id = (size_t)(t_first[t_exp[r]] + t_idx[r]);
       for (int j = 0; j < tiles2; ++j) {
-        wave_len = std::max(wave_len, t_tile[bands[b].expert]);
+        wave_len = std::max(wave_len, t_tile[t_exp[r]]);
         if (++in_wave == P) {
           t += wave_len;
-          for (size_t q : pending) ready[q] = t;
+          for (size_t q : pending) tile_done[q] = t;
           pending.clear();
           in_wave = 0;
           wave_len = 0.0;
-          if (j == tiles2 - 1) ready[b] = t;
+          if (j == tiles2 - 1) tile_done[id] = t;
         }
       }
-      if (in_wave != 0) pending.push_back(b);
+      if (in_wave != 0) pending.push_back(id);
     }
     if (in_wave > 0) {
       t += wave_len * std::max((double)in_wave / (double)P, 1.0 / 3.0);
-      for (size_t q : pending) ready[q] = t;
+      for (size_t q : pending) tile_done[q] = t;
     }
     const double t_prod = t;
     // consumer: segments of 1, g, ..., g, 1 bands per group, copied in order
@@ -155,7 +182,7 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
         double rows = 0.0, rdy = 0.0;
         for (size_t q = p; q < p + sz; ++q) {
           rows += bands[q].rows;
-          rdy = std::max(rdy, ready[q]);
+          rdy = std::max(rdy, tile_done[(size_t)(t_first[bands[q].expert] + bands[q].rel / kTileRows)]);
         }
         tc = std::max(tc, rdy) + 2.0 * rows * (double)s->H / bw + k.seg_latency_s;
         p += sz;

@@ -12,6 +12,12 @@
 // (remote band count desc, remote rows desc, id asc), their remote bands in
 // layout order, then all local bands by expert id. Segments per (expert,
 // destination) group: 1 band, middle segments of mgb bands, 1 band.
+//
+// GEMM row tiles (independent of the band height): expert e's tb_m-aligned
+// rows are cut into tiles of kTileM rows from its base (the last one shorter).
+// GEMM schedule: every tile that holds a remote band, experts in the band
+// schedule's order, then the remaining tiles by expert id. A segment's rows
+// lie in one expert, so the tiles covering it are consecutive.
 #include "common.hpp"
 
 namespace moe {
@@ -35,6 +41,9 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
   __shared__ int s_alg[kPlanMaxEl];          // tb-aligned rows of expert e
   __shared__ int s_nrb[kPlanMaxEl], s_nrr[kPlanMaxEl], s_nlb[kPlanMaxEl], s_order[kPlanMaxEl];
   __shared__ int s_nseg;
+  __shared__ int s_tbase[kPlanMaxEl + 1];   // first row tile of expert e
+  __shared__ int s_trpos[kPlanMaxEl];       // schedule position of e's first remote tile
+  __shared__ int s_tlpos[kPlanMaxEl];       // schedule position of e's first local-only tile
   __shared__ int s_usum[1024];
   const int tid = threadIdx.x;
   const int G = El * R;
@@ -97,6 +106,22 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
       s_segoff[e * R + r_self] = -1;
       band += s_nlb[e];
     }
+    // GEMM row tiles: layout ids, then schedule positions
+    int nt = 0;
+    for (int e = 0; e < El; ++e) { s_tbase[e] = nt; nt += ceil_div(s_alg[e], kTileM); }
+    s_tbase[El] = nt;
+    int pos = 0;
+    for (int o = 0; o < El; ++o) {
+      const int e = s_order[o];
+      s_trpos[e] = pos;
+      pos += ceil_div(s_rel[e * R + r_self], kTileM);   // tiles reaching into the remote groups
+    }
+    p.meta[META_NRTILES] = pos;
+    for (int e = 0; e < El; ++e) {
+      s_tlpos[e] = pos;
+      pos += ceil_div(s_alg[e], kTileM) - ceil_div(s_rel[e * R + r_self], kTileM);
+    }
+    p.meta[META_NTILES] = nt;
     p.meta[META_MPAD] = acc;
     p.meta[META_NBANDS] = band;
     p.meta[META_NREMOTE] = n_remote;
@@ -107,6 +132,16 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
   __syncthreads();
   for (int i = tid; i < kCtrWords; i += blockDim.x) p.tile_ctr[i] = 0;
   for (int e = tid; e <= El; e += blockDim.x) p.expert_base[e] = s_base[e];
+  for (int e = tid; e < El; e += blockDim.x) {
+    const int nt = ceil_div(s_alg[e], kTileM), nrt = ceil_div(s_rel[e * R + r_self], kTileM);
+    for (int j = 0; j < nt; ++j) {
+      const int t = s_tbase[e] + j;
+      p.tile_row0[t] = s_base[e] + j * kTileM;
+      p.tile_expert[t] = e;
+      p.tile_rows[t] = min(kTileM, s_alg[e] - j * kTileM);
+      p.tile_sched[j < nrt ? s_trpos[e] + j : s_tlpos[e] + (j - nrt)] = t;
+    }
+  }
   for (int s = tid; s < R; s += blockDim.x) {   // receive offsets: (expert, token) order
     int acc = 0;
     for (int e = 0; e < El; ++e) { p.recv_off[s * El + e] = acc; acc += s_cnt[e * R + s]; }
@@ -146,6 +181,8 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
         p.seg_src_row[sidx] = row0 + j * tb;
         p.seg_dst_row[sidx] = recv0 + j * tb;
         p.seg_rows[sidx] = rows;
+        p.seg_tile0[sidx] = s_tbase[e] + (row0 + j * tb - s_base[e]) / kTileM;
+        p.seg_tile1[sidx] = s_tbase[e] + (row0 + (j + sz) * tb - 1 - s_base[e]) / kTileM;
         ++sidx;
         j += sz;
       }

@@ -178,6 +178,13 @@ class MoEShare:
             out[f] = arr(f, n_bands)
         for f in ("seg_band0", "seg_nbands", "seg_dest", "seg_src_row", "seg_dst_row", "seg_rows"):
             out[f] = arr(f, n_seg)
+        n_tiles = int(meta[_abi.META_NTILES])
+        out["n_tiles"] = n_tiles
+        out["n_remote_tiles"] = int(meta[_abi.META_NRTILES])
+        for f in ("tile_row0", "tile_expert", "tile_rows", "tile_sched"):
+            out[f] = arr(f, n_tiles)
+        for f in ("seg_tile0", "seg_tile1"):
+            out[f] = arr(f, n_seg)
         out["row_src"] = arr("row_src", m_pad)
         out["recv_row"] = arr("recv_row", self.R * self.T * self.k).reshape(self.R * self.T, self.k)
         return out

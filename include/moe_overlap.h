@@ -70,7 +70,11 @@ enum { MOE_MODE_OVERLAP = 0, MOE_MODE_SEQUENTIAL = 1 };
  *  gated    1: y = (SiLU(x W1^T) * (x W3^T)) W2^T;  0: y = SiLU(x W1^T) W2^T
  *  gate_kind MOE_GATE_SOFTMAX: softmax over the k selected logits;
  *           MOE_GATE_SIGMOID: sigmoid of the k selected logits, normalised to sum 1
- *  tb_m     GEMM tile height = row-band height ([TLS] sec. 3.2.1): 64, 128 or 256
+ *  tb_m     row-band height ([TLS] sec. 3.2.1): the padding unit of the owner
+ *           groups and the transfer unit of the combine plan: 32, 64, 128 or
+ *           256. The GEMMs run tiles of moe_sizes_t.tile_m (256) rows over
+ *           each expert's tb_m-aligned rows, so the band can be smaller than
+ *           the compute tile.
  *  mgb      row bands per middle transfer segment ([TLS] sec. 3.3.2, Fig. 3(b)), >= 1
  */
 typedef struct {
@@ -79,23 +83,30 @@ typedef struct {
   int32_t tb_m, mgb;
 } moe_shape_t;
 
-/* Buffer sizes for a shape. Rows of x_perm / h / y_perm are bounded by
- * m_pad_max = min(R*T*k, R*T*E/R) + (E/R)*R*(tb_m-1) (each remote owner group is
- * padded by < tb_m rows and each expert's rows are placed tb_m-aligned). */
+/* Buffer sizes for a shape. Packed rows are bounded by
+ * rows = min(R*T*k, R*T*E/R) + (E/R)*R*(tb_m-1) rounded up to tb_m (each remote
+ * owner group is padded by < tb_m rows and each expert's rows are placed
+ * tb_m-aligned); the row buffers carry tile_m more rows, which the last GEMM
+ * tile of the last expert may read (never write). */
 typedef struct {
   size_t  ws_bytes;       /* workspace bytes (256-byte aligned pointer required) */
-  int64_t m_pad_max;      /* rows to allocate for x_perm [.,H], h [.,F], y_perm [.,H] */
-  int32_t max_bands;      /* = m_pad_max / tb_m */
-  int32_t max_flags;      /* uint32 ready flags the overlapped forward may write */
+  int64_t m_pad_max;      /* rows to allocate for x_perm [.,H], h [.,F], y_perm [.,H]:
+                             rows + tile_m */
+  int32_t max_bands;      /* = rows / tb_m */
+  int32_t max_flags;      /* uint32 ready flags the overlapped forward may write
+                             (max_tiles * H / bn_out) */
   int32_t recv_rows_max;  /* rows to allocate per combine buffer: T*min(k, E/R) */
-  int32_t bn_out;         /* tile width of the output projection (flags per band) */
+  int32_t bn_out;         /* column-tile width of the output projection */
+  int32_t tile_m;         /* GEMM row-tile height (256) */
+  int32_t max_tiles;      /* GEMM row tiles at most: ceil(rows / tile_m) + E/R */
 } moe_sizes_t;
 
 /* Read-only device views into a workspace after moe_permute (for inspection
  * and tests). Arrays indexed by band / segment are in schedule order. */
 typedef struct {
   int32_t* meta;          /* [0]=m_pad [1]=n_bands [2]=n_remote_bands [3]=n_segments
-                             [4]=device status (0 or MOE_ERR_*) [5]=64 KiB copy units */
+                             [4]=device status (0 or MOE_ERR_*) [5]=64 KiB copy units
+                             [6]=GEMM row tiles [7]=tiles holding a remote band     */
   int32_t* group_row;     /* [E_l*R] first packed row of group (e, s)                */
   int32_t* expert_base;   /* [E_l+1] first packed row of expert e, tb_m-aligned      */
   int32_t* recv_off;      /* [R*E_l] first row of (e, s) in rank s's combine buffer */
@@ -118,6 +129,17 @@ typedef struct {
   int32_t* tile_ctr;      /* internal: per-XCD tile queue counters of the two GEMMs   */
   int32_t* slot_valid;    /* [max_bands] valid rows of the band starting at row tb_m*i */
   int32_t* seg_unit0;     /* [max_bands] internal: first 64 KiB copy unit of each segment */
+  int32_t* tile_row0;     /* [max_tiles] GEMM row tile i (layout order: experts by id,
+                             tile_m rows each from the expert's base): first packed row */
+  int32_t* tile_expert;   /* [max_tiles] its local expert                               */
+  int32_t* tile_rows;     /* [max_tiles] its rows inside the expert's tb_m-aligned rows
+                             (tile_m except for an expert's last tile); rows past these
+                             are computed from the next rows but never stored            */
+  int32_t* tile_sched;    /* [max_tiles] tile at each position of the GEMM schedule:
+                             tiles holding any remote band first (experts in the band
+                             schedule's order), then the others by expert id            */
+  int32_t* seg_tile0;     /* [max_bands] first tile covering the segment's bands       */
+  int32_t* seg_tile1;     /* [max_bands] last tile covering the segment's bands        */
   float*   partial;       /* internal: fp32 partial tiles of the GEMMs' K-split tail tiles */
 } moe_plan_t;
 

@@ -92,3 +92,43 @@ def assert_plan_equal(got: dict, want: dict):
         else:
             g = np.asarray(g).reshape(np.shape(v))
             assert np.array_equal(g, np.asarray(v)), f"plan field {key} differs"
+
+
+def check_row_tiles(plan: dict, res: om.ShareResult, tile_m: int):
+    """The GEMM's row tiles (an implementation choice, not part of the method):
+    they cut every expert's tb_m-aligned rows into tile_m pieces in layout
+    order; the schedule is a permutation that lists every tile holding a
+    remote band first (experts in the band schedule's order), then the rest by
+    expert; every segment's tile range covers exactly its bands' rows."""
+    lay, bd, sg = res.layout, res.bands, res.segs
+    tb = lay.tb_m
+    row0, ex, rows = plan["tile_row0"], plan["tile_expert"], plan["tile_rows"]
+    want = []
+    for e in range(lay.E_l):
+        base = int(lay.expert_base[e])
+        alg = -(-int(lay.M_e[e]) // tb) * tb
+        for j in range(-(-alg // tile_m)):
+            want.append((base + j * tile_m, e, min(tile_m, alg - j * tile_m)))
+    got = list(zip(row0.tolist(), ex.tolist(), rows.tolist()))
+    assert got == want, "row tiles do not cut the experts' aligned rows"
+    sched = plan["tile_sched"].tolist()
+    assert sorted(sched) == list(range(len(want))), "tile schedule is not a permutation"
+    nrt = plan["n_remote_tiles"]
+    remote_rows = {e: int(lay.group_row[e, lay.r_self]) - int(lay.expert_base[e]) for e in range(lay.E_l)}
+    for pos, t in enumerate(sched):
+        r0, e, _ = want[t]
+        holds_remote = r0 - int(lay.expert_base[e]) < remote_rows[e]
+        assert holds_remote == (pos < nrt), f"tile {t} at schedule position {pos}"
+    # remote phase follows the band schedule's expert order
+    order = []
+    for e in bd.expert[:bd.n_remote].tolist():
+        if not order or order[-1] != e:
+            order.append(e)
+    assert [want[t][1] for t in sched[:nrt]] == sorted([want[t][1] for t in sched[:nrt]],
+                                                       key=order.index)
+    for i in range(len(sg.band0)):
+        first = int(bd.row0[sg.band0[i]])
+        last = int(bd.row0[sg.band0[i] + sg.nbands[i] - 1]) + tb - 1
+        t0, t1 = int(plan["seg_tile0"][i]), int(plan["seg_tile1"][i])
+        assert want[t0][0] <= first < want[t0][0] + want[t0][2], f"segment {i} first tile"
+        assert want[t1][0] <= last < want[t1][0] + want[t1][2], f"segment {i} last tile"

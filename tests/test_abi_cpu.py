@@ -44,11 +44,16 @@ def good_shape(**kw):
 
 def test_query_sizes_values():
     s = ops.moe_query_sizes(good_shape())
-    # m_pad_max = min(R*T*k, R*T*E_l) + E_l*R*(tb_m-1), rounded up to tb_m
+    # packed rows <= min(R*T*k, R*T*E_l) + E_l*R*(tb_m-1), rounded up to tb_m; the
+    # row buffers carry one GEMM row tile (256 rows) of slack
     mp = min(4 * 256 * 2, 4 * 256 * 2) + 2 * 4 * 63
-    assert s.m_pad_max == -(-mp // 64) * 64
-    assert s.max_bands == s.m_pad_max // 64
-    assert s.bn_out == 256 and s.max_flags == s.max_bands * (512 // 256)
+    rows = -(-mp // 64) * 64
+    assert s.tile_m == 256
+    assert s.m_pad_max == rows + 256
+    assert s.max_bands == rows // 64
+    # row tiles: each expert's aligned rows cut into 256-row tiles
+    assert s.max_tiles == -(-rows // 256) + 2
+    assert s.bn_out == 256 and s.max_flags == s.max_tiles * (512 // 256)
     assert s.recv_rows_max == 256 * 2
     assert s.ws_bytes > 0 and s.ws_bytes % 256 == 0
 
@@ -61,7 +66,7 @@ def test_query_sizes_values():
     (dict(gate_kind=3), _abi.MOE_ERR_INVALID_ARG), (dict(mgb=0), _abi.MOE_ERR_INVALID_ARG),
     (dict(T=0), _abi.MOE_ERR_INVALID_ARG),
     (dict(H=384), _abi.MOE_ERR_UNSUPPORTED), (dict(F=200), _abi.MOE_ERR_UNSUPPORTED),
-    (dict(tb_m=32), _abi.MOE_ERR_UNSUPPORTED), (dict(tb_m=512), _abi.MOE_ERR_UNSUPPORTED),
+    (dict(tb_m=16), _abi.MOE_ERR_UNSUPPORTED), (dict(tb_m=512), _abi.MOE_ERR_UNSUPPORTED),
     (dict(E=1024, R=4), _abi.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_shapes_rejected(kw, code):
@@ -170,3 +175,28 @@ def test_partition_rejects_bad_calibration():
         ops.moe_plan_partition(sh, counts, _abi.MoeCalib(1e12, 64, 1e9, 1e12, 0, 256, 20, 16, 1))
     with pytest.raises(_abi.MoeError):
         ops.moe_plan_partition(sh, -counts, None)
+
+
+def _struct_fields(header: str, name: str):
+    import re
+    end = re.search(r"\}\s*" + name + ";", header).start()
+    body = header[header.rindex("typedef struct {", 0, end) + len("typedef struct {"):end]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        for part in decl.split(","):
+            names.append(re.sub(r"\[.*?\]|\*", "", part.split()[-1]).strip())
+    return names
+
+
+def test_ctypes_structs_follow_the_header():
+    """The binding's struct layouts list the header's fields in the header's order."""
+    import os
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe_overlap.h")).read()
+    assert _struct_fields(hdr, "moe_plan_t") == list(_abi.PLAN_FIELDS)
+    assert _struct_fields(hdr, "moe_sizes_t") == [f[0] for f in _abi.MoeSizes._fields_]
+    assert _struct_fields(hdr, "moe_shape_t") == [f[0] for f in _abi.MoeShape._fields_]
+    assert _struct_fields(hdr, "moe_calib_t") == [f[0] for f in _abi.MoeCalib._fields_]

@@ -13,13 +13,13 @@ import pytest
 from oracle import moe_share as om
 from synth import WORKLOADS, make_local_weights, make_logits, make_x
 from synth.workloads import ShareInputs
-from parity_util import (assert_plan_equal, bits, check_rows, make_gpu_share, oracle_plan_arrays,
-                         say, widen)
+from parity_util import (assert_plan_equal, bits, check_row_tiles, check_rows, make_gpu_share,
+                         oracle_plan_arrays, say, widen)
 
 pytestmark = pytest.mark.gpu
 
 # (workload id, layer, band height) -- band heights as in bench.py
-FULL = [(2, 0, 256), (3, 0, 256), (4, 0, 128), (5, 0, 256), (5, 2, 128)]
+FULL = [(2, 0, 64), (3, 0, 256), (4, 0, 32), (5, 0, 64), (5, 2, 128)]
 
 
 @pytest.mark.parametrize("wid,layer,tb", FULL, ids=[f"cfg{a}_l{b}_tb{c}" for a, b, c in FULL])
@@ -47,6 +47,7 @@ def test_full_size_parity(wid, layer, tb):
     plan = sh.plan_arrays()
     assert plan["status"] == 0
     assert_plan_equal(plan, oracle_plan_arrays(ref))
+    check_row_tiles(plan, ref, sh.sizes.tile_m)
     m_pad = plan["m_pad"]
     rng = np.random.default_rng(wid * 10 + layer)
     rows = rng.choice(m_pad, size=min(m_pad, 512), replace=False)

@@ -10,8 +10,8 @@ import pytest
 
 from oracle import moe_share as om
 from synth import Workload, WORKLOADS, make_share_inputs
-from parity_util import (assert_plan_equal, bits, check_rows, make_gpu_share, oracle_plan_arrays,
-                         say, widen)
+from parity_util import (assert_plan_equal, bits, check_row_tiles, check_rows, make_gpu_share,
+                         oracle_plan_arrays, say, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +29,10 @@ CASES = [
     ("ragged_T300_R3", Workload("ragged", 3, 300, 256, 128, 6, 3, True, "softmax"), 1, 64, 1, 3, 0),
     ("single_rank", Workload("single", 1, 100, 256, 256, 4, 2, False, "softmax"), 0, 64, 1, 2, 0),
     ("k_equals_E", Workload("kE", 2, 64, 256, 128, 4, 4, True, "sigmoid"), 1, 128, 1, 2, 0),
+    # bands of 32 rows under 256-row GEMM tiles: tiles span several owners' bands
+    ("fine_mini_tb32", Workload("fine_mini", 8, 256, 512, 256, 64, 8, True, "sigmoid"), 0, 32, 2, 8, 0),
+    ("zipf_mini_tb32", Workload("zipf_mini", 4, 512, 1024, 1024, 8, 2, True, "softmax", "zipf",
+                                w_std="fan_in"), 2, 32, 3, 8, 0),
 ]
 
 
@@ -65,6 +69,7 @@ def test_share_parity(case):
     plan = sh.plan_arrays()
     assert plan["status"] == 0
     assert_plan_equal(plan, oracle_plan_arrays(ref))
+    check_row_tiles(plan, ref, sh.sizes.tile_m)
     m_pad = plan["m_pad"]
     assert np.array_equal(widen(b.x_perm[:m_pad]), ref.x_perm), "x_perm differs"
 
