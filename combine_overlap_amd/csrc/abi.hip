@@ -272,7 +272,7 @@ int moe_route(const moe_shape_t* shape, const float* logits, int32_t* topk_ids, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = hip_rc(launch_route(g, logits, topk_ids, gates, p, st));
   if (rc != MOE_OK) return rc;
-  return hip_rc(launch_count(g, counts, p, st));
+  return hip_rc(launch_count(g, topk_ids, counts, p, st));
 }
 
 int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_ids,

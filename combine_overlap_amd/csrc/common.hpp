@@ -16,6 +16,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // tokens per routing chunk: a chunk never spans two source ranks
 constexpr int kChunk = 256;
+// local experts per rank at most (the plan and the chunk histograms size LDS by it)
+constexpr int kPlanMaxElRoute = 256;
 // meta words in the workspace
 enum { META_MPAD = 0, META_NBANDS = 1, META_NREMOTE = 2, META_NSEG = 3, META_STATUS = 4, META_NUNITS = 5,
        META_NTILES = 6, META_NRTILES = 7, META_WORDS = 64 };
@@ -71,7 +73,8 @@ struct BufPtrs { uint16_t* p[MOE_MAX_RANKS]; };
 // ---- kernel launchers (enqueue only) ----
 hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, float* gates,
                         const moe_plan_t& p, hipStream_t st);
-hipError_t launch_count(const Geometry& g, int32_t* counts, const moe_plan_t& p, hipStream_t st);
+hipError_t launch_count(const Geometry& g, const int32_t* ids, int32_t* counts, const moe_plan_t& p,
+                        hipStream_t st);
 hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, hipStream_t st);
 hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
                          uint16_t* x_perm, const moe_plan_t& p, hipStream_t st);

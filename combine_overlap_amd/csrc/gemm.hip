@@ -55,6 +55,8 @@
 //   EPI_GATED  h = SiLU(x W1^T) * (x W3^T); the B tile interleaves 32-row
 //              blocks of W1 and W3 so each wave holds u and v of the same h
 //              columns in registers.
+#include <type_traits>
+
 #include "common.hpp"
 
 #ifndef MOE_DEVICE_SCOPE_PUBLISH
@@ -359,12 +361,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       for (int j = 0; j < C::FN; ++j)
         fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + b_off[kk] + j * 32 * BK);
     };
-    auto mfmas = [&](int buf) {
+    // 32-row blocks of this wave inside the tile's stored rows (a short last
+    // row tile of an expert skips the MFMAs of the blocks past them)
+    const int fm_act = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (vrows - wm * C::WTM) / 32)));
+    auto mfmas = [&](int buf, auto partial) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
+      for (int i = 0; i < C::FM; ++i) {
+        if (decltype(partial)::value && i >= fm_act) continue;
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+      }
     };
 
     // previous tile's stores must not be counted by the stage waits below
@@ -375,20 +382,24 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     if (nkc >= NS) wait_vm_barrier<(NS - 1) * C::LPW>();
     else wait_vm_barrier<0>();
     load_frags(0, 0, 0);
-    for (int kt = 0; kt < nkc; ++kt) {
+    auto kloop = [&](auto partial) {
+      for (int kt = 0; kt < nkc; ++kt) {
 #pragma unroll
-      for (int kk = 0; kk + 1 < KK; ++kk) {
-        load_frags(kt, kk + 1, (kk + 1) & 1);
-        mfmas(kk & 1);
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+          load_frags(kt, kk + 1, (kk + 1) & 1);
+          mfmas(kk & 1, partial);
+        }
+        if (kt + 1 < nkc) {
+          if (kt + NS <= nkc) wait_vm_barrier<(NS - 2) * C::LPW>();
+          else wait_vm_barrier<0>();
+          if (kt + NS < nkc) issue(kt + NS);
+          load_frags(kt + 1, 0, 0);
+        }
+        mfmas((KK - 1) & 1, partial);
       }
-      if (kt + 1 < nkc) {
-        if (kt + NS <= nkc) wait_vm_barrier<(NS - 2) * C::LPW>();
-        else wait_vm_barrier<0>();
-        if (kt + NS < nkc) issue(kt + NS);
-        load_frags(kt + 1, 0, 0);
-      }
-      mfmas((KK - 1) & 1);
-    }
+    };
+    if (fm_act == C::FM) kloop(std::false_type{});
+    else kloop(std::true_type{});
 
     // split tail tile: publish this chunk's accumulators; the last chunk to
     // arrive adds the others and finishes the tile
