@@ -127,7 +127,7 @@ def main():
     import torch
     from synth import WORKLOADS, make_logits, make_x, make_local_weights
     from synth.workloads import ShareInputs
-    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL
+    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL
     from combine_overlap_amd.share import MoEShare, bf16_tensor
 
     w = WORKLOADS[args.config]
@@ -179,10 +179,14 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / k
 
-    t_ovl = None
+    t_ovl = t_rs = None
     if not args.sequential_only:
         t_ovl = timed(MOE_MODE_OVERLAP, args.steps)
         log(f"[bench] overlap layer step {t_ovl * 1e3:.3f} ms")
+        for _ in range(args.warmup):
+            step(MOE_MODE_ROLE_SWITCH)
+        t_rs = timed(MOE_MODE_ROLE_SWITCH, args.steps)
+        log(f"[bench] role-switch layer step {t_rs * 1e3:.3f} ms")
         for _ in range(args.warmup):
             step(MOE_MODE_SEQUENTIAL)
     t_seq = timed(MOE_MODE_SEQUENTIAL, args.steps)
@@ -190,7 +194,8 @@ def main():
 
     # per-phase device timings (HIP events on the kernels' own streams)
     sh.ctx.set_timing(True)
-    modes = (MOE_MODE_SEQUENTIAL,) if args.sequential_only else (MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL)
+    modes = ((MOE_MODE_SEQUENTIAL,) if args.sequential_only else
+             (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
     ph = {m: [] for m in modes}
     for mode in modes:
         for _ in range(max(3, args.steps)):
@@ -213,6 +218,8 @@ def main():
         prod = med(MOE_MODE_OVERLAP, "producer")
         ovl_total = med(MOE_MODE_OVERLAP, "total")
         exposed = med(MOE_MODE_OVERLAP, "exposed")
+        log(f"[bench] role switch: gemm1 {med(MOE_MODE_ROLE_SWITCH, 'gemm1'):.3f} ms, gemm2 + copy "
+            f"{med(MOE_MODE_ROLE_SWITCH, 'producer'):.3f} ms, expert phase {med(MOE_MODE_ROLE_SWITCH, 'total'):.3f} ms")
         t_main = t_ovl
         log(f"[bench] overlap: gemm1 {g1:.3f} ms, producer {prod:.3f} ms, expert phase "
             f"{ovl_total:.3f} ms, exposed copy {exposed * 1e3:.1f} us")

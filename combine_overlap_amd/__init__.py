@@ -7,7 +7,7 @@ owns the device buffers of one shape. There is no non-GPU fallback.
 """
 from . import _abi  # noqa: F401
 from ._abi import (MOE_GATE_SIGMOID, MOE_GATE_SOFTMAX, MOE_MODE_OVERLAP,  # noqa: F401
-                   MOE_MODE_SEQUENTIAL, MoeError)
+                   MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL, MoeError)
 
-__all__ = ["ops", "share", "MoeError", "MOE_MODE_OVERLAP", "MOE_MODE_SEQUENTIAL",
+__all__ = ["ops", "share", "MoeError", "MOE_MODE_OVERLAP", "MOE_MODE_SEQUENTIAL", "MOE_MODE_ROLE_SWITCH",
            "MOE_GATE_SOFTMAX", "MOE_GATE_SIGMOID"]

@@ -23,6 +23,7 @@ MOE_GATE_SOFTMAX = 0
 MOE_GATE_SIGMOID = 1
 MOE_MODE_OVERLAP = 0
 MOE_MODE_SEQUENTIAL = 1
+MOE_MODE_ROLE_SWITCH = 2
 
 META_MPAD, META_NBANDS, META_NREMOTE, META_NSEG, META_STATUS, META_NUNITS, META_NTILES, \
     META_NRTILES = range(8)

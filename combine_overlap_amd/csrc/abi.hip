@@ -300,7 +300,8 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
   if (rc != MOE_OK) return rc;
   if (!ctx || !x_perm || !w1 || !w2 || !h || !y_perm || !combine_buf) return MOE_ERR_INVALID_ARG;
   if ((g.gated != 0) != (w3 != nullptr)) return MOE_ERR_INVALID_ARG;
-  if (mode != MOE_MODE_OVERLAP && mode != MOE_MODE_SEQUENTIAL) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_MODE_OVERLAP && mode != MOE_MODE_SEQUENTIAL && mode != MOE_MODE_ROLE_SWITCH)
+    return MOE_ERR_INVALID_ARG;
   if (!ws_ok(ws)) return MOE_ERR_WORKSPACE;
   BufPtrs bufs{};
   for (int s = 0; s < g.R; ++s) {
@@ -312,6 +313,8 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
     if (!flags || epoch == 0 || n_consumer_cu < 1 || n_consumer_cu > 64 ||
         n_consumer_cu >= ctx->n_cu || consumer_stream == producer_stream)
       return MOE_ERR_INVALID_ARG;
+  } else if (mode == MOE_MODE_ROLE_SWITCH) {
+    if (!flags || epoch == 0) return MOE_ERR_INVALID_ARG;
   } else if (n_consumer_cu < 0 || n_consumer_cu > 64 || n_consumer_cu >= ctx->n_cu) {
     return MOE_ERR_INVALID_ARG;
   }
@@ -327,7 +330,7 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
   if ((rc = rec(1, ps)) != MOE_OK) return rc;
   if (mode == MOE_MODE_SEQUENTIAL) {
     if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu, ncu - n_consumer_cu,
-                                  ps))) != MOE_OK)
+                                  nullptr, ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
     if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 4 * ncu, ps))) != MOE_OK) return rc;
@@ -337,10 +340,22 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
     ctx->timed_mode = mode;
     return MOE_OK;
   }
+  if (mode == MOE_MODE_ROLE_SWITCH) {
+    // one launch on every CU does both duties; the split is sized for all CUs
+    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu, ncu, &bufs, ps))) !=
+        MOE_OK)
+      return rc;
+    if ((rc = rec(2, ps)) != MOE_OK) return rc;
+    if ((rc = rec(3, ps)) != MOE_OK) return rc;
+    if ((rc = rec(4, ps)) != MOE_OK) return rc;
+    ctx->timed = tm;
+    ctx->timed_mode = mode;
+    return MOE_OK;
+  }
   if ((rc = hip_rc(hipEventRecord(ctx->ev_producer, ps))) != MOE_OK) return rc;
   if ((rc = hip_rc(hipStreamWaitEvent(cs, ctx->ev_producer, 0))) != MOE_OK) return rc;
   if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu - n_consumer_cu,
-                                ncu - n_consumer_cu, ps))) != MOE_OK)
+                                ncu - n_consumer_cu, nullptr, ps))) != MOE_OK)
     return rc;
   if ((rc = rec(2, ps)) != MOE_OK) return rc;
   if ((rc = hip_rc(launch_consumer(g, y_perm, bufs, p, flags, epoch, ctx->trace, n_consumer_cu, cs))) !=

@@ -26,10 +26,13 @@ enum { META_MPAD = 0, META_NBANDS = 1, META_NREMOTE = 2, META_NSEG = 3, META_STA
 constexpr int kTileM = 256;
 // segments are also cut into copy units of this many bytes (the baseline bulk copy)
 constexpr int kCopyUnitBytes = 65536;
-// per-XCD tile queues of the two GEMM launches: counter (phase, xcd) at tile_ctr[(phase*8 + xcd) * 32]
+// per-XCD tile queues of the two GEMM launches: counter (phase, xcd) at
+// tile_ctr[(phase*8 + xcd) * 32]; then one block of kCtrStride words per
+// phase for the role-switching copy (word 0: next segment to claim)
 constexpr int kXcds = 8;
 constexpr int kCtrStride = 32;
-constexpr int kCtrWords = 2 * kXcds * kCtrStride;
+constexpr int kCtrWords = 2 * kXcds * kCtrStride + 2 * kCtrStride;
+constexpr int kCopyCtrOffset = 2 * kXcds * kCtrStride;
 // K-split tail tiles of a GEMM launch: per XCD queue at most kTailSlots chunks,
 // each with a tb_m x 256 fp32 partial tile; word 1 + t of the XCD's counter
 // block counts the arrivals of tail tile t
@@ -70,6 +73,23 @@ void plan_from_ws(const Geometry& g, void* ws, moe_plan_t* p);
 // combine-buffer pointers travel to kernels by value
 struct BufPtrs { uint16_t* p[MOE_MAX_RANKS]; };
 
+#define GLOBAL_AS __attribute__((address_space(1)))
+
+// 16-byte load of rows another workgroup published with device-scope
+// write-through stores: device-scope (sc1) loads, two 8-byte halves, which
+// miss in this XCD's L2 unless the line is coherent. (Explicit global address
+// space: generic "flat" atomics would each wait for all earlier accesses.)
+__device__ __forceinline__ u32x4 load16_device(const u32x4* a) {
+  const GLOBAL_AS uint64_t* s64 = (const GLOBAL_AS uint64_t*)a;
+  const uint64_t x = __hip_atomic_load(s64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t y = __hip_atomic_load(s64 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32)};
+}
+
+__device__ __forceinline__ void store16_nt(u32x4* a, u32x4 v) {
+  __builtin_nontemporal_store(v, (GLOBAL_AS u32x4*)a);
+}
+
 // ---- kernel launchers (enqueue only) ----
 hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, float* gates,
                         const moe_plan_t& p, hipStream_t st);
@@ -83,9 +103,12 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_
                         hipStream_t st);
 // split_grid: the producer grid the K-split tail is sized for (the overlapped
 // run's n_cu - c in both modes, so that both compute identical bits)
+// copy_bufs: non-null gives the launch the consumer's duty as well (role
+// switching): between tiles a workgroup copies every remote segment whose row
+// tiles are all flagged, and once the tiles run out it drains the rest
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
-                        int grid, int split_grid, hipStream_t st);
+                        int grid, int split_grid, const BufPtrs* copy_bufs, hipStream_t st);
 hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
                            const uint32_t* flags, uint32_t epoch, uint64_t* trace, int n_wg,
                            hipStream_t st);

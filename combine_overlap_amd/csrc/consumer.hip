@@ -45,26 +45,10 @@ constexpr int kBatchUnits = MOE_CONSUMER_BATCH;
 #define MOE_COPY_UNROLL 8
 #endif
 
-// 16-byte load: device-scope (sc1, two 8-byte halves) loads miss in this
-// XCD's L2 unless the line is coherent, so they see the producer's
-// write-through stores; plain loads otherwise
-// (global address space explicitly: generic "flat" atomics would each be
-// preceded by a wait for every earlier memory access of the wave)
-#define GLOBAL_AS __attribute__((address_space(1)))
 template <bool DEVICE_SCOPE>
 __device__ __forceinline__ u32x4 load16(const u32x4* a) {
-  if constexpr (DEVICE_SCOPE) {
-    const GLOBAL_AS uint64_t* s64 = (const GLOBAL_AS uint64_t*)a;
-    const uint64_t x = __hip_atomic_load(s64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t y = __hip_atomic_load(s64 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return u32x4{(uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32)};
-  } else {
-    return *(const GLOBAL_AS u32x4*)a;
-  }
-}
-
-__device__ __forceinline__ void store16_nt(u32x4* a, u32x4 v) {
-  __builtin_nontemporal_store(v, (GLOBAL_AS u32x4*)a);
+  if constexpr (DEVICE_SCOPE) return load16_device(a);
+  else return *(const GLOBAL_AS u32x4*)a;
 }
 
 // plain 16-byte loads (non-temporal loads halve the per-CU rate), streaming

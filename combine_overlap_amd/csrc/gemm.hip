@@ -27,6 +27,13 @@
 //    complete and increments the tile's arrival counter; the chunk that
 //    arrives last adds the other partials (device-scope loads) and runs the
 //    tile's epilogue, flag included.
+//  * Role switching (optional, output projection): the workgroups also do
+//    the consumer's work. Before each tile a workgroup claims the next
+//    remote segment (one atomic) if all its row tiles are flagged and copies
+//    it into its owner's combine buffer, repeating while segments are ready;
+//    once the tiles run out the workgroups wait for and copy the rest. The
+//    copy thus takes the few CU-microseconds it costs instead of a standing
+//    partition of CUs.
 //  * 4 or 8 waves per workgroup in a WM x WN grid (8 = two waves per SIMD);
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 //  * The k-loop streams BK-wide slices of A and B straight from global memory
@@ -109,6 +116,17 @@ struct GemmArgs {
   int32_t* other_ctr;          // the other launch's counters (zeroed here)
   float* partial;              // fp32 partial tiles of split tail tiles, [8 * kTailSlots][BM * BN]
   uint32_t* flags;             // output projection in overlap mode, else null
+  // role switching (output projection): the consumer's copy duty between tiles
+  int copy_duty;
+  int32_t* my_copy;            // [0] next remote segment to claim
+  int32_t* other_copy;         // the other launch's copy words (cleared here)
+  BufPtrs bufs;                // combine buffers by source rank
+  const int32_t* seg_tile0;
+  const int32_t* seg_tile1;
+  const int32_t* seg_rows;
+  const int32_t* seg_src_row;
+  const int32_t* seg_dst_row;
+  const int32_t* seg_dest;
   uint64_t* trace;             // optional timeline: [0] start, [8 + t] tile t done
   uint32_t epoch;
   int K, Nw, Nout, tiles_n;
@@ -221,12 +239,118 @@ __device__ __forceinline__ int xcc_id() {
   return v & (kXcds - 1);
 }
 
-template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI>
+constexpr uint64_t kCopyWaitTicks = 200000000ull;   // 2 s at the 100 MHz constant clock
+
+// Copies remote segment sg's valid rows (y rows published by other
+// workgroups) into its owner's combine buffer with all NT threads.
+template <int NT>
+__device__ __forceinline__ void copy_segment(const GemmArgs& a, int sg, int tid) {
+  constexpr int kRound = 16;   // 16-byte loads per thread in flight
+  const int H = a.Nout;
+  const uint32_t words = (uint32_t)a.seg_rows[sg] * (uint32_t)(H / 8);
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.C + (size_t)a.seg_src_row[sg] * H);
+  u32x4* dst = reinterpret_cast<u32x4*>(a.bufs.p[a.seg_dest[sg]] + (size_t)a.seg_dst_row[sg] * H);
+  for (uint32_t w0 = 0; w0 < words; w0 += NT * kRound) {
+    u32x4 v[kRound];
+#pragma unroll
+    for (int z = 0; z < kRound; ++z) {   // unconditional loads, index clamped into the segment
+      const uint32_t i = w0 + (uint32_t)(z * NT + tid);
+      v[z] = load16_device(src + (i < words ? i : words - 1));
+    }
+#pragma unroll
+    for (int z = 0; z < kRound; ++z) {
+      const uint32_t i = w0 + (uint32_t)(z * NT + tid);
+      if (i < words) store16_nt(dst + i, v[z]);
+    }
+  }
+}
+
+// The copy duty, segments in schedule order.
+//  wait = false (between tiles): if the next unclaimed segment's row tiles are
+//    all flagged, claim it together with the following segments those same
+//    flags cover (one compare-and-swap), copy them, and look again; return as
+//    soon as the next segment is not ready.
+//  wait = true (no tiles left): take segments by ticket (fetch-and-add), so
+//    the workgroups claim in parallel; wait (bounded) for each one's flags and
+//    copy it; return once every segment is taken.
+constexpr int kMaxClaim = 16;
+
+template <int NT>
+__device__ void copy_duty(const GemmArgs& a, bool wait, int tid, int* s_copy) {
+  const int n_seg = a.meta[META_NSEG];
+  const int lane = tid & 63;
+  auto tiles_ready = [&](int t0, int t1) {
+    const int nf = (t1 - t0 + 1) * a.tiles_n;
+    const uint32_t* f = a.flags + (size_t)t0 * a.tiles_n;
+    bool ok = true;
+    for (int i = lane; i < nf; i += 64)
+      ok &= (__hip_atomic_load(f + i, MOE_DEVICE_SCOPE_PUBLISH ? __ATOMIC_RELAXED : __ATOMIC_ACQUIRE,
+                               __HIP_MEMORY_SCOPE_AGENT) == a.epoch);
+    return __ballot(!ok) == 0ull;
+  };
+  while (true) {
+    if (tid < 64) {
+      int d0 = -1, d1 = -1;   // claimed segments [d0, d1); d0 < 0: nothing now (-2: all taken)
+      if (!wait) {
+        while (true) {
+          const int sg = __hip_atomic_load(a.my_copy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (sg >= n_seg) { d0 = -2; break; }
+          const int t0 = a.seg_tile0[sg], t1 = a.seg_tile1[sg];
+          if (!tiles_ready(t0, t1)) break;
+          int n = 1;
+          while (n < kMaxClaim && sg + n < n_seg && a.seg_tile0[sg + n] >= t0 && a.seg_tile1[sg + n] <= t1) ++n;
+          int won = 0;
+          if (lane == 0) {
+            int expected = sg;
+            won = __hip_atomic_compare_exchange_strong(a.my_copy, &expected, sg + n, __ATOMIC_RELAXED,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (__shfl(won, 0)) { d0 = sg; d1 = sg + n; break; }
+        }
+      } else {
+        int sg = 0;
+        if (lane == 0) sg = __hip_atomic_fetch_add(a.my_copy, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sg = __shfl(sg, 0);
+        if (sg >= n_seg) {
+          d0 = -2;
+        } else {
+          const int t0 = a.seg_tile0[sg], t1 = a.seg_tile1[sg];
+          const uint64_t t_start = wall_clock64();
+          d0 = sg;
+          d1 = sg + 1;
+          while (!tiles_ready(t0, t1)) {
+            if (wall_clock64() - t_start > kCopyWaitTicks) {
+              if (lane == 0) {
+                int expected = 0;
+                __hip_atomic_compare_exchange_strong(const_cast<int32_t*>(a.meta) + META_STATUS, &expected,
+                                                     MOE_ERR_TIMEOUT, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+              }
+              d0 = -2;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+      }
+      if (lane == 0) { s_copy[0] = d0; s_copy[1] = d1; }
+    }
+    __syncthreads();
+    const int d0 = s_copy[0], d1 = s_copy[1];
+    __syncthreads();
+    if (d0 < 0) return;
+    if (!MOE_DEVICE_SCOPE_PUBLISH) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int sg = d0; sg < d1; ++sg) copy_segment<NT>(a, sg, tid);
+  }
+}
+
+template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool COPY = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   using C = Tile<BM, BN, BK, NS, WM, WN>;
   static_assert(EPI != EPI_GATED || C::FN % 2 == 0, "gated tiles pair W1/W3 32-column blocks per wave");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
   __shared__ int s_item[5];   // tile, chunk, nsplit, slot, queue
+  __shared__ int s_copy[2];   // copy duty: claimed segments [s_copy[0], s_copy[1])
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -235,6 +359,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 
   // the other launch's queue and tail counters (this launch's were cleared by it)
   if (blockIdx.x == 0 && tid < kXcds * kCtrStride) a.other_ctr[tid] = 0;
+  if (blockIdx.x == 0 && tid < kCtrStride) a.other_copy[tid] = 0;
   const int px = max(1, a.px);
   if (a.trace != nullptr && blockIdx.x == 0 && tid == 0) a.trace[0] = wall_clock64();
 
@@ -262,6 +387,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   const int n_rt = a.meta[META_NTILES];   // row tiles, in schedule positions
   int q = xcc_id(), tried = 0;
   while (true) {
+    if constexpr (COPY) copy_duty<C::NT>(a, false, tid, s_copy);
     if (tid == 0) {
       Item it{-1, 0, 1, 0};
       while (tried < kXcds) {
@@ -277,7 +403,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     }
     __syncthreads();
     const int tile = s_item[0];
-    if (tile < 0) break;
+    if (tile < 0) {
+      if constexpr (COPY) copy_duty<C::NT>(a, true, tid, s_copy);
+      break;
+    }
     const int chunk = __builtin_amdgcn_readfirstlane(s_item[1]);
     const int nsplit = __builtin_amdgcn_readfirstlane(s_item[2]);
     const int slot = __builtin_amdgcn_readfirstlane(s_item[3]);
@@ -546,6 +675,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 
 template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI>
 static hipError_t launch_t(const GemmArgs& a, int grid, hipStream_t st) {
+  if constexpr (EPI == EPI_PLAIN) {
+    if (a.copy_duty) {
+      hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI, true>), dim3(grid), dim3(WM * WN * 64), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI>), dim3(grid), dim3(WM * WN * 64), 0, st, a);
   return hipGetLastError();
 }
@@ -585,6 +720,8 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_
   a.tile_sched = p.tile_sched;
   a.my_ctr = p.tile_ctr;
   a.other_ctr = p.tile_ctr + kXcds * kCtrStride;
+  a.my_copy = p.tile_ctr + kCopyCtrOffset;
+  a.other_copy = p.tile_ctr + kCopyCtrOffset + kCtrStride;
   a.partial = p.partial;
   a.flags = nullptr;
   a.trace = nullptr;
@@ -600,7 +737,7 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_
 
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
-                        int grid, int split_grid, hipStream_t st) {
+                        int grid, int split_grid, const BufPtrs* copy_bufs, hipStream_t st) {
   GemmArgs a{};
   a.A = h;
   a.B0 = w2;
@@ -613,7 +750,19 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
   a.tile_sched = p.tile_sched;
   a.my_ctr = p.tile_ctr + kXcds * kCtrStride;
   a.other_ctr = p.tile_ctr;
+  a.my_copy = p.tile_ctr + kCopyCtrOffset + kCtrStride;
+  a.other_copy = p.tile_ctr + kCopyCtrOffset;
   a.partial = p.partial;
+  if (copy_bufs != nullptr) {
+    a.copy_duty = 1;
+    a.bufs = *copy_bufs;
+    a.seg_tile0 = p.seg_tile0;
+    a.seg_tile1 = p.seg_tile1;
+    a.seg_rows = p.seg_rows;
+    a.seg_src_row = p.seg_src_row;
+    a.seg_dst_row = p.seg_dst_row;
+    a.seg_dest = p.seg_dest;
+  }
   a.flags = flags;
   a.trace = trace;
   a.epoch = epoch;

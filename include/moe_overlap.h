@@ -57,7 +57,7 @@ extern "C" {
 #define MOE_MAX_RANKS 16          /* R limit: combine buffer pointers go by value */
 
 enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 };
-enum { MOE_MODE_OVERLAP = 0, MOE_MODE_SEQUENTIAL = 1 };
+enum { MOE_MODE_OVERLAP = 0, MOE_MODE_SEQUENTIAL = 1, MOE_MODE_ROLE_SWITCH = 2 };
 
 /* Problem shape of one rank's share ([TLS] sec. 3.2, Algorithm 1 inputs).
  *  R        simulated ranks (1..MOE_MAX_RANKS)
@@ -262,6 +262,15 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *            every segment once all its tiles are flagged.
  *            MOE_MODE_SEQUENTIAL (baseline, [TLS] sec. 4.1.3): both projections
  *            on all CUs, then one bulk copy of all remote rows on all CUs.
+ *            MOE_MODE_ROLE_SWITCH: both projections on all CUs, the output
+ *            projection's workgroups doing the consumer's work as well: before
+ *            each tile a workgroup copies every remote segment whose tiles are
+ *            all flagged (claimed in schedule order, one claim per segment),
+ *            and once the tiles run out the workgroups copy the rest (each
+ *            wait bounded like the consumer's). No CU is reserved; c is
+ *            ignored and the K-split is sized for all CUs (the same bits as
+ *            SEQUENTIAL with c = 0). consumer_stream is not used. The
+ *            per-layer worker split of [Weave] taken to its temporal end.
  *   producer_stream  all work is ordered after prior work on this stream and
  *            completes before later work on it (the consumer is joined back)
  *   consumer_stream  second stream for the consumer (OVERLAP only; must differ

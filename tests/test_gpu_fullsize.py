@@ -15,6 +15,7 @@ from synth import WORKLOADS, make_local_weights, make_logits, make_x
 from synth.workloads import ShareInputs
 from parity_util import (assert_plan_equal, bits, check_row_tiles, check_rows, make_gpu_share,
                          oracle_plan_arrays, say, widen)
+from test_gpu_parity import check_role_switch
 
 pytestmark = pytest.mark.gpu
 
@@ -99,3 +100,6 @@ def test_full_size_parity(wid, layer, tb):
     torch.cuda.synchronize()
     assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits)
     assert np.array_equal(bits(b.y_share), share_bits)
+
+    say(f"[fullsize] {w.name}: role switching")
+    check_role_switch(sh, ref, w, 0, w.name)

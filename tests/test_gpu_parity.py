@@ -46,7 +46,7 @@ def _inputs(w, r_self, layer):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_share_parity(case):
     import torch
-    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL
+    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL
     name, w, r_self, tb, mgb, c, layer = case
     say(f"[parity] {name}: R={w.R} T={w.T} H={w.H} F={w.F} E={w.E} k={w.k} r_self={r_self} "
         f"tb_m={tb} mgb={mgb} c={c}")
@@ -110,6 +110,34 @@ def test_share_parity(case):
     torch.cuda.synchronize()
     assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits), "sequential y_perm differs from overlap"
     assert np.array_equal(bits(b.y_share), y_share_ovl), "sequential y_share differs from overlap"
+
+    # role switching: the producer's workgroups copy; same bits as SEQUENTIAL with c = 0
+    check_role_switch(sh, ref, w, r_self, name)
+
+
+def check_role_switch(sh, ref, w, r_self, name):
+    import torch
+    from combine_overlap_amd import MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL
+    b = sh.buf
+    m_pad = int(ref.layout.m_pad)
+    sh.expert_forward(MOE_MODE_SEQUENTIAL, n_consumer_cu=0)
+    sh.combine()
+    torch.cuda.synchronize()
+    seq_y, seq_share = bits(b.y_perm[:m_pad]).copy(), bits(b.y_share).copy()
+    for s in range(w.R):
+        if b.combine[s] is not None:
+            b.combine[s].fill_(float("nan"))
+    sh.expert_forward(MOE_MODE_ROLE_SWITCH)
+    sh.combine()
+    torch.cuda.synchronize()
+    assert sh.status() == 0
+    y_bits = bits(b.y_perm[:m_pad])
+    assert np.array_equal(y_bits, seq_y), f"{name}: role-switch y_perm differs from sequential"
+    bd = ref.bands
+    for i in range(bd.n_remote):
+        s, r0, rc, n = int(bd.dest[i]), int(bd.row0[i]), int(bd.recv0[i]), int(bd.valid[i])
+        assert np.array_equal(bits(b.combine[s][rc:rc + n]), y_bits[r0:r0 + n]), f"{name}: role-switch band {i}"
+    assert np.array_equal(bits(b.y_share), seq_share), f"{name}: role-switch y_share differs from sequential"
 
 
 def test_repeated_overlap_calls_are_deterministic():
