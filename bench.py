@@ -53,6 +53,11 @@ def parse():
                     help="run only the non-overlapped path (for counter collection, which "
                          "serialises kernels and so cannot run the concurrent consumer)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--layer-sweep", action="store_true",
+                    help="layered workload: per layer, the CU-partition overlap at the partition "
+                         "model's consumer count and at every candidate count, the role-switching "
+                         "overlap and the sequential baseline (expert phase, HIP events); adds a "
+                         "'layer_sweep' object to the JSON line")
     return ap.parse_args()
 
 
@@ -124,6 +129,54 @@ def cpu_baseline(w, inp, tb, target_s):
                        f"{len(experts)} local experts ({flops / 1e9:.1f} GFLOP in {t_ffn:.2f} s)")}
 
 
+def layer_sweep(sh, w, make_logits, torch, ops, modes, reps=5, cands=(8, 16, 24, 32, 40, 48)):
+    """Expert-phase times (ms, median of reps after 2 warmups) per layer and form.
+
+    Compares the partition model's per-layer consumer count with the best
+    single count over all layers and with the best count of each layer."""
+    MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL = modes
+    sh.ctx.set_timing(True)
+
+    def phase(mode, c):
+        d = []
+        for i in range(reps + 2):
+            sh.expert_forward(mode, n_consumer_cu=c)
+            if i >= 2:
+                d.append(sh.ctx.timings()["total"])
+        return float(np.median(d))
+    rows = []
+    for layer in range(w.layers):
+        sh.buf.logits.copy_(torch.from_numpy(make_logits(w, layer)))
+        sh.route()
+        sh.permute()
+        torch.cuda.synchronize()
+        counts = sh.buf.counts.cpu().numpy()
+        c_model, _, pred = ops.moe_plan_partition(sh.shape, counts)
+        t = {c: phase(MOE_MODE_OVERLAP, c) for c in cands}
+        if c_model not in t:
+            t[c_model] = phase(MOE_MODE_OVERLAP, c_model)
+        row = {"layer": layer, "valid_rows": int(counts.sum()),
+               "remote_rows": int(counts.sum() - counts[:, sh.r_self].sum()),
+               "c_model": int(c_model), "predicted_ms": round(pred * 1e3, 4),
+               "partition_ms": {str(c): round(v, 4) for c, v in sorted(t.items())},
+               "role_switch_ms": round(phase(MOE_MODE_ROLE_SWITCH, c_model), 4),
+               "sequential_ms": round(phase(MOE_MODE_SEQUENTIAL, c_model), 4)}
+        rows.append(row)
+        log(f"[sweep] layer {layer:2d}: rows {row['valid_rows']}, model c={c_model} "
+            f"{t[c_model]:.3f} ms, best c={min(cands, key=t.get)} {min(t[c] for c in cands):.3f} ms, "
+            f"role switch {row['role_switch_ms']:.3f}, sequential {row['sequential_ms']:.3f}")
+    sh.ctx.set_timing(False)
+    tot = lambda f: round(sum(f(r) for r in rows), 4)
+    fixed = {c: tot(lambda r, c=c: r["partition_ms"][str(c)]) for c in cands}
+    c_fixed = min(fixed, key=fixed.get)
+    return {"layers": rows,
+            "total_ms": {"model_c": tot(lambda r: r["partition_ms"][str(r["c_model"])]),
+                         "best_fixed_c": fixed[c_fixed], "best_fixed_c_value": c_fixed,
+                         "per_layer_best_c": tot(lambda r: min(r["partition_ms"][str(c)] for c in cands)),
+                         "role_switch": tot(lambda r: r["role_switch_ms"]),
+                         "sequential": tot(lambda r: r["sequential_ms"])}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -135,6 +188,7 @@ def main():
     from synth.workloads import ShareInputs
     from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL
     from combine_overlap_amd.share import MoEShare, bf16_tensor
+    from combine_overlap_amd import ops
 
     w = WORKLOADS[args.config]
     tb = args.tb or DEFAULT_TB[args.config]
@@ -281,6 +335,11 @@ def main():
                      "traffic": traffic, "traffic_unit": "bytes per launch",
                      "algorithmic_bytes": gemm1_bytes, "launch_ms": round(g1, 4)},
     }
+    if args.layer_sweep and w.layers > 1:
+        log("[bench] layer sweep")
+        out["layer_sweep"] = layer_sweep(sh, w, make_logits, torch, ops,
+                                         (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
+        log("[bench] layer sweep totals " + json.dumps(out["layer_sweep"]["total_ms"]))
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, inp, tb, args.cpu_seconds)

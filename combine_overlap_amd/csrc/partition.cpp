@@ -8,19 +8,22 @@
 //
 // Model (its form is not given on the pages; this is the plainest one that
 // uses only the routing counts and measured rates). For c consumer CUs:
-//  * the output projection runs on P = n_cu - c CUs; every tile (256 rows of
-//    one expert's tb_m-aligned rows x 256 columns, K = F; a short last row
-//    tile costs a full one) takes t_tile = 2 256 256 F / rate(M_e) on one CU,
-//    with rate(M) = gemm_flops_per_cu * M / (M + gemm_m_half) for an expert of
-//    M rows; tiles run in waves of P in schedule order (row tiles holding a
+//  * the output projection runs on P = n_cu - c CUs; a tile (up to 256 rows
+//    of one expert's tb_m-aligned rows x 256 columns, K = F; a short last row
+//    tile computes its rows rounded up to 32) takes t_tile = 2 rows 256 F /
+//    rate(M_e) on one CU, with rate(M) = gemm_flops_per_cu * M / (M +
+//    gemm_m_half) for an expert of M rows; tiles run in waves of P in
+//    schedule order (row tiles holding a
 //    remote band first, experts by remote band count, then rows, then id; then
 //    the other row tiles by expert), so a band is ready when the wave holding
 //    the last column tile of its row tile ends; a partial last wave of n tiles
 //    lasts max(n / P, 1/3) of a full one (fewer tiles share the memory
 //    bandwidth);
 //  * the consumer copies the segments in order, each when its bands are ready
-//    and the previous copy is done, at BW(c) = min(c * copy_bw_per_cu,
-//    copy_bw_max) plus seg_latency_s per segment;
+//    and the previous copy is done, at BW(c) = c b / (1 + c b / B) with
+//    b = copy_bw_per_cu and B = copy_bw_max (linear in c for few CUs,
+//    saturating at B: what the copy reaches while the GEMM loads the memory
+//    system), plus seg_latency_s once for the last batch;
 //  * T(c) = max(producer end, consumer end).
 // c = argmin T(c) over c_min, c_min + c_step, ..., <= c_max (smallest c on
 // ties). The step defaults to the XCD count: workgroups are dealt to the 8
@@ -56,14 +59,14 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
       s->r_self >= s->R || s->H < 1 || s->F < 1 || s->tb_m < 1)
     return MOE_ERR_INVALID_ARG;
   moe_calib_t c0;
-  // measured on MI355X over the five synthetic workloads: 3.1-4.1 TFLOP/s per
-  // producer CU on the output projection, 15-25 GB/s moved per consumer CU
-  // while the producer runs
+  // measured on MI355X over the five synthetic workloads: 3.6-4.4 TFLOP/s per
+  // producer CU on the output projection; the consumer moves 121, 208, 309
+  // and 407 GB/s with 8, 16, 32 and 48 CUs while the producer runs
   c0.gemm_flops_per_cu = 3.5e12;
-  c0.gemm_m_half = 64.0;
-  c0.copy_bw_per_cu = 16e9;
-  c0.copy_bw_max = 1.0e12;
-  c0.seg_latency_s = 2e-6;
+  c0.gemm_m_half = 0.0;
+  c0.copy_bw_per_cu = 17.8e9;
+  c0.copy_bw_max = 800e9;
+  c0.seg_latency_s = 10e-6;
   c0.n_cu = 256;
   c0.c_min = 8;
   c0.c_max = 48;
@@ -133,11 +136,16 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
   const double band_bytes = 2.0 * tb * (double)s->H;
   const int g = band_bytes < 0.5 * 1048576.0 ? 2 : 1;
   const int tiles2 = (s->H + 255) / 256;
-  std::vector<double> t_tile(El);
+  std::vector<double> rate(El);
   for (int e = 0; e < El; ++e) {
     const double m = (double)std::max<long>(m_e[e], 1);
-    t_tile[e] = 2.0 * kTileRows * 256.0 * (double)s->F / (k.gemm_flops_per_cu * m / (m + k.gemm_m_half));
+    rate[e] = k.gemm_flops_per_cu * m / (m + k.gemm_m_half);
   }
+  auto t_tile = [&](int e, int j) {   // row tile j of expert e
+    const long alg = (m_e[e] + tb - 1) / tb * tb;
+    const long rows = std::min<long>(kTileRows, alg - (long)j * kTileRows);
+    return 2.0 * (double)((rows + 31) / 32 * 32) * 256.0 * (double)s->F / rate[e];
+  };
   std::vector<double> tile_done((size_t)t_first[El], 0.0);
 
   double best_t = INFINITY;
@@ -152,7 +160,7 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
     for (size_t r = 0; r < t_exp.size(); ++r) {
       const size_t id = (size_t)(t_first[t_exp[r]] + t_idx[r]);
       for (int j = 0; j < tiles2; ++j) {
-        wave_len = std::max(wave_len, t_tile[t_exp[r]]);
+        wave_len = std::max(wave_len, t_tile(t_exp[r], t_idx[r]));
         if (++in_wave == P) {
           t += wave_len;
           for (size_t q : pending) tile_done[q] = t;
@@ -170,7 +178,7 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
     }
     const double t_prod = t;
     // consumer: segments of 1, g, ..., g, 1 bands per group, copied in order
-    const double bw = std::min(c * k.copy_bw_per_cu, k.copy_bw_max);
+    const double bw = c * k.copy_bw_per_cu / (1.0 + c * k.copy_bw_per_cu / k.copy_bw_max);
     double tc = 0.0;
     size_t b = 0;
     while (b < n_remote) {
@@ -184,12 +192,12 @@ extern "C" int moe_plan_partition(const moe_shape_t* s, const int32_t* counts, c
           rows += bands[q].rows;
           rdy = std::max(rdy, tile_done[(size_t)(t_first[bands[q].expert] + bands[q].rel / kTileRows)]);
         }
-        tc = std::max(tc, rdy) + 2.0 * rows * (double)s->H / bw + k.seg_latency_s;
+        tc = std::max(tc, rdy) + 2.0 * rows * (double)s->H / bw;
         p += sz;
       }
       b = last + 1;
     }
-    const double total = std::max(t_prod, tc);
+    const double total = std::max(t_prod, tc + (n_remote > 0 ? k.seg_latency_s : 0.0));
     if (total < best_t) { best_t = total; best_c = c; }
   }
   *n_consumer_cu = best_c;

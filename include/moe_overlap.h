@@ -146,10 +146,12 @@ typedef struct {
 /* Calibration of the partition cost model (measured on the device). */
 typedef struct {
   double gemm_flops_per_cu;   /* sustained bf16 FLOP/s of one producer CU, large M */
-  double gemm_m_half;         /* rows per expert at which GEMM efficiency halves    */
-  double copy_bw_per_cu;      /* bytes/s one consumer CU moves (large segments)     */
-  double copy_bw_max;         /* bytes/s ceiling of the copy (HBM)                  */
-  double seg_latency_s;       /* fixed cost per transfer segment, seconds           */
+  double gemm_m_half;         /* rows per expert at which GEMM efficiency halves
+                                 (0: every expert at the full rate)                 */
+  double copy_bw_per_cu;      /* b: bytes/s one consumer CU moves beside the GEMM   */
+  double copy_bw_max;         /* B: bytes/s the copy saturates at; c CUs move
+                                 c b / (1 + c b / B)                                */
+  double seg_latency_s;       /* fixed cost of the copy's last batch, seconds       */
   int32_t n_cu;               /* CUs on the device (256 on MI355X)                  */
   int32_t c_min, c_max;       /* consumer CU range considered                       */
   int32_t c_step;             /* candidates c_min, c_min + c_step, ...: a multiple of
