@@ -44,7 +44,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
   __shared__ int s_tbase[kPlanMaxEl + 1];   // first row tile of expert e
   __shared__ int s_trpos[kPlanMaxEl];       // schedule position of e's first remote tile
   __shared__ int s_tlpos[kPlanMaxEl];       // schedule position of e's first local-only tile
-  __shared__ int s_usum[1024];
+  __shared__ int s_usum[16];             // per-wave totals of the copy-unit scan
   const int tid = threadIdx.x;
   const int G = El * R;
   for (int i = tid; i < G; i += blockDim.x) s_cnt[i] = counts[i];
@@ -198,15 +198,23 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
   };
   int local = 0;
   for (int sg = lo; sg < hi; ++sg) local += units(sg);
-  s_usum[tid] = local;
+  // exclusive scan over the workgroup: inclusive scan inside each wave, then
+  // the waves' totals
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = local;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_usum[wave] = incl;
   __syncthreads();
   if (tid == 0) {
     int acc = 0;
-    for (int t = 0; t < (int)blockDim.x; ++t) { const int v = s_usum[t]; s_usum[t] = acc; acc += v; }
+    for (int w = 0; w < (int)blockDim.x / 64; ++w) { const int v = s_usum[w]; s_usum[w] = acc; acc += v; }
     p.meta[META_NUNITS] = acc;
   }
   __syncthreads();
-  int acc = s_usum[tid];
+  int acc = s_usum[wave] + incl - local;
   for (int sg = lo; sg < hi; ++sg) { p.seg_unit0[sg] = acc; acc += units(sg); }
 }
 

@@ -3,10 +3,12 @@
 // plus the per-(local expert, source rank) row counts that the dispatch
 // delivers to this rank.
 //
-// k_route: one routing group of G lanes (G = min(64, next power of two >= E))
-// owns a token; lane i of the group holds logits i, i+G, i+2G, ...  Each of
-// the k rounds is a butterfly arg-max inside the group (higher logit wins,
-// equal logits go to the lower expert id) followed by masking the winner.
+// k_route: one routing group of G lanes (G = the smallest power of two with
+// 8 G >= E) owns a token; lane i of the group holds logits i, i+G, i+2G, ...
+// (at most 8). Each of the k rounds is a butterfly arg-max inside the group
+// (higher logit wins, equal logits go to the lower expert id) followed by
+// masking the winner. Small groups keep the butterfly short and put many
+// tokens in each wave.
 // The grid covers the tokens (a workgroup holds 256 / G of them), so every
 // CU has many tokens' loads in flight.
 //
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     if (r >= k) break;
-    if (gi == r) {
+    if (r % G == gi) {   // G may be smaller than k: lane gi writes selections gi, gi + G, ...
       ids_out[g * k + r] = sel_id[r];
       gates_out[g * k + r] = w[r] / sum;
     }
@@ -126,7 +128,7 @@ hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, fl
                         const moe_plan_t& p, hipStream_t st) {
   (void)p;
   int G = 1;
-  while (G < g.E && G < 64) G <<= 1;
+  while (G * 8 < g.E) G <<= 1;   // E <= 512: G <= 64
   const int nq = (g.E + G - 1) / G;
   const int n_tok = g.R * g.T;
   const int per_block = kRouteThreads / G;
