@@ -9,8 +9,11 @@ reduction. Inputs are resident in HBM before the timed region.
 Three forms of the expert phase are timed in the same run: the overlap with
 a consumer on its own CU partition (the paper's design), the role-switching
 overlap (the producer's workgroups do the copy between tiles), and the
-non-overlapped baseline (GEMMs on all CUs, then one bulk copy). `value` is the
-faster overlapped form (named in config.overlap_mode).
+non-overlapped baseline (GEMMs on all CUs, then one bulk copy), each with the
+routed rows gathered into x_perm by the permute step and with the gather
+fused into the first projection's tile loads. `value` is the fastest
+overlapped form (config.overlap_mode, config.gather); the sequential baseline
+it is compared with uses the same gather.
 
 Prints ONE JSON line on stdout (details on stderr).
 """
@@ -52,6 +55,9 @@ def parse():
     ap.add_argument("--sequential-only", action="store_true",
                     help="run only the non-overlapped path (for counter collection, which "
                          "serialises kernels and so cannot run the concurrent consumer)")
+    ap.add_argument("--gather", choices=("both", "materialized", "fused"), default="both",
+                    help="A rows of the first projection: the materialized x_perm, the gather "
+                         "fused into its tile loads, or both (timed side by side)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--layer-sweep", action="store_true",
                     help="layered workload: per layer, the CU-partition overlap at the partition "
@@ -70,11 +76,13 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, tb: int):
+def stored_traffic(workload: str, tb: int, gathered: bool):
     """HBM-side bytes per launch of the first-projection GEMM from the committed
-    FETCH_SIZE / WRITE_SIZE summary for this workload and band height, or None
-    when there is none or the GEMM sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"pmc_gemm1_{workload}_tb{tb}.md")
+    FETCH_SIZE / WRITE_SIZE summary for this workload, band height and A-row
+    source, or None when there is none or the GEMM sources changed since it
+    was taken."""
+    path = os.path.join(ROOT, "profiles",
+                        f"pmc_gemm1{'_gathered' if gathered else ''}_{workload}_tb{tb}.md")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -209,6 +217,8 @@ def main():
         c = sh.layer(mode, n_consumer_cu=args.c or None)
         return c, sh.shape.mgb
 
+    gathers = {"both": (False, True), "materialized": (False,), "fused": (True,)}[args.gather]
+    sh.fused_gather = gathers[0]
     main_mode = MOE_MODE_SEQUENTIAL if args.sequential_only else MOE_MODE_OVERLAP
     # warmup + sanity
     for _ in range(max(1, args.warmup)):
@@ -224,10 +234,12 @@ def main():
     flops1 = float((4 if w.gated else 2) * w.H * w.F) * M
     plan = sh.plan_arrays()
     m_pad = plan["m_pad"]
-    # compulsory HBM bytes of the first-projection GEMM: x_perm, W1 (+W3) of the
-    # experts that received rows, h
+    # compulsory HBM bytes of the first-projection GEMM: its A rows (x_perm, or
+    # the valid rows of x when gathered: padding reads one cached zero row),
+    # W1 (+W3) of the experts that received rows, h
     n_w = (2 if w.gated else 1) * int((counts.sum(axis=1) > 0).sum())
-    gemm1_bytes = 2 * (m_pad * w.H + n_w * w.F * w.H + m_pad * w.F)
+    gemm1_bytes = {False: 2 * (m_pad * w.H + n_w * w.F * w.H + m_pad * w.F),
+                   True: 2 * (M * w.H + n_w * w.F * w.H + m_pad * w.F)}
     log(f"[bench] valid rows {M}, remote rows {remote}, padded rows {m_pad}, bands {plan['n_bands']}, "
         f"segments {plan['n_seg']}, c={c_used}, mgb={mgb_used}")
 
@@ -239,78 +251,88 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / k
 
-    t_ovl = t_rs = None
-    if not args.sequential_only:
-        t_ovl = timed(MOE_MODE_OVERLAP, args.steps)
-        log(f"[bench] overlap layer step {t_ovl * 1e3:.3f} ms")
-        for _ in range(args.warmup):
-            step(MOE_MODE_ROLE_SWITCH)
-        t_rs = timed(MOE_MODE_ROLE_SWITCH, args.steps)
-        log(f"[bench] role-switch layer step {t_rs * 1e3:.3f} ms")
-        for _ in range(args.warmup):
-            step(MOE_MODE_SEQUENTIAL)
-    t_seq = timed(MOE_MODE_SEQUENTIAL, args.steps)
-    log(f"[bench] sequential layer step {t_seq * 1e3:.3f} ms")
+    modes = ((MOE_MODE_SEQUENTIAL,) if args.sequential_only else
+             (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
+    mname = {MOE_MODE_OVERLAP: "cu_partition", MOE_MODE_ROLE_SWITCH: "role_switch",
+             MOE_MODE_SEQUENTIAL: "sequential"}
+    gname = {False: "materialized", True: "fused"}
+    t_step = {}
+    for fused in gathers:
+        sh.fused_gather = fused
+        for mode in modes:
+            for _ in range(args.warmup):
+                step(mode)
+            t_step[(fused, mode)] = timed(mode, args.steps)
+            log(f"[bench] gather {gname[fused]}, {mname[mode]}: layer step "
+                f"{t_step[(fused, mode)] * 1e3:.3f} ms")
 
     # per-phase device timings (HIP events on the kernels' own streams)
     sh.ctx.set_timing(True)
-    modes = ((MOE_MODE_SEQUENTIAL,) if args.sequential_only else
-             (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
-    ph = {m: [] for m in modes}
-    for mode in modes:
-        for _ in range(max(3, args.steps)):
-            sh.expert_forward(mode, n_consumer_cu=c_used)
-            ph[mode].append(sh.ctx.timings())
+    ph = {}
+    for fused in gathers:
+        sh.fused_gather = fused
+        sh.permute()
+        for mode in modes:
+            ph[(fused, mode)] = []
+            for _ in range(max(3, args.steps)):
+                sh.expert_forward(mode, n_consumer_cu=c_used)
+                ph[(fused, mode)].append(sh.ctx.timings())
     sh.ctx.set_timing(False)
+    torch.cuda.synchronize()
+    if sh.status() != 0:
+        raise RuntimeError(f"device status {sh.status()} after the timed runs")
 
-    def med(mode, key):
-        return float(np.median([d[key] for d in ph[mode]]))
-    seq_g1 = med(MOE_MODE_SEQUENTIAL, "gemm1")
-    seq_g2 = med(MOE_MODE_SEQUENTIAL, "producer")
-    seq_copy = med(MOE_MODE_SEQUENTIAL, "exposed")
-    seq_total = med(MOE_MODE_SEQUENTIAL, "total")
-    log(f"[bench] sequential: gemm1 {seq_g1:.3f} ms, gemm2 {seq_g2:.3f} ms, bulk copy "
-        f"{seq_copy * 1e3:.1f} us, expert phase {seq_total:.3f} ms")
-    if args.sequential_only:
-        best_mode, t_best = "sequential", t_seq
-        g1, prod, ovl_total, exposed = seq_g1, seq_g2, seq_total, seq_copy
-        rs = {}
-    else:
-        g1 = med(MOE_MODE_OVERLAP, "gemm1")
-        prod = med(MOE_MODE_OVERLAP, "producer")
-        ovl_total = med(MOE_MODE_OVERLAP, "total")
-        exposed = med(MOE_MODE_OVERLAP, "exposed")
-        log(f"[bench] overlap: gemm1 {g1:.3f} ms, producer {prod:.3f} ms, expert phase "
-            f"{ovl_total:.3f} ms, exposed copy {exposed * 1e3:.1f} us")
-        rs = {k: med(MOE_MODE_ROLE_SWITCH, k) for k in ("gemm1", "producer", "total")}
-        log(f"[bench] role switch: gemm1 {rs['gemm1']:.3f} ms, gemm2 + copy {rs['producer']:.3f} ms, "
-            f"expert phase {rs['total']:.3f} ms")
-        best_mode, t_best = ("role_switch", t_rs) if t_rs < t_ovl else ("cu_partition", t_ovl)
+    def med(fused, mode, key):
+        return float(np.median([d[key] for d in ph[(fused, mode)]]))
+    for fused in gathers:
+        log(f"[bench] gather {gname[fused]}, sequential: gemm1 {med(fused, MOE_MODE_SEQUENTIAL, 'gemm1'):.3f} ms, "
+            f"gemm2 {med(fused, MOE_MODE_SEQUENTIAL, 'producer'):.3f} ms, bulk copy "
+            f"{med(fused, MOE_MODE_SEQUENTIAL, 'exposed') * 1e3:.1f} us, expert phase "
+            f"{med(fused, MOE_MODE_SEQUENTIAL, 'total'):.3f} ms")
+        if not args.sequential_only:
+            log(f"[bench] gather {gname[fused]}, overlap: gemm1 {med(fused, MOE_MODE_OVERLAP, 'gemm1'):.3f} ms, "
+                f"producer {med(fused, MOE_MODE_OVERLAP, 'producer'):.3f} ms, expert phase "
+                f"{med(fused, MOE_MODE_OVERLAP, 'total'):.3f} ms, exposed copy "
+                f"{med(fused, MOE_MODE_OVERLAP, 'exposed') * 1e3:.1f} us; role switch: expert phase "
+                f"{med(fused, MOE_MODE_ROLE_SWITCH, 'total'):.3f} ms")
+    overlapped = [k for k in t_step if k[1] != MOE_MODE_SEQUENTIAL] or list(t_step)
+    best = min(overlapped, key=t_step.get)
+    b_fused, b_mode = best
+    t_best = t_step[best]
+    t_seq = t_step[(b_fused, MOE_MODE_SEQUENTIAL)]
+    g1 = med(b_fused, b_mode, "gemm1")
     ach1 = flops1 / (g1 * 1e-3) / 1e12
-    traffic = stored_traffic(w.name, tb)
+    traffic = stored_traffic(w.name, tb, b_fused)
 
     layer = {
         "valid_rows": M, "remote_rows": remote, "padded_rows": m_pad,
         "algorithmic_tflop": round(flops / 1e12, 4),
+        "step_ms": {gname[f]: {mname[m]: round(t_step[(f, m)] * 1e3, 4) for m in modes} for f in gathers},
         "sequential_ms": round(t_seq * 1e3, 4),
-        "expert_phase_sequential_ms": round(seq_total, 4),
-        "sequential_gemm2_ms": round(seq_g2, 4), "bulk_copy_us": round(seq_copy * 1e3, 2),
+        "speedup_vs_sequential": round(t_seq / t_best, 4),
         "gemm1_ms": round(g1, 4),
     }
+    for fused in gathers:
+        seq_copy = med(fused, MOE_MODE_SEQUENTIAL, "exposed")
+        d = {"sequential": {"expert_phase_ms": round(med(fused, MOE_MODE_SEQUENTIAL, "total"), 4),
+                            "gemm1_ms": round(med(fused, MOE_MODE_SEQUENTIAL, "gemm1"), 4),
+                            "gemm2_ms": round(med(fused, MOE_MODE_SEQUENTIAL, "producer"), 4),
+                            "bulk_copy_us": round(seq_copy * 1e3, 2)}}
+        if not args.sequential_only:
+            prod = med(fused, MOE_MODE_OVERLAP, "producer")
+            exposed = med(fused, MOE_MODE_OVERLAP, "exposed")
+            d["cu_partition"] = {
+                "consumer_cus": c_used, "expert_phase_ms": round(med(fused, MOE_MODE_OVERLAP, "total"), 4),
+                "gemm1_ms": round(med(fused, MOE_MODE_OVERLAP, "gemm1"), 4),
+                "producer_ms": round(prod, 4),
+                "producer_tflops": round(float(2 * w.H * w.F * M) / (prod * 1e-3) / 1e12, 2),
+                "exposed_copy_us": round(exposed * 1e3, 2),
+                "exposed_copy_fraction": round(exposed / seq_copy, 4) if seq_copy > 0 else None}
+            d["role_switch"] = {"expert_phase_ms": round(med(fused, MOE_MODE_ROLE_SWITCH, "total"), 4),
+                                "gemm2_and_copy_ms": round(med(fused, MOE_MODE_ROLE_SWITCH, "producer"), 4)}
+        layer["gather_" + gname[fused]] = d
     if not args.sequential_only:
-        layer.update({
-            "overlap_cu_partition_ms": round(t_ovl * 1e3, 4),
-            "overlap_role_switch_ms": round(t_rs * 1e3, 4),
-            "speedup_vs_sequential": round(t_seq / t_best, 4),
-            "pct_mfma_peak_layer": round(100 * flops / t_best / 1e12 / PEAK_BF16_TFLOPS, 2),
-            "cu_partition": {"consumer_cus": c_used, "expert_phase_ms": round(ovl_total, 4),
-                             "producer_ms": round(prod, 4),
-                             "producer_tflops": round(float(2 * w.H * w.F * M) / (prod * 1e-3) / 1e12, 2),
-                             "exposed_copy_us": round(exposed * 1e3, 2),
-                             "exposed_copy_fraction": round(exposed / seq_copy, 4) if seq_copy > 0 else None},
-            "role_switch": {"expert_phase_ms": round(rs["total"], 4),
-                            "gemm2_and_copy_ms": round(rs["producer"], 4)},
-        })
+        layer["pct_mfma_peak_layer"] = round(100 * flops / t_best / 1e12 / PEAK_BF16_TFLOPS, 2)
     out = {
         "metric": "MoE-layer TFLOP/s per EP rank (overlapped combine), % of bf16 MFMA peak",
         "value": round(flops / t_best / 1e12, 3),
@@ -325,18 +347,21 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; random-init expert weights)",
         "config": {"workload": w.name, "layer": args.layer, "R": w.R, "T": w.T, "H": w.H, "F": w.F,
-                   "E": w.E, "k": w.k, "r_self": r_self, "tb_m": tb, "overlap_mode": best_mode,
+                   "E": w.E, "k": w.k, "r_self": r_self, "tb_m": tb, "overlap_mode": mname[b_mode],
+                   "gather": gname[b_fused],
                    "consumer_cus": c_used, "mgb": mgb_used,
                    "parallelism": "one EP rank share on one GPU"},
         "layer": layer,
-        "roofline": {"kernel": "k_gemm first projection (x W1^T, x W3^T, SiLU gate)",
+        "roofline": {"kernel": "k_gemm first projection (x W1^T, x W3^T, SiLU gate)" +
+                     (", rows gathered from x" if b_fused else ""),
                      "bound": "mfma", "achieved": round(ach1, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach1 / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "traffic_unit": "bytes per launch",
-                     "algorithmic_bytes": gemm1_bytes, "launch_ms": round(g1, 4)},
+                     "algorithmic_bytes": gemm1_bytes[b_fused], "launch_ms": round(g1, 4)},
     }
     if args.layer_sweep and w.layers > 1:
-        log("[bench] layer sweep")
+        log(f"[bench] layer sweep (gather {gname[b_fused]})")
+        sh.fused_gather = b_fused
         out["layer_sweep"] = layer_sweep(sh, w, make_logits, torch, ops,
                                          (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
         log("[bench] layer sweep totals " + json.dumps(out["layer_sweep"]["total_ms"]))

@@ -60,7 +60,8 @@ class MoeCalib(C.Structure):
 
 EXPORTS = ("moe_error_string", "moe_query_sizes", "moe_plan_view", "moe_ctx_create",
            "moe_ctx_destroy", "moe_ctx_num_cus", "moe_ctx_set_timing", "moe_ctx_timings", "moe_ctx_set_trace", "moe_route", "moe_permute",
-           "moe_plan_partition", "moe_expert_forward_overlap", "moe_combine", "moe_read_status")
+           "moe_plan_partition", "moe_expert_forward_overlap", "moe_expert_forward_gathered",
+           "moe_combine", "moe_read_status")
 
 _lib = None
 
@@ -91,6 +92,7 @@ def lib() -> C.CDLL:
                                      C.POINTER(C.c_double)]
     L.moe_expert_forward_overlap.argtypes = [vp, pshape, vp, vp, vp, vp, vp, vp, vp,
                                              C.POINTER(vp), vp, u32, i32, i32, vp, vp]
+    L.moe_expert_forward_gathered.argtypes = L.moe_expert_forward_overlap.argtypes
     L.moe_combine.argtypes = [pshape, C.POINTER(vp), vp, vp, vp, vp, vp]
     L.moe_read_status.argtypes = [pshape, vp, pi32, vp]
     for name in EXPORTS:

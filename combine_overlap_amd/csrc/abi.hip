@@ -97,6 +97,7 @@ WsLayout ws_layout(const Geometry& g) {
   const size_t mt = (size_t)g.max_tiles;
   L.tile_row0 = take(mt); L.tile_expert = take(mt); L.tile_rows = take(mt); L.tile_sched = take(mt);
   L.seg_tile0 = take(mb); L.seg_tile1 = take(mb);
+  L.zero_row = take((size_t)g.H / 2);
   L.total = off;
   return L;
 }
@@ -123,6 +124,10 @@ void plan_from_ws(const Geometry& g, void* ws, moe_plan_t* p) {
   p->partial = reinterpret_cast<float*>(b + L.partial);
   p->tile_row0 = at(L.tile_row0); p->tile_expert = at(L.tile_expert); p->tile_rows = at(L.tile_rows);
   p->tile_sched = at(L.tile_sched); p->seg_tile0 = at(L.seg_tile0); p->seg_tile1 = at(L.seg_tile1);
+}
+
+uint16_t* zero_row_of(const Geometry& g, void* ws) {
+  return reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + ws_layout(g).zero_row);
 }
 
 static inline bool ws_ok(const void* ws) {
@@ -280,25 +285,29 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
   Geometry g;
   int rc = make_geometry(shape, &g);
   if (rc != MOE_OK) return rc;
-  if (!x || !topk_ids || !counts || !x_perm) return MOE_ERR_INVALID_ARG;
+  if (!topk_ids || !counts || (x_perm && !x)) return MOE_ERR_INVALID_ARG;
   if (!ws_ok(ws)) return MOE_ERR_WORKSPACE;
   moe_plan_t p;
   plan_from_ws(g, ws, &p);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = hip_rc(launch_plan(g, counts, p, st))) != MOE_OK) return rc;
+  if ((rc = hip_rc(launch_plan(g, counts, p, zero_row_of(g, ws), st))) != MOE_OK) return rc;
   return hip_rc(launch_gather(g, x, topk_ids, x_perm, p, st));
 }
 
-int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16_t* x_perm,
-                               const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
-                               void* ws, uint16_t* h, uint16_t* y_perm,
-                               uint16_t* const* combine_buf, uint32_t* flags, uint32_t epoch,
-                               int32_t n_consumer_cu, int32_t mode, void* producer_stream,
-                               void* consumer_stream) {
+}  // extern "C"
+
+// Both expert-phase entry points: `a` is x_perm (gathered = false) or x
+// (gathered = true: the first projection reads packed row r from x row
+// row_src[r], or the workspace's zero row for padding).
+static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16_t* a, bool gathered,
+                          const uint16_t* w1, const uint16_t* w3, const uint16_t* w2, void* ws,
+                          uint16_t* h, uint16_t* y_perm, uint16_t* const* combine_buf, uint32_t* flags,
+                          uint32_t epoch, int32_t n_consumer_cu, int32_t mode, void* producer_stream,
+                          void* consumer_stream) {
   Geometry g;
   int rc = make_geometry(shape, &g);
   if (rc != MOE_OK) return rc;
-  if (!ctx || !x_perm || !w1 || !w2 || !h || !y_perm || !combine_buf) return MOE_ERR_INVALID_ARG;
+  if (!ctx || !a || !w1 || !w2 || !h || !y_perm || !combine_buf) return MOE_ERR_INVALID_ARG;
   if ((g.gated != 0) != (w3 != nullptr)) return MOE_ERR_INVALID_ARG;
   if (mode != MOE_MODE_OVERLAP && mode != MOE_MODE_SEQUENTIAL && mode != MOE_MODE_ROLE_SWITCH)
     return MOE_ERR_INVALID_ARG;
@@ -326,7 +335,9 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
   const bool tm = ctx->timing != 0;
   auto rec = [&](int i, hipStream_t st) { return tm ? hip_rc(hipEventRecord(ctx->tev[i], st)) : MOE_OK; };
   if ((rc = rec(0, ps)) != MOE_OK) return rc;
-  if ((rc = hip_rc(launch_gemm1(g, x_perm, w1, w3, h, p, ncu, ps))) != MOE_OK) return rc;
+  if ((rc = hip_rc(launch_gemm1(g, a, gathered ? p.row_src : nullptr, gathered ? zero_row_of(g, ws) : nullptr,
+                                w1, w3, h, p, ncu, ps))) != MOE_OK)
+    return rc;
   if ((rc = rec(1, ps)) != MOE_OK) return rc;
   if (mode == MOE_MODE_SEQUENTIAL) {
     if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu, ncu - n_consumer_cu,
@@ -368,6 +379,28 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
   ctx->timed = tm;
   ctx->timed_mode = mode;
   return MOE_OK;
+}
+
+extern "C" {
+
+int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16_t* x_perm,
+                               const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                               void* ws, uint16_t* h, uint16_t* y_perm,
+                               uint16_t* const* combine_buf, uint32_t* flags, uint32_t epoch,
+                               int32_t n_consumer_cu, int32_t mode, void* producer_stream,
+                               void* consumer_stream) {
+  return expert_forward(ctx, shape, x_perm, false, w1, w3, w2, ws, h, y_perm, combine_buf, flags, epoch,
+                        n_consumer_cu, mode, producer_stream, consumer_stream);
+}
+
+int moe_expert_forward_gathered(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16_t* x,
+                                const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                                void* ws, uint16_t* h, uint16_t* y_perm,
+                                uint16_t* const* combine_buf, uint32_t* flags, uint32_t epoch,
+                                int32_t n_consumer_cu, int32_t mode, void* producer_stream,
+                                void* consumer_stream) {
+  return expert_forward(ctx, shape, x, true, w1, w3, w2, ws, h, y_perm, combine_buf, flags, epoch,
+                        n_consumer_cu, mode, producer_stream, consumer_stream);
 }
 
 int moe_combine(const moe_shape_t* shape, uint16_t* const* combine_buf, const uint16_t* y_perm,

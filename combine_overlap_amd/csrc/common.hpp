@@ -63,12 +63,15 @@ struct WsLayout {
   size_t band_row0, band_expert, band_dest, band_recv0, band_valid;
   size_t seg_band0, seg_nbands, seg_dest, seg_src_row, seg_dst_row, seg_rows;
   size_t row_src, recv_row, tile_ctr, slot_valid, seg_unit0, partial;
-  size_t tile_row0, tile_expert, tile_rows, tile_sched, seg_tile0, seg_tile1, total;
+  size_t tile_row0, tile_expert, tile_rows, tile_sched, seg_tile0, seg_tile1;
+  size_t zero_row;   // [H] bf16 zeros (written by the plan): padding rows of the gathered GEMM
+  size_t total;
 };
 
 int make_geometry(const moe_shape_t* s, Geometry* g);
 WsLayout ws_layout(const Geometry& g);
 void plan_from_ws(const Geometry& g, void* ws, moe_plan_t* p);
+uint16_t* zero_row_of(const Geometry& g, void* ws);
 
 // combine-buffer pointers travel to kernels by value
 struct BufPtrs { uint16_t* p[MOE_MAX_RANKS]; };
@@ -95,12 +98,16 @@ hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, fl
                         const moe_plan_t& p, hipStream_t st);
 hipError_t launch_count(const Geometry& g, const int32_t* ids, int32_t* counts, const moe_plan_t& p,
                         hipStream_t st);
-hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, hipStream_t st);
+hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, uint16_t* zero_row,
+                       hipStream_t st);
+// x_perm null: only the indexes (row_src, with -1 for every padding row, and recv_row)
 hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
                          uint16_t* x_perm, const moe_plan_t& p, hipStream_t st);
-hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_t* w1,
-                        const uint16_t* w3, uint16_t* h, const moe_plan_t& p, int grid,
-                        hipStream_t st);
+// a_rows null: A = x_perm (packed rows); else A = x and packed row r reads x row
+// a_rows[r] (a_zero for padding), the gather fused into the tile loads
+hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t* a_rows,
+                        const uint16_t* a_zero, const uint16_t* w1, const uint16_t* w3, uint16_t* h,
+                        const moe_plan_t& p, int grid, hipStream_t st);
 // split_grid: the producer grid the K-split tail is sized for (the overlapped
 // run's n_cu - c in both modes, so that both compute identical bits)
 // copy_bufs: non-null gives the launch the consumer's duty as well (role

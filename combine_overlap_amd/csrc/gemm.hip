@@ -103,7 +103,11 @@ struct Tile {
 };
 
 struct GemmArgs {
-  const uint16_t* A;           // [rows, K]
+  const uint16_t* A;           // [rows, K]; gathered: [a_nrows, K] rows picked by a_rows
+  const int32_t* a_rows;       // gathered first projection: source row of each packed row
+                               // (-1 = padding), rows >= meta[META_MPAD] read as padding
+  const uint16_t* a_zero;      // [K] zeros: the source of padding rows
+  int a_nrows;
   const uint16_t* B0;          // [El, Nw, K]
   const uint16_t* B1;          // [El, Nw, K] (gated only)
   uint16_t* C;                 // [rows, Nout]
@@ -229,6 +233,19 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t lane_off, uint
       : "memory");
 }
 
+// The same copy with a per-lane 64-bit address (rows gathered from anywhere).
+__device__ __forceinline__ void dma16_v(const void* lane_addr, uint32_t lds_byte) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(lane_addr), "s"(lds_byte)
+      : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const LDS_AS void*)p));
 }
@@ -344,7 +361,7 @@ __device__ void copy_duty(const GemmArgs& a, bool wait, int tid, int* s_copy) {
   }
 }
 
-template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool COPY = false>
+template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool COPY = false, bool GATHER = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   using C = Tile<BM, BN, BK, NS, WM, WN>;
   static_assert(EPI != EPI_GATED || C::FN % 2 == 0, "gated tiles pair W1/W3 32-column blocks per wave");
@@ -385,6 +402,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   }
 
   const int n_rt = a.meta[META_NTILES];   // row tiles, in schedule positions
+  const int m_pad = GATHER ? a.meta[META_MPAD] : 0;
   int q = xcc_id(), tried = 0;
   while (true) {
     if constexpr (COPY) copy_duty<C::NT>(a, false, tid, s_copy);
@@ -425,13 +443,31 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     const int vrows = a.tile_rows[rt];           // rows to store (the rest is the next expert's)
     const int fidx = rt * a.tiles_n + tn;        // flag / trace index
 
-    // wave-uniform global bases of this wave's DMA instructions (k offset added per stage)
+    // wave-uniform global bases of this wave's DMA instructions (k offset added per stage);
+    // gathered A: each lane's own source row instead, its swizzled chunk included
     const char* abase[C::A_PW];
     const char* bbase[C::B_PW];
+    if constexpr (GATHER) {
+      // every source index is loaded before any is used (one wait), with
+      // unconditional clamped loads
+      int src[C::A_PW];
 #pragma unroll
-    for (int i = 0; i < C::A_PW; ++i) {
-      const int r = (wave_u * C::A_PW + i) * C::RPI;
-      abase[i] = reinterpret_cast<const char*>(a.A) + ((size_t)(row0 + r) * K) * 2;
+      for (int i = 0; i < C::A_PW; ++i)
+        src[i] = a.a_rows[min(row0 + (wave_u * C::A_PW + i) * C::RPI + d_row, m_pad - 1)];
+#pragma unroll
+      for (int i = 0; i < C::A_PW; ++i) {
+        const int blk = wave_u * C::A_PW + i;
+        const int r = row0 + blk * C::RPI + d_row;
+        const bool real = r < m_pad && (unsigned)src[i] < (unsigned)a.a_nrows;
+        const uint64_t rp = real ? reinterpret_cast<uint64_t>(a.A) + (uint64_t)(uint32_t)src[i] * (uint64_t)(K * 2)
+                                 : reinterpret_cast<uint64_t>(a.a_zero);
+        abase[i] = reinterpret_cast<const char*>(rp + swz<C::CPR>((blk & 1) * C::RPI + d_row, d_pch) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::A_PW; ++i)
+        abase[i] = reinterpret_cast<const char*>(a.A) +
+                   ((size_t)(row0 + (wave_u * C::A_PW + i) * C::RPI) * K) * 2;
     }
 #pragma unroll
     for (int i = 0; i < C::B_PW; ++i) {
@@ -454,7 +490,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < C::A_PW; ++i) {
         const int blk = wave_u * C::A_PW + i;
-        dma16(abase[i] + ko, lane_off[blk & 1], st + (uint32_t)(blk * C::RPI * BK * 2));
+        if constexpr (GATHER) dma16_v(abase[i] + ko, st + (uint32_t)(blk * C::RPI * BK * 2));
+        else dma16(abase[i] + ko, lane_off[blk & 1], st + (uint32_t)(blk * C::RPI * BK * 2));
       }
 #pragma unroll
       for (int i = 0; i < C::B_PW; ++i) {
@@ -680,6 +717,12 @@ static hipError_t launch_t(const GemmArgs& a, int grid, hipStream_t st) {
       hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI, true>), dim3(grid), dim3(WM * WN * 64), 0, st, a);
       return hipGetLastError();
     }
+  } else {
+    if (a.a_rows != nullptr) {
+      hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI, false, true>), dim3(grid), dim3(WM * WN * 64), 0,
+                         st, a);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI>), dim3(grid), dim3(WM * WN * 64), 0, st, a);
   return hipGetLastError();
@@ -705,11 +748,14 @@ static hipError_t dispatch(GemmArgs a, int bm, int bn, int grid, hipStream_t st)
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm1(const Geometry& g, const uint16_t* x_perm, const uint16_t* w1,
-                        const uint16_t* w3, uint16_t* h, const moe_plan_t& p, int grid,
-                        hipStream_t st) {
+hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t* a_rows,
+                        const uint16_t* a_zero, const uint16_t* w1, const uint16_t* w3, uint16_t* h,
+                        const moe_plan_t& p, int grid, hipStream_t st) {
   GemmArgs a{};
-  a.A = x_perm;
+  a.A = a_src;
+  a.a_rows = a_rows;
+  a.a_zero = a_zero;
+  a.a_nrows = g.R * g.T;
   a.B0 = w1;
   a.B1 = w3;
   a.C = h;

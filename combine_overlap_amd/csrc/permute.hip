@@ -18,6 +18,10 @@
 // GEMM schedule: every tile that holds a remote band, experts in the band
 // schedule's order, then the remaining tiles by expert id. A segment's rows
 // lie in one expert, so the tiles covering it are consecutive.
+//
+// With the gather fused into the first projection's tile loads the rows are
+// not copied: only the indexes are built (row_src, -1 for padding). The plan
+// also zeroes the one row of H zeros that padding rows read there.
 #include "common.hpp"
 
 namespace moe {
@@ -32,7 +36,8 @@ constexpr int kPlanMaxGroups = 2048;  // E_l * R limit (checked on the host)
 
 // single workgroup: everything here is O(E_l * R) metadata
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ counts, moe_plan_t p,
-                                                int R, int El, int r_self, int tb, int mgb, int H) {
+                                                u32x4* __restrict__ zero_row, int R, int El, int r_self,
+                                                int tb, int mgb, int H) {
   __shared__ int s_cnt[kPlanMaxGroups];
   __shared__ int s_rel[kPlanMaxGroups];      // group start relative to its expert base
   __shared__ int s_bandoff[kPlanMaxGroups];  // first band index of the group (schedule order)
@@ -47,6 +52,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
   __shared__ int s_usum[16];             // per-wave totals of the copy-unit scan
   const int tid = threadIdx.x;
   const int G = El * R;
+  for (int i = tid; i < H / 8; i += blockDim.x) zero_row[i] = u32x4{0u, 0u, 0u, 0u};
   for (int i = tid; i < G; i += blockDim.x) s_cnt[i] = counts[i];
   __syncthreads();
 
@@ -295,10 +301,18 @@ __global__ __launch_bounds__(256) void k_gather_copy(const uint16_t* __restrict_
   }
 }
 
-hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p,
+// index only (the gather fused into the first projection): row_src = -1 for
+// every row of [0, m_pad) that is not a valid row of its band slot
+__global__ __launch_bounds__(256) void k_pad_index(moe_plan_t p, int tb) {
+  const int m_pad = p.meta[META_MPAD];
+  for (int r = blockIdx.x * 256 + threadIdx.x; r < m_pad; r += gridDim.x * 256)
+    if ((r % tb) >= p.slot_valid[r / tb]) p.row_src[r] = -1;
+}
+
+hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, uint16_t* zero_row,
                        hipStream_t st) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, counts, p, g.R, g.El, g.r_self, g.tb_m,
-                     g.mgb, g.H);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, counts, p, reinterpret_cast<u32x4*>(zero_row),
+                     g.R, g.El, g.r_self, g.tb_m, g.mgb, g.H);
   return hipGetLastError();
 }
 
@@ -308,6 +322,11 @@ hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* id
                      g.r_self * g.El, g.r_self, g.chunks_per_rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (x_perm == nullptr) {
+    const int64_t blocks = (g.m_pad_max + 255) / 256;
+    hipLaunchKernelGGL(k_pad_index, dim3((int)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, st, p, g.tb_m);
+    return hipGetLastError();
+  }
   // grid-stride over at most m_pad_max rows, four rows per block
   const int64_t blocks = (g.m_pad_max + 3) / 4;
   const int grid = (int)(blocks < 4096 ? blocks : 4096);

@@ -3,7 +3,9 @@
 MoEShare allocates every device buffer the C ABI needs for one shape and runs
 route -> permute -> (partition) -> expert forward (overlap or sequential) ->
 combine, all through the HIP library. PyTorch only provides device memory,
-streams and events.
+streams and events. With fused_gather the routed rows are not copied into
+x_perm: permute builds the indexes only and the expert forward's first
+projection reads them from x (moe_expert_forward_gathered).
 """
 from __future__ import annotations
 
@@ -34,7 +36,7 @@ class ShareBuffers:
     gates: torch.Tensor
     counts: torch.Tensor
     ws: torch.Tensor
-    x_perm: torch.Tensor
+    x_perm: Optional[torch.Tensor]   # None while the gather is fused
     h: torch.Tensor
     y_perm: torch.Tensor
     combine: list
@@ -46,8 +48,9 @@ class MoEShare:
     """Buffers and launch sequence for rank r_self's share of one MoE layer."""
 
     def __init__(self, R, T, H, F, E, k, gated, gate_kind, r_self=0, tb_m=128, mgb=None,
-                 device="cuda:0"):
+                 device="cuda:0", fused_gather=False):
         self.device = torch.device(device)
+        self.fused_gather = bool(fused_gather)
         self.shape = ops.make_shape(R, T, H, F, E, k, r_self, gated, gate_kind, tb_m, mgb or 1)
         self.sizes = ops.moe_query_sizes(self.shape)
         self.R, self.T, self.H, self.F, self.E, self.k = R, T, H, F, E, k
@@ -81,7 +84,7 @@ class MoEShare:
             gates=torch.empty((R * T, k), dtype=torch.float32, device=d),
             counts=torch.empty((El, R), dtype=torch.int32, device=d),
             ws=ws,
-            x_perm=torch.empty((mp, H), dtype=torch.bfloat16, device=d),
+            x_perm=None if self.fused_gather else torch.empty((mp, H), dtype=torch.bfloat16, device=d),
             h=torch.empty((mp, F), dtype=torch.bfloat16, device=d),
             y_perm=torch.empty((mp, H), dtype=torch.bfloat16, device=d),
             combine=combine,
@@ -110,6 +113,12 @@ class MoEShare:
 
     def permute(self, stream=None):
         b = self.buf
+        if self.fused_gather:
+            ops.moe_permute(self.shape, None, b.topk_ids, b.counts, None, b.ws, stream)
+            return
+        if b.x_perm is None:
+            b.x_perm = torch.empty((int(self.sizes.m_pad_max), self.H), dtype=torch.bfloat16,
+                                   device=self.device)
         ops.moe_permute(self.shape, b.x, b.topk_ids, b.counts, b.x_perm, b.ws, stream)
 
     def partition(self, calib=None):
@@ -119,9 +128,10 @@ class MoEShare:
     def expert_forward(self, mode=_abi.MOE_MODE_OVERLAP, n_consumer_cu=8, stream=None):
         b = self.buf
         self.epoch = (self.epoch % 0xFFFFFFF0) + 1
-        ops.moe_expert_forward_overlap(self.ctx, self.shape, b.x_perm, b.w1, b.w3, b.w2, b.ws, b.h,
-                                       b.y_perm, b.combine, b.flags, self.epoch, n_consumer_cu,
-                                       mode, stream, self.consumer_stream)
+        fwd = ops.moe_expert_forward_gathered if self.fused_gather else ops.moe_expert_forward_overlap
+        fwd(self.ctx, self.shape, b.x if self.fused_gather else b.x_perm, b.w1, b.w3, b.w2, b.ws, b.h,
+            b.y_perm, b.combine, b.flags, self.epoch, n_consumer_cu, mode, stream,
+            self.consumer_stream)
 
     def combine(self, stream=None):
         b = self.buf

@@ -21,6 +21,9 @@
  *                   projection raises one ready flag per tile while a
  *                   consumer kernel on a few CUs copies each ready segment
  *                   into its source rank's combine buffer
+ *   moe_expert_forward_gathered
+ *                   the same, its first projection reading the routed rows
+ *                   straight from x (the gather fused into the tile loads)
  *   moe_combine     gate-weighted reduction of the returned rows
  *
  * Conventions
@@ -223,6 +226,9 @@ int moe_route(const moe_shape_t* shape, const float* logits, int32_t* topk_ids,
  *   x_perm  [m_pad_max, H] bf16 (out): row i = x of token row_src[i]; zero
  *           rows for owner-boundary padding and between experts. Rows beyond
  *           m_pad are not written.
+ *           NULL: no row is copied; the plan and the indexes (row_src with -1
+ *           for every padding row, recv_row) are built as usual, for
+ *           moe_expert_forward_gathered. x may then be NULL too.
  *   ws      workspace: plan arrays written (see moe_plan_t). */
 int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_ids,
                 const int32_t* counts, uint16_t* x_perm, void* ws, void* stream);
@@ -284,6 +290,23 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape,
                                uint16_t* h, uint16_t* y_perm, uint16_t* const* combine_buf,
                                uint32_t* flags, uint32_t epoch, int32_t n_consumer_cu,
                                int32_t mode, void* producer_stream, void* consumer_stream);
+
+/* moe_expert_forward_overlap with the gather fused into the first
+ * projection (the dispatch side of [TLS] sec. 2.1 steps 2-3): instead of
+ * x_perm it takes x [R, T, H] bf16 (every rank's tokens, as given to
+ * moe_permute) and the first projection's tile loads read packed row r
+ * straight from x row row_src[r] of the workspace's plan (a zero row for
+ * padding), so x_perm is neither written nor read. Requires a preceding
+ * moe_permute on this workspace (x_perm may be NULL there). Every other
+ * argument, mode and output is as in moe_expert_forward_overlap, and h,
+ * y_perm and the combine buffers are bit-identical to it for the same plan,
+ * mode and n_consumer_cu. */
+int moe_expert_forward_gathered(moe_ctx_t* ctx, const moe_shape_t* shape,
+                                const uint16_t* x, const uint16_t* w1,
+                                const uint16_t* w3, const uint16_t* w2, void* ws,
+                                uint16_t* h, uint16_t* y_perm, uint16_t* const* combine_buf,
+                                uint32_t* flags, uint32_t epoch, int32_t n_consumer_cu,
+                                int32_t mode, void* producer_stream, void* consumer_stream);
 
 /* Step 5, weighted reduction ([TLS] sec. 2.1 step 5): for every token (s, t),
  * y_share[s, t] = sum over slots j ascending whose expert is local of

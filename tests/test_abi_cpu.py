@@ -86,16 +86,19 @@ def test_entry_points_reject_bad_args_before_hip():
     assert L.moe_route(C.byref(sh), fake, fake, fake, fake, None, None) == _abi.MOE_ERR_WORKSPACE
     assert L.moe_permute(C.byref(sh), fake, None, fake, fake, fake, None) == _abi.MOE_ERR_INVALID_ARG
     assert L.moe_permute(C.byref(sh), fake, fake, fake, fake, mis, None) == _abi.MOE_ERR_WORKSPACE
+    # index-only permute (x_perm NULL) may omit x; a gather target without x may not
+    assert L.moe_permute(C.byref(sh), None, fake, fake, fake, fake, None) == _abi.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(C.byref(sh), None, fake, fake, None, mis, None) == _abi.MOE_ERR_WORKSPACE
     bufs = (C.c_void_p * 4)(None, fake.value, fake.value, fake.value)
     assert L.moe_combine(C.byref(sh), bufs, fake, fake, fake, None, None) == _abi.MOE_ERR_INVALID_ARG
     bufs_missing = (C.c_void_p * 4)(None, fake.value, None, fake.value)
     assert L.moe_combine(C.byref(sh), bufs_missing, fake, fake, fake, fake, None) == _abi.MOE_ERR_INVALID_ARG
     # forward: no context, wrong gated/w3 pairing, bad mode
-    f = L.moe_expert_forward_overlap
-    assert f(None, C.byref(sh), fake, fake, None, fake, fake, fake, fake, bufs, fake, 1, 4, 0,
-             None, fake) == _abi.MOE_ERR_INVALID_ARG
-    assert f(None, C.byref(bad), fake, fake, None, fake, fake, fake, fake, bufs, fake, 1, 4, 0,
-             None, fake) == _abi.MOE_ERR_INVALID_ARG
+    for f in (L.moe_expert_forward_overlap, L.moe_expert_forward_gathered):
+        assert f(None, C.byref(sh), fake, fake, None, fake, fake, fake, fake, bufs, fake, 1, 4, 0,
+                 None, fake) == _abi.MOE_ERR_INVALID_ARG
+        assert f(None, C.byref(bad), fake, fake, None, fake, fake, fake, fake, bufs, fake, 1, 4, 0,
+                 None, fake) == _abi.MOE_ERR_INVALID_ARG
     st = C.c_int32()
     assert L.moe_read_status(C.byref(sh), mis, C.byref(st), None) == _abi.MOE_ERR_WORKSPACE
     assert L.moe_plan_view(C.byref(sh), mis, C.byref(_abi.MoePlan())) == _abi.MOE_ERR_WORKSPACE

@@ -4,7 +4,8 @@ benchmark uses (default band height, partition-model consumer CU count).
 Integer work (ids, counts, layout, schedule, plan, segments, row maps) is
 compared bit-exactly with the oracle in full; x_perm and the combine
 buffers are checked bit-exactly (rows against the source tokens / against
-y_perm); expert outputs and the share are compared on sampled rows/tokens
+y_perm), and the gathered forward (no x_perm) against the materialized one;
+expert outputs and the share are compared on sampled rows/tokens
 against the fp64 oracle (one expert's weights widened at a time).
 """
 import numpy as np
@@ -15,7 +16,7 @@ from synth import WORKLOADS, make_local_weights, make_logits, make_x
 from synth.workloads import ShareInputs
 from parity_util import (assert_plan_equal, bits, check_row_tiles, check_rows, make_gpu_share,
                          oracle_plan_arrays, say, widen)
-from test_gpu_parity import check_role_switch
+from test_gpu_parity import check_fused_gather, check_role_switch
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +101,9 @@ def test_full_size_parity(wid, layer, tb):
     torch.cuda.synchronize()
     assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits)
     assert np.array_equal(bits(b.y_share), share_bits)
+
+    say(f"[fullsize] {w.name}: gather fused into the first projection")
+    check_fused_gather(sh, ref, w, w.name, c, y_bits, share_bits)
 
     say(f"[fullsize] {w.name}: role switching")
     check_role_switch(sh, ref, w, 0, w.name)

@@ -111,8 +111,51 @@ def test_share_parity(case):
     assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits), "sequential y_perm differs from overlap"
     assert np.array_equal(bits(b.y_share), y_share_ovl), "sequential y_share differs from overlap"
 
+    # the gather fused into the first projection: same bits as the materialized path
+    check_fused_gather(sh, ref, w, name, c, y_bits, y_share_ovl)
+
     # role switching: the producer's workgroups copy; same bits as SEQUENTIAL with c = 0
     check_role_switch(sh, ref, w, r_self, name)
+
+
+def check_fused_gather(sh, ref, w, name, c, y_bits, share_bits):
+    """moe_permute without x_perm builds the same plan and indexes (row_src is
+    -1 on every padding row whatever the workspace held before), and
+    moe_expert_forward_gathered, whose first projection reads the rows straight
+    from x, gives the bits of the materialized overlapped run with the same c:
+    y_perm (padding rows included), the combine buffers and the share."""
+    import torch
+    from combine_overlap_amd import MOE_MODE_OVERLAP, ops
+    b = sh.buf
+    m_pad = int(ref.layout.m_pad)
+    # stale indexes that a missing padding pass would leave: every row -> token 0
+    v = ops.moe_plan_view(sh.shape, b.ws)
+    o = (v["row_src"] - b.ws.data_ptr()) // 4
+    b.ws.view(torch.int32)[o:o + int(sh.sizes.m_pad_max)].fill_(0)
+    sh.fused_gather = True
+    try:
+        sh.permute()
+        plan = sh.plan_arrays()
+        assert plan["status"] == 0
+        assert_plan_equal(plan, oracle_plan_arrays(ref))
+        for s in range(w.R):
+            if b.combine[s] is not None:
+                b.combine[s].fill_(float("nan"))
+        b.h.fill_(float("nan"))
+        b.y_perm.fill_(float("nan"))
+        sh.expert_forward(MOE_MODE_OVERLAP, n_consumer_cu=c)
+        sh.combine()
+        torch.cuda.synchronize()
+        assert sh.status() == 0
+        got = bits(b.y_perm[:m_pad])
+        assert np.array_equal(got, y_bits), f"{name}: gathered y_perm differs from the materialized run"
+        bd = ref.bands
+        for i in range(bd.n_remote):
+            s, r0, rc, n = int(bd.dest[i]), int(bd.row0[i]), int(bd.recv0[i]), int(bd.valid[i])
+            assert np.array_equal(bits(b.combine[s][rc:rc + n]), got[r0:r0 + n]), f"{name}: gathered band {i}"
+        assert np.array_equal(bits(b.y_share), share_bits), f"{name}: gathered y_share differs"
+    finally:
+        sh.fused_gather = False
 
 
 def check_role_switch(sh, ref, w, r_self, name):
