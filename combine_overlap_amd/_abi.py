@@ -24,9 +24,11 @@ MOE_GATE_SIGMOID = 1
 MOE_MODE_OVERLAP = 0
 MOE_MODE_SEQUENTIAL = 1
 MOE_MODE_ROLE_SWITCH = 2
+MOE_CONSUMER_AUTO = -1
 
 META_MPAD, META_NBANDS, META_NREMOTE, META_NSEG, META_STATUS, META_NUNITS, META_NTILES, \
-    META_NRTILES = range(8)
+    META_NRTILES, META_CAUTO = range(9)
+META_PRED = 20   # double over words 20-21
 
 
 class MoeShape(C.Structure):

@@ -19,8 +19,9 @@ OUT = os.path.join(HERE, "libmoe_overlap.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["route.hip", "permute.hip", "gemm.hip", "consumer.hip", "combine.hip", "abi.hip"]
-CXX_SOURCES = ["partition.cpp"]
+HIP_SOURCES = ["route.hip", "permute.hip", "gemm.hip", "consumer.hip", "combine.hip", "partition.hip",
+               "abi.hip"]
+CXX_SOURCES = []
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INC, "-I", CSRC,

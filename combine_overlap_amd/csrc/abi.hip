@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include "common.hpp"
+#include "partition_model.hpp"
 
 struct moe_ctx {
   int device;
@@ -15,6 +16,7 @@ struct moe_ctx {
   hipEvent_t tev[5];        // start, first projection end, producer end, consumer end, join
   uint64_t* trace;          // device timeline (see moe_ctx_set_trace) or null
   int32_t trace_flags;      // max_flags of the shape the trace was sized for
+  const int32_t* timed_meta;   // workspace meta words of the last timed call (device stamps)
 };
 
 namespace moe {
@@ -236,6 +238,14 @@ int moe_ctx_timings(moe_ctx_t* ctx, float* ms) {
   ms[2] = t13;
   ms[3] = t04;
   ms[4] = t23 > 0.f ? t23 : 0.f;
+  if (ctx->timed_mode == MOE_MODE_OVERLAP) {
+    // one launch holds both roles: the exposed transfer comes from its device
+    // clock stamps (100 MHz) of the last producer exit and consumer completion
+    uint64_t st[2];
+    if (hipMemcpy(st, ctx->timed_meta + META_T_PROD, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess)
+      return MOE_ERR_HIP;
+    ms[4] = st[1] > st[0] ? (float)((double)(st[1] - st[0]) * 1e-5) : 0.f;
+  }
   return MOE_OK;
 }
 
@@ -290,7 +300,13 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
   moe_plan_t p;
   plan_from_ws(g, ws, &p);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = hip_rc(launch_plan(g, counts, p, zero_row_of(g, ws), st))) != MOE_OK) return rc;
+  // the plan also evaluates the CU-split model for this device (MOE_CONSUMER_AUTO)
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MOE_ERR_HIP;
+  const moe_calib_t calib = default_calib(n_cu);
+  if ((rc = hip_rc(launch_plan(g, counts, p, zero_row_of(g, ws), calib, st))) != MOE_OK) return rc;
   return hip_rc(launch_gather(g, x, topk_ids, x_perm, p, st));
 }
 
@@ -318,19 +334,20 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
     if (combine_buf[s] == nullptr) return MOE_ERR_INVALID_ARG;
     bufs.p[s] = combine_buf[s];
   }
+  const bool auto_c = n_consumer_cu == MOE_CONSUMER_AUTO;
   if (mode == MOE_MODE_OVERLAP) {
-    if (!flags || epoch == 0 || n_consumer_cu < 1 || n_consumer_cu > 64 ||
-        n_consumer_cu >= ctx->n_cu || consumer_stream == producer_stream)
+    if (!flags || epoch == 0 ||
+        (!auto_c && (n_consumer_cu < 1 || n_consumer_cu > 64 || n_consumer_cu >= ctx->n_cu)))
       return MOE_ERR_INVALID_ARG;
   } else if (mode == MOE_MODE_ROLE_SWITCH) {
     if (!flags || epoch == 0) return MOE_ERR_INVALID_ARG;
-  } else if (n_consumer_cu < 0 || n_consumer_cu > 64 || n_consumer_cu >= ctx->n_cu) {
+  } else if (!auto_c && (n_consumer_cu < 0 || n_consumer_cu > 64 || n_consumer_cu >= ctx->n_cu)) {
     return MOE_ERR_INVALID_ARG;
   }
   moe_plan_t p;
   plan_from_ws(g, ws, &p);
   hipStream_t ps = static_cast<hipStream_t>(producer_stream);
-  hipStream_t cs = static_cast<hipStream_t>(consumer_stream);
+  (void)consumer_stream;
   const int ncu = ctx->n_cu;
   const bool tm = ctx->timing != 0;
   auto rec = [&](int i, hipStream_t st) { return tm ? hip_rc(hipEventRecord(ctx->tev[i], st)) : MOE_OK; };
@@ -340,8 +357,8 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
     return rc;
   if ((rc = rec(1, ps)) != MOE_OK) return rc;
   if (mode == MOE_MODE_SEQUENTIAL) {
-    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu, ncu - n_consumer_cu,
-                                  nullptr, ps))) != MOE_OK)
+    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu,
+                                  auto_c ? 0 : ncu - n_consumer_cu, nullptr, 0, nullptr, ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
     if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 4 * ncu, ps))) != MOE_OK) return rc;
@@ -353,8 +370,8 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   }
   if (mode == MOE_MODE_ROLE_SWITCH) {
     // one launch on every CU does both duties; the split is sized for all CUs
-    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu, ncu, &bufs, ps))) !=
-        MOE_OK)
+    if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu, ncu, &bufs, 0, nullptr,
+                                  ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
     if ((rc = rec(3, ps)) != MOE_OK) return rc;
@@ -363,19 +380,15 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
     ctx->timed_mode = mode;
     return MOE_OK;
   }
-  if ((rc = hip_rc(hipEventRecord(ctx->ev_producer, ps))) != MOE_OK) return rc;
-  if ((rc = hip_rc(hipStreamWaitEvent(cs, ctx->ev_producer, 0))) != MOE_OK) return rc;
-  if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu - n_consumer_cu,
-                                ncu - n_consumer_cu, nullptr, ps))) != MOE_OK)
+  // CU partition: one launch on every CU, workgroups [0, c) the consumer
+  if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu,
+                                auto_c ? 0 : ncu - n_consumer_cu, nullptr, auto_c ? -1 : n_consumer_cu, &bufs,
+                                ps))) != MOE_OK)
     return rc;
   if ((rc = rec(2, ps)) != MOE_OK) return rc;
-  if ((rc = hip_rc(launch_consumer(g, y_perm, bufs, p, flags, epoch, ctx->trace, n_consumer_cu, cs))) !=
-      MOE_OK)
-    return rc;
-  if ((rc = rec(3, cs)) != MOE_OK) return rc;
-  if ((rc = hip_rc(hipEventRecord(ctx->ev_consumer, cs))) != MOE_OK) return rc;
-  if ((rc = hip_rc(hipStreamWaitEvent(ps, ctx->ev_consumer, 0))) != MOE_OK) return rc;
+  if ((rc = rec(3, ps)) != MOE_OK) return rc;
   if ((rc = rec(4, ps)) != MOE_OK) return rc;
+  ctx->timed_meta = p.meta;
   ctx->timed = tm;
   ctx->timed_mode = mode;
   return MOE_OK;

@@ -19,8 +19,13 @@ constexpr int kChunk = 256;
 // local experts per rank at most (the plan and the chunk histograms size LDS by it)
 constexpr int kPlanMaxElRoute = 256;
 // meta words in the workspace
+// META_CAUTO: consumer CUs the plan kernel's evaluation of the CU-split model
+// chose (MOE_CONSUMER_AUTO); META_PRED: its predicted time (double, two words).
+// META_T_PROD / META_T_CONS: uint64 device clock stamps (two words each) of the
+// overlapped output projection's last producer exit and last consumer completion
 enum { META_MPAD = 0, META_NBANDS = 1, META_NREMOTE = 2, META_NSEG = 3, META_STATUS = 4, META_NUNITS = 5,
-       META_NTILES = 6, META_NRTILES = 7, META_WORDS = 64 };
+       META_NTILES = 6, META_NRTILES = 7, META_CAUTO = 8, META_T_PROD = 16, META_T_CONS = 18,
+       META_PRED = 20, META_WORDS = 64 };
 // GEMM row-tile height: the producer computes tiles of this many rows over each
 // expert's tb_m-aligned rows, independently of the (possibly smaller) band
 constexpr int kTileM = 256;
@@ -98,8 +103,9 @@ hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, fl
                         const moe_plan_t& p, hipStream_t st);
 hipError_t launch_count(const Geometry& g, const int32_t* ids, int32_t* counts, const moe_plan_t& p,
                         hipStream_t st);
+// also evaluates the CU-split model for `calib` (META_CAUTO, META_PRED)
 hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, uint16_t* zero_row,
-                       hipStream_t st);
+                       const moe_calib_t& calib, hipStream_t st);
 // x_perm null: only the indexes (row_src, with -1 for every padding row, and recv_row)
 hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
                          uint16_t* x_perm, const moe_plan_t& p, hipStream_t st);
@@ -113,9 +119,13 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t*
 // copy_bufs: non-null gives the launch the consumer's duty as well (role
 // switching): between tiles a workgroup copies every remote segment whose row
 // tiles are all flagged, and once the tiles run out it drains the rest
+// n_cons != 0: workgroups [0, n_cons) of the launch are the consumer (copying
+// into cons_bufs), the others the producer (the CU-partition overlap in one
+// launch); n_cons = -1 and split_grid = 0 take the plan's consumer count
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
-                        int grid, int split_grid, const BufPtrs* copy_bufs, hipStream_t st);
+                        int grid, int split_grid, const BufPtrs* copy_bufs, int n_cons,
+                        const BufPtrs* cons_bufs, hipStream_t st);
 hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
                            const uint32_t* flags, uint32_t epoch, uint64_t* trace, int n_wg,
                            hipStream_t st);

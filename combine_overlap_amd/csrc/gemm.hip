@@ -64,7 +64,7 @@
 //              columns in registers.
 #include <type_traits>
 
-#include "common.hpp"
+#include "consumer.hpp"
 
 #ifndef MOE_DEVICE_SCOPE_PUBLISH
 #define MOE_DEVICE_SCOPE_PUBLISH 1
@@ -132,11 +132,17 @@ struct GemmArgs {
   const int32_t* seg_dst_row;
   const int32_t* seg_dest;
   uint64_t* trace;             // optional timeline: [0] start, [8 + t] tile t done
+  // CU-partition overlap inside one launch: workgroups [0, n_cons) run the
+  // consumer (one per CU, n_cons / 8 per XCD), the others the tiles;
+  // -1: the plan's choice meta[META_CAUTO]
+  int n_cons;
+  ConsumerArgs cons;
   uint32_t epoch;
   int K, Nw, Nout, tiles_n;
   int xb, xn;                  // XCD grid: xcd = (row tile % xb) * xn + (column tile % xn)
   int gp, gq;                  // blocks of gp row tiles x gq column tiles inside an XCD queue
-  int px;                      // workgroups per XCD queue the tail split is sized for
+  int px;                      // workgroups per XCD queue the tail split is sized for;
+                               // 0: (grid - meta[META_CAUTO]) / 8
 };
 
 // Queue index i of XCD x -> tile (row-tile schedule position * tiles_n + column tile).
@@ -361,9 +367,19 @@ __device__ void copy_duty(const GemmArgs& a, bool wait, int tid, int* s_copy) {
   }
 }
 
-template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool COPY = false, bool GATHER = false>
+// device clock stamps of an overlapped output projection (100 MHz ticks),
+// cleared by the first projection: the last producer workgroup's exit and
+// the last consumer workgroup's completion
+__device__ __forceinline__ void stamp_max(const int32_t* meta, int word) {
+  uint64_t* w = reinterpret_cast<uint64_t*>(const_cast<int32_t*>(meta) + word);
+  __hip_atomic_fetch_max(w, (uint64_t)wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool COPY = false, bool GATHER = false,
+          bool CONS = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   using C = Tile<BM, BN, BK, NS, WM, WN>;
+  static_assert(!CONS || C::LDS_ELEMS * 2 >= kSegLdsBytes, "consumer tables fit the tile's LDS");
   static_assert(EPI != EPI_GATED || C::FN % 2 == 0, "gated tiles pair W1/W3 32-column blocks per wave");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
   __shared__ int s_item[5];   // tile, chunk, nsplit, slot, queue
@@ -377,8 +393,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   // the other launch's queue and tail counters (this launch's were cleared by it)
   if (blockIdx.x == 0 && tid < kXcds * kCtrStride) a.other_ctr[tid] = 0;
   if (blockIdx.x == 0 && tid < kCtrStride) a.other_copy[tid] = 0;
-  const int px = max(1, a.px);
+  if (EPI != EPI_PLAIN && blockIdx.x == 0 && tid < 4)   // the output projection's stamps
+    const_cast<int32_t*>(a.meta)[META_T_PROD + tid] = 0;
+  const int px = max(1, a.px > 0 ? a.px : ((int)gridDim.x - a.meta[META_CAUTO]) / kXcds);
   if (a.trace != nullptr && blockIdx.x == 0 && tid == 0) a.trace[0] = wall_clock64();
+  if constexpr (CONS) {
+    const int n_cons = a.n_cons > 0 ? a.n_cons : a.meta[META_CAUTO];
+    if ((int)blockIdx.x < n_cons) {
+      consume<C::NT, 4, 16>(a.cons, blockIdx.x, n_cons, reinterpret_cast<int*>(lds), s_copy);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this workgroup's copies have completed
+      __syncthreads();
+      if (tid == 0) stamp_max(a.meta, META_T_CONS);
+      return;
+    }
+  }
 
   // DMA lane geometry: lane -> (row inside the instruction, physical chunk).
   // The swizzle depends on the tile row modulo 2*RPI, so one byte offset per
@@ -423,6 +451,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     const int tile = s_item[0];
     if (tile < 0) {
       if constexpr (COPY) copy_duty<C::NT>(a, true, tid, s_copy);
+      if constexpr (CONS) if (tid == 0) stamp_max(a.meta, META_T_PROD);
       break;
     }
     const int chunk = __builtin_amdgcn_readfirstlane(s_item[1]);
@@ -717,6 +746,11 @@ static hipError_t launch_t(const GemmArgs& a, int grid, hipStream_t st) {
       hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI, true>), dim3(grid), dim3(WM * WN * 64), 0, st, a);
       return hipGetLastError();
     }
+    if (a.n_cons != 0) {
+      hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI, false, false, true>), dim3(grid),
+                         dim3(WM * WN * 64), 0, st, a);
+      return hipGetLastError();
+    }
   } else {
     if (a.a_rows != nullptr) {
       hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI, false, true>), dim3(grid), dim3(WM * WN * 64), 0,
@@ -783,7 +817,8 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t*
 
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
-                        int grid, int split_grid, const BufPtrs* copy_bufs, hipStream_t st) {
+                        int grid, int split_grid, const BufPtrs* copy_bufs, int n_cons,
+                        const BufPtrs* cons_bufs, hipStream_t st) {
   GemmArgs a{};
   a.A = h;
   a.B0 = w2;
@@ -809,6 +844,10 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
     a.seg_dst_row = p.seg_dst_row;
     a.seg_dest = p.seg_dest;
   }
+  if (n_cons != 0) {
+    a.n_cons = n_cons;
+    a.cons = consumer_args(g, y, *cons_bufs, p, flags, epoch, trace);
+  }
   a.flags = flags;
   a.trace = trace;
   a.epoch = epoch;
@@ -816,7 +855,7 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
   a.Nw = g.H;
   a.Nout = g.H;
   a.tiles_n = g.tiles2;
-  a.px = split_grid / kXcds;
+  a.px = split_grid > 0 ? split_grid / kXcds : 0;
   return dispatch<EPI_PLAIN>(a, g.tile_m, g.bn2, grid, st);
 }
 

@@ -23,6 +23,7 @@
 // not copied: only the indexes are built (row_src, -1 for padding). The plan
 // also zeroes the one row of H zeros that padding rows read there.
 #include "common.hpp"
+#include "partition_model.hpp"
 
 namespace moe {
 
@@ -34,10 +35,18 @@ __device__ __forceinline__ int nseg_of(int nb, int mgb) {
 constexpr int kPlanMaxEl = 256;
 constexpr int kPlanMaxGroups = 2048;  // E_l * R limit (checked on the host)
 
+// device evaluation of the CU-split model: bounds of its LDS tables (past
+// them the choice falls back to calib.c_min, with META_PRED = -1)
+constexpr int kPartPos = 2048;     // row tiles
+constexpr int kPartSegs = 2048;    // segments
+constexpr int kPartWaves = 2048;   // producer waves over all candidates
+constexpr int kPartCand = 64;      // candidates
+
 // single workgroup: everything here is O(E_l * R) metadata
+
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ counts, moe_plan_t p,
-                                                u32x4* __restrict__ zero_row, int R, int El, int r_self,
-                                                int tb, int mgb, int H) {
+                                                u32x4* __restrict__ zero_row, const moe_calib_t calib,
+                                                int R, int El, int r_self, int tb, int mgb, int H, int F) {
   __shared__ int s_cnt[kPlanMaxGroups];
   __shared__ int s_rel[kPlanMaxGroups];      // group start relative to its expert base
   __shared__ int s_bandoff[kPlanMaxGroups];  // first band index of the group (schedule order)
@@ -50,6 +59,14 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
   __shared__ int s_trpos[kPlanMaxEl];       // schedule position of e's first remote tile
   __shared__ int s_tlpos[kPlanMaxEl];       // schedule position of e's first local-only tile
   __shared__ int s_usum[16];             // per-wave totals of the copy-unit scan
+  __shared__ double s_tt[kPartPos];      // model: instance time of the row tile at each position
+  __shared__ double s_wv[kPartWaves];    // model: wave lengths, then wave ends, per candidate
+  __shared__ int s_spos[kPartSegs];      // model: position of each segment's last row tile
+  __shared__ int s_sfrom[kPartSegs];     // model: valid rows of segments i, i+1, ...
+  __shared__ int s_woff[kPartCand + 1];  // model: first wave of each candidate
+  __shared__ double s_tprod[kPartCand];
+  __shared__ double s_red[16];
+  __shared__ int s_fit, s_rtot;
   const int tid = threadIdx.x;
   const int G = El * R;
   for (int i = tid; i < H / 8; i += blockDim.x) zero_row[i] = u32x4{0u, 0u, 0u, 0u};
@@ -222,6 +239,118 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ count
   __syncthreads();
   int acc = s_usum[wave] + incl - local;
   for (int sg = lo; sg < hi; ++sg) { p.seg_unit0[sg] = acc; acc += units(sg); }
+
+  // ---- the CU-split model (partition_model.hpp) for this plan's row tiles
+  // and segments, the same closed form as moe_plan_partition
+  const int n_pos = s_tbase[El];
+  const int tiles2 = (H + kModelTileCols - 1) / kModelTileCols;
+  const int n_cand = (calib.c_max - calib.c_min) / calib.c_step + 1;
+  __syncthreads();   // s_usum is reused below
+  if (tid == 0) {
+    int fit = n_pos <= kPartPos && n_seg <= kPartSegs && n_cand <= kPartCand;
+    int w = 0;
+    for (int ci = 0; fit && ci < n_cand; ++ci) {
+      const long P = calib.n_cu - (calib.c_min + ci * calib.c_step);
+      s_woff[ci] = w;
+      w += (int)(((long)n_pos * tiles2 + P - 1) / P);
+      if (w > kPartWaves) fit = 0;
+    }
+    if (fit) s_woff[n_cand] = w;
+    s_fit = fit;
+  }
+  __syncthreads();
+  if (!s_fit) {
+    if (tid == 0) {
+      p.meta[META_CAUTO] = calib.c_min;
+      *reinterpret_cast<double*>(p.meta + META_PRED) = -1.0;
+    }
+    return;
+  }
+  for (int q = tid; q < n_pos; q += blockDim.x) {   // instance time per schedule position
+    const int rt = p.tile_sched[q];
+    const int e = p.tile_expert[rt];
+    const long m_e = (long)s_rel[e * R + r_self] + s_cnt[e * R + r_self];   // the local group is last
+    s_tt[q] = model_tile_time(p.tile_rows[rt], F, model_rate(calib, m_e));
+  }
+  // segments: position of the last row tile (remote tiles of expert e sit at
+  // positions s_trpos[e] + j) and the valid rows from each segment on
+  // (integers: total minus an exclusive prefix, chunked like the unit scan)
+  int rsum = 0;
+  for (int sg = lo; sg < hi; ++sg) {
+    const int e = p.band_expert[p.seg_band0[sg]];
+    s_spos[sg] = s_trpos[e] + (p.seg_tile1[sg] - s_tbase[e]);
+    rsum += p.seg_rows[sg];
+  }
+  int rincl = rsum;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(rincl, d, 64);
+    if (lane >= d) rincl += y;
+  }
+  if (lane == 63) s_usum[wave] = rincl;
+  __syncthreads();
+  if (tid == 0) {
+    int a = 0;
+    for (int w = 0; w < (int)blockDim.x / 64; ++w) { const int v = s_usum[w]; s_usum[w] = a; a += v; }
+    s_rtot = a;
+  }
+  __syncthreads();
+  int before = s_usum[wave] + rincl - rsum;   // valid rows of the segments before this thread's chunk
+  for (int sg = lo; sg < hi; ++sg) { s_sfrom[sg] = s_rtot - before; before += p.seg_rows[sg]; }
+  // producer waves: lengths (maxima over the positions each wave covers)
+  const int tw = s_woff[n_cand];
+  for (int idx = tid; idx < tw; idx += blockDim.x) {
+    int ci = 0;
+    while (s_woff[ci + 1] <= idx) ++ci;
+    const long P = calib.n_cu - (calib.c_min + ci * calib.c_step);
+    long p0, p1;
+    model_wave_span(idx - s_woff[ci], P, tiles2, n_pos, &p0, &p1);
+    double len = 0.0;
+    for (long q = p0; q <= p1; ++q) len = len > s_tt[q] ? len : s_tt[q];
+    s_wv[idx] = len;
+  }
+  __syncthreads();
+  if (tid < n_cand) {   // wave ends, in order
+    const long P = calib.n_cu - (calib.c_min + tid * calib.c_step);
+    const long n_inst = (long)n_pos * tiles2;
+    double t = 0.0;
+    for (int w = s_woff[tid]; w < s_woff[tid + 1]; ++w) {
+      const long wi = w - s_woff[tid];
+      t = model_wave_end(t, s_wv[w], n_inst - wi * P < P ? n_inst - wi * P : P, P);
+      s_wv[w] = t;
+    }
+    s_tprod[tid] = t;
+  }
+  __syncthreads();
+  double best_t = 0.0;
+  int best_c = -1;
+  for (int ci = 0; ci < n_cand; ++ci) {
+    const int c = calib.c_min + ci * calib.c_step;
+    const long P = calib.n_cu - c;
+    const double bw = model_copy_bw(calib, c);
+    double tc = 0.0;
+    for (int sg = tid; sg < n_seg; sg += blockDim.x) {
+      const double r = s_wv[s_woff[ci] + (int)(((long)s_spos[sg] * tiles2 + tiles2 - 1) / P)];
+      const double v = model_copy_end(r, s_sfrom[sg], H, bw);
+      tc = tc > v ? tc : v;
+    }
+    for (int d = 32; d > 0; d >>= 1) {
+      const double o = __shfl_xor(tc, d, 64);
+      tc = tc > o ? tc : o;
+    }
+    if (lane == 0) s_red[wave] = tc;
+    __syncthreads();
+    if (tid == 0) {
+      double m = 0.0;
+      for (int w = 0; w < (int)blockDim.x / 64; ++w) m = m > s_red[w] ? m : s_red[w];
+      const double total = model_total(s_tprod[ci], m, n_seg > 0, calib.seg_latency_s);
+      if (best_c < 0 || total < best_t) { best_t = total; best_c = c; }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    p.meta[META_CAUTO] = best_c;
+    *reinterpret_cast<double*>(p.meta + META_PRED) = best_t;
+  }
 }
 
 // index: every local (token, slot) -> its packed row; writes row_src and recv_row.
@@ -310,9 +439,9 @@ __global__ __launch_bounds__(256) void k_pad_index(moe_plan_t p, int tb) {
 }
 
 hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, uint16_t* zero_row,
-                       hipStream_t st) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, counts, p, reinterpret_cast<u32x4*>(zero_row),
-                     g.R, g.El, g.r_self, g.tb_m, g.mgb, g.H);
+                       const moe_calib_t& calib, hipStream_t st) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, counts, p, reinterpret_cast<u32x4*>(zero_row), calib,
+                     g.R, g.El, g.r_self, g.tb_m, g.mgb, g.H, g.F);
   return hipGetLastError();
 }
 

@@ -145,22 +145,36 @@ class MoEShare:
 
     def layer(self, mode=_abi.MOE_MODE_OVERLAP, n_consumer_cu: Optional[int] = None, calib=None,
               stream=None) -> int:
-        """The whole share with the per-layer CU split: route; counts to pinned
-        host memory (async); permute runs on the GPU while the host waits for the
-        counts and evaluates the partition model; expert phase; combine.
-        Returns the consumer CU count used."""
+        """The whole share with the per-layer CU split: route, permute, expert
+        phase, combine. By default the plan kernel picks the consumer CU count
+        on the device (MOE_CONSUMER_AUTO) and the host never waits. With a
+        calibration the host evaluates the partition model instead: the counts
+        go to pinned host memory (async) and the permute runs while the host
+        waits for them. Returns the consumer CU count passed to the forward."""
         s = torch.cuda.current_stream(self.device) if stream is None else stream
         self.route(s)
-        with torch.cuda.stream(s):
-            self.counts_host.copy_(self.buf.counts, non_blocking=True)
-        self.counts_ready.record(s)
-        self.permute(s)
-        if n_consumer_cu is None:
+        if n_consumer_cu is None and calib is not None:
+            with torch.cuda.stream(s):
+                self.counts_host.copy_(self.buf.counts, non_blocking=True)
+            self.counts_ready.record(s)
+            self.permute(s)
             self.counts_ready.synchronize()
             n_consumer_cu = ops.moe_plan_partition(self.shape, self.counts_host.numpy(), calib)[0]
+        else:
+            self.permute(s)
+            if n_consumer_cu is None:
+                n_consumer_cu = _abi.MOE_CONSUMER_AUTO
         self.expert_forward(mode, n_consumer_cu, s)
         self.combine(s)
         return n_consumer_cu
+
+    def auto_consumer_cu(self):
+        """(consumer CUs, predicted seconds) the last permute's plan chose on the device."""
+        torch.cuda.synchronize(self.device)
+        v = ops.moe_plan_view(self.shape, self.buf.ws)
+        o = (v["meta"] - self.buf.ws.data_ptr()) // 4
+        meta = self.buf.ws.view(torch.int32)[o:o + _abi.META_PRED + 2].cpu().numpy()
+        return int(meta[_abi.META_CAUTO]), float(meta[_abi.META_PRED:].view(np.float64)[0])
 
     def status(self, stream=None) -> int:
         return ops.moe_read_status(self.shape, self.buf.ws, stream)

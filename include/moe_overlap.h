@@ -61,6 +61,8 @@ extern "C" {
 
 enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 };
 enum { MOE_MODE_OVERLAP = 0, MOE_MODE_SEQUENTIAL = 1, MOE_MODE_ROLE_SWITCH = 2 };
+/* n_consumer_cu of the expert forward: the plan's own choice (see moe_permute) */
+#define MOE_CONSUMER_AUTO (-1)
 
 /* Problem shape of one rank's share ([TLS] sec. 3.2, Algorithm 1 inputs).
  *  R        simulated ranks (1..MOE_MAX_RANKS)
@@ -109,7 +111,11 @@ typedef struct {
 typedef struct {
   int32_t* meta;          /* [0]=m_pad [1]=n_bands [2]=n_remote_bands [3]=n_segments
                              [4]=device status (0 or MOE_ERR_*) [5]=64 KiB copy units
-                             [6]=GEMM row tiles [7]=tiles holding a remote band     */
+                             [6]=GEMM row tiles [7]=tiles holding a remote band
+                             [8]=consumer CUs chosen by the plan (MOE_CONSUMER_AUTO)
+                             [20..21]=its predicted time in seconds (a double; -1 if
+                             the device evaluation fell back to c_min)
+                             [16..19]=internal clock stamps of the overlapped forward */
   int32_t* group_row;     /* [E_l*R] first packed row of group (e, s)                */
   int32_t* expert_base;   /* [E_l+1] first packed row of expert e, tb_m-aligned      */
   int32_t* recv_off;      /* [R*E_l] first row of (e, s) in rank s's combine buffer */
@@ -184,12 +190,14 @@ int moe_ctx_num_cus(const moe_ctx_t* ctx);
  * streams the kernels run on (off by default; enabling creates 5 events).
  * moe_ctx_timings waits for the last timed call and writes, in ms:
  *   ms[0] first projection (all CUs)
- *   ms[1] output projection (producer) from its start to its end
- *   ms[2] from the output projection's start to the consumer's end
+ *   ms[1] output projection launch (OVERLAP: producer and consumer roles;
+ *         ROLE_SWITCH: with the copy)
+ *   ms[2] from the output projection's start to the end of the transfer
  *         (SEQUENTIAL: to the end of the bulk copy)
  *   ms[3] whole call
- *   ms[4] exposed transfer: consumer end minus producer end, >= 0
- *         (SEQUENTIAL: the bulk copy's duration)
+ *   ms[4] exposed transfer (OVERLAP: the last consumer completion minus the
+ *         last producer exit, >= 0, from device clock stamps; SEQUENTIAL: the
+ *         bulk copy's duration; ROLE_SWITCH: 0) 
  * Returns MOE_ERR_INVALID_ARG if timing is off or nothing was timed. */
 int moe_ctx_set_timing(moe_ctx_t* ctx, int enable);
 int moe_ctx_timings(moe_ctx_t* ctx, float* ms);
@@ -229,7 +237,14 @@ int moe_route(const moe_shape_t* shape, const float* logits, int32_t* topk_ids,
  *           NULL: no row is copied; the plan and the indexes (row_src with -1
  *           for every padding row, recv_row) are built as usual, for
  *           moe_expert_forward_gathered. x may then be NULL too.
- *   ws      workspace: plan arrays written (see moe_plan_t). */
+ *   ws      workspace: plan arrays written (see moe_plan_t).
+ * The plan kernel also evaluates the CU-split model of moe_plan_partition
+ * (calib = NULL, with n_cu = the current device's CU count) on the device,
+ * from this plan's row tiles and segments, and leaves c in meta[8] for
+ * n_consumer_cu = MOE_CONSUMER_AUTO: the same c and predicted time as
+ * moe_plan_partition returns for these counts when shape->mgb is the mgb it
+ * returns. Plans past its table bounds (2048 row tiles, 2048 segments, 2048
+ * producer waves over the candidates) take c_min. */
 int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_ids,
                 const int32_t* counts, uint16_t* x_perm, void* ws, void* stream);
 
@@ -259,15 +274,18 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *   flags    [max_flags] uint32, zero-initialised once by the caller and then
  *            reused: tile t is ready when flags[t] == epoch
  *   epoch    nonzero, different from the previous call's epoch on these flags
- *   n_consumer_cu  c: OVERLAP 1..64, SEQUENTIAL 0..64, and < device CUs. The
+ *   n_consumer_cu  c: OVERLAP 1..64, SEQUENTIAL 0..64, and < device CUs; or
+ *            MOE_CONSUMER_AUTO (OVERLAP, SEQUENTIAL): the c the preceding
+ *            moe_permute chose on the device, with no host round trip. The
  *            output projection splits its tail tiles along K for CUs - c
  *            producers in both modes, so OVERLAP and SEQUENTIAL calls with the
  *            same c compute bit-identical results (different c may differ in
  *            the last bits of the split tiles, from the fp32 summation order)
- *   mode     MOE_MODE_OVERLAP: first projection on all CUs; then the output
- *            projection on (CUs - c) persistent workgroups raising a flag per
- *            tile, concurrently with the consumer on c workgroups that copies
- *            every segment once all its tiles are flagged.
+ *   mode     MOE_MODE_OVERLAP: first projection on all CUs; then one launch
+ *            of the output projection on every CU whose first c workgroups
+ *            (one per CU, c/8 per XCD) are the consumer, copying every segment
+ *            once all its tiles are flagged, while the others run the tiles as
+ *            persistent producers raising a flag per tile.
  *            MOE_MODE_SEQUENTIAL (baseline, [TLS] sec. 4.1.3): both projections
  *            on all CUs, then one bulk copy of all remote rows on all CUs.
  *            MOE_MODE_ROLE_SWITCH: both projections on all CUs, the output
@@ -280,9 +298,8 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *            SEQUENTIAL with c = 0). consumer_stream is not used. The
  *            per-layer worker split of [Weave] taken to its temporal end.
  *   producer_stream  all work is ordered after prior work on this stream and
- *            completes before later work on it (the consumer is joined back)
- *   consumer_stream  second stream for the consumer (OVERLAP only; must differ
- *            from producer_stream)
+ *            completes before later work on it
+ *   consumer_stream  unused (every mode runs on producer_stream); may be NULL
  * Calls that overlap in time on the same flags/workspace race. */
 int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape,
                                const uint16_t* x_perm, const uint16_t* w1,

@@ -16,7 +16,7 @@ from synth import WORKLOADS, make_local_weights, make_logits, make_x
 from synth.workloads import ShareInputs
 from parity_util import (assert_plan_equal, bits, check_row_tiles, check_rows, make_gpu_share,
                          oracle_plan_arrays, say, widen)
-from test_gpu_parity import check_fused_gather, check_role_switch
+from test_gpu_parity import check_auto_partition, check_fused_gather, check_role_switch
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,7 @@ FULL = [(2, 0, 64), (3, 0, 256), (4, 0, 32), (5, 0, 64), (5, 2, 128)]
 @pytest.mark.parametrize("wid,layer,tb", FULL, ids=[f"cfg{a}_l{b}_tb{c}" for a, b, c in FULL])
 def test_full_size_parity(wid, layer, tb):
     import torch
-    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL
+    from combine_overlap_amd import MOE_CONSUMER_AUTO, MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL
     w = WORKLOADS[wid]
     say(f"[fullsize] {w.name} layer {layer} tb_m={tb}: inputs")
     W1, W3, W2 = make_local_weights(w, 0)
@@ -50,6 +50,8 @@ def test_full_size_parity(wid, layer, tb):
     assert plan["status"] == 0
     assert_plan_equal(plan, oracle_plan_arrays(ref))
     check_row_tiles(plan, ref, sh.sizes.tile_m)
+    check_auto_partition(sh, w.name)
+    assert sh.auto_consumer_cu()[0] == c
     m_pad = plan["m_pad"]
     rng = np.random.default_rng(wid * 10 + layer)
     rows = rng.choice(m_pad, size=min(m_pad, 512), replace=False)
@@ -101,6 +103,18 @@ def test_full_size_parity(wid, layer, tb):
     torch.cuda.synchronize()
     assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits)
     assert np.array_equal(bits(b.y_share), share_bits)
+
+    say(f"[fullsize] {w.name}: the plan's own consumer count (no host round trip)")
+    for mode in (MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL):
+        for s in range(w.R):
+            if b.combine[s] is not None:
+                b.combine[s].fill_(float("nan"))
+        sh.expert_forward(mode, n_consumer_cu=MOE_CONSUMER_AUTO)
+        sh.combine()
+        torch.cuda.synchronize()
+        assert sh.status() == 0
+        assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits), f"mode {mode}: AUTO y_perm differs"
+        assert np.array_equal(bits(b.y_share), share_bits), f"mode {mode}: AUTO y_share differs"
 
     say(f"[fullsize] {w.name}: gather fused into the first projection")
     check_fused_gather(sh, ref, w, w.name, c, y_bits, share_bits)

@@ -72,6 +72,7 @@ def test_share_parity(case):
     check_row_tiles(plan, ref, sh.sizes.tile_m)
     m_pad = plan["m_pad"]
     assert np.array_equal(widen(b.x_perm[:m_pad]), ref.x_perm), "x_perm differs"
+    check_auto_partition(sh, name)
 
     # expert FFN + overlapped transfer
     for s in range(w.R):
@@ -116,6 +117,22 @@ def test_share_parity(case):
 
     # role switching: the producer's workgroups copy; same bits as SEQUENTIAL with c = 0
     check_role_switch(sh, ref, w, r_self, name)
+
+
+def check_auto_partition(sh, name):
+    """The plan kernel's evaluation of the CU-split model (MOE_CONSUMER_AUTO)
+    picks the host model's c with a bit-identical predicted time whenever
+    the plan's segments are the host model's (shape mgb = its mgb), and a
+    valid candidate otherwise."""
+    c_dev, t_dev = sh.auto_consumer_cu()
+    c_host, g_host, t_host = sh.partition()
+    say(f"  {name}: CU split device c={c_dev} ({t_dev:.6e} s), host c={c_host} ({t_host:.6e} s), "
+        f"mgb {sh.shape.mgb} / model {g_host}")
+    assert c_dev in range(8, 49, 8), f"{name}: device c {c_dev}"
+    assert t_dev > 0 or (t_dev == 0 and t_host == 0)
+    if g_host == sh.shape.mgb and sh.ctx.num_cus == 256:
+        assert c_dev == c_host, f"{name}: device c {c_dev} != host c {c_host}"
+        assert t_dev == t_host, f"{name}: predicted {t_dev!r} != {t_host!r}"
 
 
 def check_fused_gather(sh, ref, w, name, c, y_bits, share_bits):
