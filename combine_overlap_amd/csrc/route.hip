@@ -3,12 +3,14 @@
 // plus the per-(local expert, source rank) row counts that the dispatch
 // delivers to this rank.
 //
-// k_route: one routing group of G lanes (G = the smallest power of two with
-// 8 G >= E) owns a token; lane i of the group holds logits i, i+G, i+2G, ...
-// (at most 8). Each of the k rounds is a butterfly arg-max inside the group
-// (higher logit wins, equal logits go to the lower expert id) followed by
-// masking the winner. Small groups keep the butterfly short and put many
-// tokens in each wave.
+// k_route: one routing group of G lanes (the fewest with at most 32 logits
+// each: G = 8 for 256 experts, 1 up to 32) owns a token; lane i of the group
+// holds the logits of experts i, i+G, i+2G, ... as order-preserving integer
+// keys. Each of the k rounds takes the lane's best key by a tournament, then
+// the group's best by a butterfly (higher logit wins, equal logits go to the
+// lower expert id), and the winner's key drops to 0 (below every logit).
+// The width balances the per-token instruction count (vector-ALU issue
+// bound) against enough waves per SIMD to hide each wave's dependency chain.
 // The grid covers the tokens (a workgroup holds 256 / G of them), so every
 // CU has many tokens' loads in flight.
 //
@@ -22,64 +24,85 @@ namespace moe {
 
 constexpr int kRouteThreads = 256;
 
-template <int NQ>
+// order-preserving unsigned key of a float (larger key = larger value; -0 is
+// taken as +0); 0 is below every key and marks "not a candidate"
+__device__ __forceinline__ uint32_t order_key(uint32_t u) {
+  u = (u == 0x80000000u) ? 0u : u;
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);   // negative: all bits flipped
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+template <int G, int NQ>
 __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict__ logits,
                                                           int32_t* __restrict__ ids_out,
                                                           float* __restrict__ gates_out,
-                                                          int n_tok, int E, int k, int G,
-                                                          int gate_kind) {
+                                                          int n_tok, int E, int k, int gate_kind) {
   const int lane = threadIdx.x & 63;
-  const int gi = lane % G;                               // lane inside the routing group
-  const int per_block = kRouteThreads / G;
+  const int gi = lane & (G - 1);                         // lane inside the routing group
+  constexpr int per_block = kRouteThreads / G;
   const int g_tok = blockIdx.x * per_block + (int)threadIdx.x / G;
   const bool active = g_tok < n_tok;
   const size_t g = active ? (size_t)g_tok : 0;
-  float v[NQ];
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(logits) + g * E;
+  // keys of experts gi + q G: unconditional loads with clamped indices
+  // (predicated ones would each wait for the previous), then the selection
+  uint32_t key[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int e = gi + q * G;
-    v[q] = (active && e < E) ? logits[g * E + e] : -INFINITY;
-  }
-  uint32_t taken = 0;
-  float sel_v[16];
+  for (int q = 0; q < NQ; ++q) key[q] = row[min(gi + q * G, E - 1)];
+  // (an inactive token's group reads row 0 and writes nothing; experts past E get key 0)
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) key[q] = order_key(key[q]) & (0u - (uint32_t)(gi + q * G < E));
+  uint32_t sel_k[16];
   int sel_id[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     if (r >= k) break;
-    // best of this lane: ids rise with q, so a strict '>' keeps the lowest id among equals
-    float bv = -INFINITY;
-    int bid = 0x7fffffff;
+    // best of this lane: a tournament over q in which the right entry replaces
+    // the left only if strictly larger, so the lower q (lower id) wins ties
+    uint32_t tk[NQ];
+    int tq[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int e = gi + q * G;
-      if (e < E && !(taken >> q & 1u) && (bid == 0x7fffffff || v[q] > bv)) { bv = v[q]; bid = e; }
-    }
-    for (int off = G >> 1; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, G);
+    for (int q = 0; q < NQ; ++q) { tk[q] = key[q]; tq[q] = q; }
+#pragma unroll
+    for (int st = 1; st < NQ; st <<= 1)
+#pragma unroll
+      for (int q = 0; q + st < NQ; q += 2 * st)
+        if (tk[q + st] > tk[q]) { tk[q] = tk[q + st]; tq[q] = tq[q + st]; }
+    uint32_t bk = tk[0];
+    int bid = gi + tq[0] * G;
+#pragma unroll
+    for (int off = G >> 1; off > 0; off >>= 1) {   // across the group: larger key, then lower id
+      const uint32_t ok = __shfl_xor(bk, off, G);
       const int oid = __shfl_xor(bid, off, G);
-      if (ov > bv || (ov == bv && oid < bid)) { bv = ov; bid = oid; }
+      if (ok > bk || (ok == bk && oid < bid)) { bk = ok; bid = oid; }
     }
-    if (bid % G == gi) taken |= 1u << (bid / G);
-    sel_v[r] = bv;
+    const int wq = ((bid & (G - 1)) == gi) ? bid / G : -1;   // the winner leaves the candidates
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) key[q] = (q == wq) ? 0u : key[q];
+    sel_k[r] = bk;
     sel_id[r] = bid;
   }
   if (!active) return;
   // gates over the k selected logits (fp32)
   float w[16];
   float sum = 0.f;
+  const float v0 = key_value(sel_k[0]);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     if (r >= k) break;
+    const float v = key_value(sel_k[r]);
     float x;
-    if (gate_kind == MOE_GATE_SOFTMAX) x = expf(sel_v[r] - sel_v[0]);
-    else x = 1.0f / (1.0f + expf(-sel_v[r]));
+    if (gate_kind == MOE_GATE_SOFTMAX) x = expf(v - v0);
+    else x = 1.0f / (1.0f + expf(-v));
     w[r] = x;
     sum += x;
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     if (r >= k) break;
-    if (r % G == gi) {   // G may be smaller than k: lane gi writes selections gi, gi + G, ...
+    if ((r & (G - 1)) == gi) {   // G may be smaller than k: lane gi writes selections gi, gi + G, ...
       ids_out[g * k + r] = sel_id[r];
       gates_out[g * k + r] = w[r] / sum;
     }
@@ -115,10 +138,16 @@ __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ chunk
   for (int p = threadIdx.x; p < El * R; p += blockDim.x) {
     const int e = p / R, s = p % R;
     int acc = 0;
-    for (int c = 0; c < chunks_per_rank; ++c) {
-      const int ch = s * chunks_per_rank + c;
-      chunk_base[ch * El + e] = acc;
-      acc += chunk_counts[ch * El + e];
+    for (int c0 = 0; c0 < chunks_per_rank; c0 += 8) {   // 8 loads in flight, then the 8 stores
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = c0 + u < chunks_per_rank ? chunk_counts[(s * chunks_per_rank + c0 + u) * El + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < chunks_per_rank) chunk_base[(s * chunks_per_rank + c0 + u) * El + e] = acc;
+        acc += v[u];
+      }
     }
     counts[e * R + s] = acc;
   }
@@ -127,22 +156,27 @@ __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ chunk
 hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, float* gates,
                         const moe_plan_t& p, hipStream_t st) {
   (void)p;
+  // group width: the fewest lanes with at most 32 logits each (E <= 512: G <= 16)
   int G = 1;
-  while (G * 8 < g.E) G <<= 1;   // E <= 512: G <= 64
-  const int nq = (g.E + G - 1) / G;
+  while (G * 32 < g.E) G <<= 1;
+  int NQ = 8;
+  while (NQ * G < g.E) NQ <<= 1;
   const int n_tok = g.R * g.T;
   const int per_block = kRouteThreads / G;
   dim3 grid((n_tok + per_block - 1) / per_block), block(kRouteThreads);
-#define MOE_ROUTE_CASE(N)                                                                     \
-  if (nq <= N) {                                                                              \
-    hipLaunchKernelGGL(k_route<N>, grid, block, 0, st, logits, ids, gates, n_tok, g.E, g.k, G, \
-                       g.gate_kind);                                                          \
-    return hipGetLastError();                                                                 \
+#define MOE_ROUTE_CASE(GG, QQ)                                                                 \
+  if (G == GG && NQ == QQ) {                                                                   \
+    hipLaunchKernelGGL((k_route<GG, QQ>), grid, block, 0, st, logits, ids, gates, n_tok, g.E, g.k, \
+                       g.gate_kind);                                                           \
+    return hipGetLastError();                                                                  \
   }
-  MOE_ROUTE_CASE(1)
-  MOE_ROUTE_CASE(2)
-  MOE_ROUTE_CASE(4)
-  MOE_ROUTE_CASE(8)
+  MOE_ROUTE_CASE(1, 8)
+  MOE_ROUTE_CASE(1, 16)
+  MOE_ROUTE_CASE(1, 32)
+  MOE_ROUTE_CASE(2, 32)
+  MOE_ROUTE_CASE(4, 32)
+  MOE_ROUTE_CASE(8, 32)
+  MOE_ROUTE_CASE(16, 32)
 #undef MOE_ROUTE_CASE
   return hipErrorInvalidValue;
 }
