@@ -35,7 +35,8 @@ PEAK_HBM_GBS = 8000.0
 # band height per workload: the fastest measured overlapped layer step
 DEFAULT_TB = {1: 64, 2: 64, 3: 256, 4: 32, 5: 64}
 # sources whose change invalidates stored hardware-counter traffic figures
-GEMM_SOURCES = ("combine_overlap_amd/csrc/gemm.hip", "combine_overlap_amd/csrc/common.hpp")
+GEMM_SOURCES = ("combine_overlap_amd/csrc/gemm.hip", "combine_overlap_amd/csrc/common.hpp",
+                "combine_overlap_amd/csrc/consumer.hpp")
 
 
 def log(*a):
@@ -244,6 +245,8 @@ def main():
                    True: 2 * (M * w.H + n_w * w.F * w.H + m_pad * w.F)}
     log(f"[bench] valid rows {M}, remote rows {remote}, padded rows {m_pad}, bands {plan['n_bands']}, "
         f"segments {plan['n_seg']}, c={c_used}, mgb={mgb_used}")
+    log(f"[bench] first-projection algorithmic bytes: materialized {gemm1_bytes[False]}, "
+        f"fused {gemm1_bytes[True]}")
 
     def timed(mode, k):
         torch.cuda.synchronize()
