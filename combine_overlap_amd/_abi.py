@@ -93,7 +93,7 @@ def lib() -> C.CDLL:
     L.moe_plan_partition.argtypes = [pshape, pi32, C.POINTER(MoeCalib), pi32, pi32,
                                      C.POINTER(C.c_double)]
     L.moe_expert_forward_overlap.argtypes = [vp, pshape, vp, vp, vp, vp, vp, vp, vp,
-                                             C.POINTER(vp), vp, u32, i32, i32, vp, vp]
+                                             C.POINTER(vp), vp, u32, i32, i32, vp]
     L.moe_expert_forward_gathered.argtypes = L.moe_expert_forward_overlap.argtypes
     L.moe_combine.argtypes = [pshape, C.POINTER(vp), vp, vp, vp, vp, vp]
     L.moe_read_status.argtypes = [pshape, vp, pi32, vp]

@@ -8,8 +8,6 @@
 struct moe_ctx {
   int device;
   int n_cu;
-  hipEvent_t ev_producer;   // first projection done -> consumer may start
-  hipEvent_t ev_consumer;   // consumer done -> joined back into the producer stream
   int timing;               // 1: record tev[] in the forward
   int timed;                // a timed call has been enqueued
   int timed_mode;
@@ -192,13 +190,7 @@ int moe_ctx_create(moe_ctx_t** out) {
   c->trace = nullptr;
   c->trace_flags = 0;
   if (hipGetDevice(&c->device) != hipSuccess ||
-      hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess ||
-      hipEventCreateWithFlags(&c->ev_producer, hipEventDisableTiming) != hipSuccess) {
-    delete c;
-    return MOE_ERR_HIP;
-  }
-  if (hipEventCreateWithFlags(&c->ev_consumer, hipEventDisableTiming) != hipSuccess) {
-    (void)hipEventDestroy(c->ev_producer);
+      hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess) {
     delete c;
     return MOE_ERR_HIP;
   }
@@ -266,11 +258,9 @@ int moe_ctx_set_trace(moe_ctx_t* ctx, const moe_shape_t* shape, uint64_t* trace,
 
 int moe_ctx_destroy(moe_ctx_t* ctx) {
   if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
-  if (ctx->timing) (void)moe_ctx_set_timing(ctx, 0);
-  const hipError_t a = hipEventDestroy(ctx->ev_producer);
-  const hipError_t b = hipEventDestroy(ctx->ev_consumer);
+  const int rc = ctx->timing ? moe_ctx_set_timing(ctx, 0) : MOE_OK;
   delete ctx;
-  return (a == hipSuccess && b == hipSuccess) ? MOE_OK : MOE_ERR_HIP;
+  return rc;
 }
 
 int moe_ctx_num_cus(const moe_ctx_t* ctx) { return ctx ? ctx->n_cu : MOE_ERR_INVALID_ARG; }
@@ -318,8 +308,7 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
 static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16_t* a, bool gathered,
                           const uint16_t* w1, const uint16_t* w3, const uint16_t* w2, void* ws,
                           uint16_t* h, uint16_t* y_perm, uint16_t* const* combine_buf, uint32_t* flags,
-                          uint32_t epoch, int32_t n_consumer_cu, int32_t mode, void* producer_stream,
-                          void* consumer_stream) {
+                          uint32_t epoch, int32_t n_consumer_cu, int32_t mode, void* stream) {
   Geometry g;
   int rc = make_geometry(shape, &g);
   if (rc != MOE_OK) return rc;
@@ -346,8 +335,7 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   }
   moe_plan_t p;
   plan_from_ws(g, ws, &p);
-  hipStream_t ps = static_cast<hipStream_t>(producer_stream);
-  (void)consumer_stream;
+  hipStream_t ps = static_cast<hipStream_t>(stream);
   const int ncu = ctx->n_cu;
   const bool tm = ctx->timing != 0;
   auto rec = [&](int i, hipStream_t st) { return tm ? hip_rc(hipEventRecord(ctx->tev[i], st)) : MOE_OK; };
@@ -400,20 +388,18 @@ int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape, const u
                                const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
                                void* ws, uint16_t* h, uint16_t* y_perm,
                                uint16_t* const* combine_buf, uint32_t* flags, uint32_t epoch,
-                               int32_t n_consumer_cu, int32_t mode, void* producer_stream,
-                               void* consumer_stream) {
+                               int32_t n_consumer_cu, int32_t mode, void* stream) {
   return expert_forward(ctx, shape, x_perm, false, w1, w3, w2, ws, h, y_perm, combine_buf, flags, epoch,
-                        n_consumer_cu, mode, producer_stream, consumer_stream);
+                        n_consumer_cu, mode, stream);
 }
 
 int moe_expert_forward_gathered(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16_t* x,
                                 const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
                                 void* ws, uint16_t* h, uint16_t* y_perm,
                                 uint16_t* const* combine_buf, uint32_t* flags, uint32_t epoch,
-                                int32_t n_consumer_cu, int32_t mode, void* producer_stream,
-                                void* consumer_stream) {
+                                int32_t n_consumer_cu, int32_t mode, void* stream) {
   return expert_forward(ctx, shape, x, true, w1, w3, w2, ws, h, y_perm, combine_buf, flags, epoch,
-                        n_consumer_cu, mode, producer_stream, consumer_stream);
+                        n_consumer_cu, mode, stream);
 }
 
 int moe_combine(const moe_shape_t* shape, uint16_t* const* combine_buf, const uint16_t* y_perm,

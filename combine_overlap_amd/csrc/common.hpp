@@ -126,9 +126,6 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
                         int grid, int split_grid, const BufPtrs* copy_bufs, int n_cons,
                         const BufPtrs* cons_bufs, hipStream_t st);
-hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
-                           const uint32_t* flags, uint32_t epoch, uint64_t* trace, int n_wg,
-                           hipStream_t st);
 hipError_t launch_bulk_copy(const Geometry& g, const uint16_t* y, BufPtrs bufs,
                             const moe_plan_t& p, int grid, hipStream_t st);
 hipError_t launch_combine(const Geometry& g, BufPtrs bufs, const uint16_t* y, const float* gates,

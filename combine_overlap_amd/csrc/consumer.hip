@@ -1,30 +1,14 @@
-// Consumer of the tile-signalling overlap paper (sec. 3.3.2-3.3.3) as its
-// own kernel on a small set of CUs: it walks the transfer segments in
-// schedule order, waits until every tile of a segment's row bands carries the
-// current epoch flag, and moves the segment's valid rows into the combine
-// buffer of the owner rank (the copy loop is consume(), shared with the
-// consumer role of the overlapped output projection). On one GPU the owner's
-// receive buffer is a buffer in local HBM.
+// The transfer's host-side setup and the baseline's bulk copy.
 //
-// Each consumer workgroup (1024 threads) also reserves enough LDS that no
-// producer workgroup can share its CU, which keeps the two partitions
-// disjoint (sec. 2.4: persistent kernels with fixed workgroup counts).
+// The consumer of the tile-signalling overlap paper (sec. 3.3.2-3.3.3) is the
+// device function consume() (consumer.hpp), run by the first c workgroups of
+// the overlapped output projection; consumer_args() packs its arguments.
 //
 // The bulk copy (the non-overlapped baseline's second all-to-all, sec. 4.1.3)
 // copies all segments after the producer has finished, using every CU.
 #include "consumer.hpp"
 
 namespace moe {
-
-constexpr int kConsumerThreads = 1024;
-constexpr int kConsumerLdsBytes = 80 * 1024;
-static_assert(kSegLdsBytes <= kConsumerLdsBytes, "segment tables fit the reservation");
-
-// 64 KiB copy units per consumer batch (loads in flight per workgroup)
-#ifndef MOE_CONSUMER_BATCH
-#define MOE_CONSUMER_BATCH 4
-#endif
-constexpr int kBatchUnits = MOE_CONSUMER_BATCH;
 
 #ifndef MOE_COPY_UNROLL
 #define MOE_COPY_UNROLL 8
@@ -44,13 +28,6 @@ __device__ __forceinline__ void copy_units(const u32x4* __restrict__ src, u32x4*
     for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], dst + i + u * (size_t)nthr);
   }
   for (; i < hi; i += nthr) __builtin_nontemporal_store(src[i], dst + i);
-}
-
-__global__ __launch_bounds__(kConsumerThreads) void k_consumer(const ConsumerArgs c) {
-  __shared__ int s_abort;
-  __shared__ __attribute__((aligned(16))) int s_tab[kConsumerLdsBytes / 4];
-  consume<kConsumerThreads, kBatchUnits, 16>(c, blockIdx.x, gridDim.x, s_tab, &s_abort);
-  if (threadIdx.x == 0 && s_tab[kConsumerLdsBytes / 4 - 1] == 0x7fffffff) s_abort = 2;   // keeps the reservation
 }
 
 // baseline: all remote segments after the producer, on all CUs. The segments
@@ -97,14 +74,6 @@ ConsumerArgs consumer_args(const Geometry& g, const uint16_t* y, BufPtrs bufs, c
   c.tiles2 = g.tiles2;
   c.H = g.H;
   return c;
-}
-
-hipError_t launch_consumer(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
-                           const uint32_t* flags, uint32_t epoch, uint64_t* trace, int n_wg,
-                           hipStream_t st) {
-  hipLaunchKernelGGL(k_consumer, dim3(n_wg), dim3(kConsumerThreads), 0, st,
-                     consumer_args(g, y, bufs, p, flags, epoch, trace));
-  return hipGetLastError();
 }
 
 hipError_t launch_bulk_copy(const Geometry& g, const uint16_t* y, BufPtrs bufs,

@@ -47,7 +47,7 @@ def moe_plan_view(shape: MoeShape, ws) -> dict:
 
 
 class Context:
-    """Owns a moe_ctx_t (two HIP events and the device's CU count)."""
+    """Owns a moe_ctx_t (the device's CU count, optional timing events)."""
 
     def __init__(self):
         h = C.c_void_p()
@@ -111,23 +111,19 @@ def _buf_array(shape, bufs: Sequence):
 
 
 def moe_expert_forward_overlap(ctx: Context, shape, x_perm, w1, w3, w2, ws, h, y_perm, combine_bufs,
-                               flags, epoch: int, n_consumer_cu: int, mode: int,
-                               producer_stream=None, consumer_stream=None):
-    cs = C.c_void_p(consumer_stream.cuda_stream) if consumer_stream is not None else None
+                               flags, epoch: int, n_consumer_cu: int, mode: int, stream=None):
     check("moe_expert_forward_overlap", lib().moe_expert_forward_overlap(
         ctx.handle, C.byref(shape), _ptr(x_perm), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws), _ptr(h),
         _ptr(y_perm), _buf_array(shape, combine_bufs), _ptr(flags), C.c_uint32(epoch),
-        int(n_consumer_cu), int(mode), _stream(producer_stream), cs))
+        int(n_consumer_cu), int(mode), _stream(stream)))
 
 
 def moe_expert_forward_gathered(ctx: Context, shape, x, w1, w3, w2, ws, h, y_perm, combine_bufs,
-                                flags, epoch: int, n_consumer_cu: int, mode: int,
-                                producer_stream=None, consumer_stream=None):
-    cs = C.c_void_p(consumer_stream.cuda_stream) if consumer_stream is not None else None
+                                flags, epoch: int, n_consumer_cu: int, mode: int, stream=None):
     check("moe_expert_forward_gathered", lib().moe_expert_forward_gathered(
         ctx.handle, C.byref(shape), _ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws), _ptr(h),
         _ptr(y_perm), _buf_array(shape, combine_bufs), _ptr(flags), C.c_uint32(epoch),
-        int(n_consumer_cu), int(mode), _stream(producer_stream), cs))
+        int(n_consumer_cu), int(mode), _stream(stream)))
 
 
 def moe_combine(shape, combine_bufs, y_perm, gates, ws, y_share, stream=None):

@@ -58,7 +58,6 @@ class MoEShare:
         self.r_self = r_self
         self.gated = bool(gated)
         self.ctx = ops.Context()
-        self.consumer_stream = torch.cuda.Stream(device=self.device)
         self.epoch = 0
         self.buf: Optional[ShareBuffers] = None
         self.counts_host = torch.empty((self.El, R), dtype=torch.int32, pin_memory=True)
@@ -130,8 +129,7 @@ class MoEShare:
         self.epoch = (self.epoch % 0xFFFFFFF0) + 1
         fwd = ops.moe_expert_forward_gathered if self.fused_gather else ops.moe_expert_forward_overlap
         fwd(self.ctx, self.shape, b.x if self.fused_gather else b.x_perm, b.w1, b.w3, b.w2, b.ws, b.h,
-            b.y_perm, b.combine, b.flags, self.epoch, n_consumer_cu, mode, stream,
-            self.consumer_stream)
+            b.y_perm, b.combine, b.flags, self.epoch, n_consumer_cu, mode, stream)
 
     def combine(self, stream=None):
         b = self.buf

@@ -179,8 +179,8 @@ int moe_query_sizes(const moe_shape_t* shape, moe_sizes_t* out);
 /* Fills device views into a workspace of ws_bytes at ws. Host only. */
 int moe_plan_view(const moe_shape_t* shape, void* ws, moe_plan_t* out);
 
-/* Creates a context for the current HIP device: two events used to order the
- * producer and consumer streams, and the device's CU count. Returns MOE_OK and
+/* Creates a context for the current HIP device: its CU count (the grids of
+ * the expert forward) and, once enabled, timing events. Returns MOE_OK and
  * sets *out, or MOE_ERR_HIP. Destroy with moe_ctx_destroy. */
 int moe_ctx_create(moe_ctx_t** out);
 int moe_ctx_destroy(moe_ctx_t* ctx);
@@ -285,7 +285,8 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *            of the output projection on every CU whose first c workgroups
  *            (one per CU, c/8 per XCD) are the consumer, copying every segment
  *            once all its tiles are flagged, while the others run the tiles as
- *            persistent producers raising a flag per tile.
+ *            persistent producers raising a flag per tile (one stream: the
+ *            CU split comes from the roles of one grid, not from two kernels).
  *            MOE_MODE_SEQUENTIAL (baseline, [TLS] sec. 4.1.3): both projections
  *            on all CUs, then one bulk copy of all remote rows on all CUs.
  *            MOE_MODE_ROLE_SWITCH: both projections on all CUs, the output
@@ -295,18 +296,17 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *            and once the tiles run out the workgroups copy the rest (each
  *            wait bounded like the consumer's). No CU is reserved; c is
  *            ignored and the K-split is sized for all CUs (the same bits as
- *            SEQUENTIAL with c = 0). consumer_stream is not used. The
- *            per-layer worker split of [Weave] taken to its temporal end.
- *   producer_stream  all work is ordered after prior work on this stream and
- *            completes before later work on it
- *   consumer_stream  unused (every mode runs on producer_stream); may be NULL
+ *            SEQUENTIAL with c = 0). The per-layer worker split of [Weave]
+ *            taken to its temporal end.
+ *   stream   every mode runs on this one stream: its work is ordered after
+ *            prior work on it and completes before later work on it
  * Calls that overlap in time on the same flags/workspace race. */
 int moe_expert_forward_overlap(moe_ctx_t* ctx, const moe_shape_t* shape,
                                const uint16_t* x_perm, const uint16_t* w1,
                                const uint16_t* w3, const uint16_t* w2, void* ws,
                                uint16_t* h, uint16_t* y_perm, uint16_t* const* combine_buf,
                                uint32_t* flags, uint32_t epoch, int32_t n_consumer_cu,
-                               int32_t mode, void* producer_stream, void* consumer_stream);
+                               int32_t mode, void* stream);
 
 /* moe_expert_forward_overlap with the gather fused into the first
  * projection (the dispatch side of [TLS] sec. 2.1 steps 2-3): instead of
@@ -323,7 +323,7 @@ int moe_expert_forward_gathered(moe_ctx_t* ctx, const moe_shape_t* shape,
                                 const uint16_t* w3, const uint16_t* w2, void* ws,
                                 uint16_t* h, uint16_t* y_perm, uint16_t* const* combine_buf,
                                 uint32_t* flags, uint32_t epoch, int32_t n_consumer_cu,
-                                int32_t mode, void* producer_stream, void* consumer_stream);
+                                int32_t mode, void* stream);
 
 /* Step 5, weighted reduction ([TLS] sec. 2.1 step 5): for every token (s, t),
  * y_share[s, t] = sum over slots j ascending whose expert is local of

@@ -96,9 +96,9 @@ def test_entry_points_reject_bad_args_before_hip():
     # forward: no context, wrong gated/w3 pairing, bad mode
     for f in (L.moe_expert_forward_overlap, L.moe_expert_forward_gathered):
         assert f(None, C.byref(sh), fake, fake, None, fake, fake, fake, fake, bufs, fake, 1, 4, 0,
-                 None, fake) == _abi.MOE_ERR_INVALID_ARG
+                 None) == _abi.MOE_ERR_INVALID_ARG
         assert f(None, C.byref(bad), fake, fake, None, fake, fake, fake, fake, bufs, fake, 1, 4, 0,
-                 None, fake) == _abi.MOE_ERR_INVALID_ARG
+                 None) == _abi.MOE_ERR_INVALID_ARG
     st = C.c_int32()
     assert L.moe_read_status(C.byref(sh), mis, C.byref(st), None) == _abi.MOE_ERR_WORKSPACE
     assert L.moe_plan_view(C.byref(sh), mis, C.byref(_abi.MoePlan())) == _abi.MOE_ERR_WORKSPACE
