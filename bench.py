@@ -60,6 +60,12 @@ def parse():
                     help="A rows of the first projection: the materialized x_perm, the gather "
                          "fused into its tile loads, or both (timed side by side)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--table2-sweep", action="store_true",
+                    help="the shape sweep of the tile-signalling paper's Table 2 on this GPU (tokens per "
+                         "rank 8192/16384, K = 2048, N = 4096/8192, experts per rank 4..64, three router "
+                         "skews): per shape the sequential baseline, the CU-partition overlap at the "
+                         "model's c and at c = 8..48, the other segment size, and role switching; adds a "
+                         "'table2_sweep' object to the JSON line")
     ap.add_argument("--layer-sweep", action="store_true",
                     help="layered workload: per layer, the CU-partition overlap at the partition "
                          "model's consumer count and at every candidate count, the role-switching "
@@ -164,7 +170,7 @@ def layer_sweep(sh, w, make_logits, torch, ops, modes, reps=5, cands=(8, 16, 24,
         t = {c: phase(MOE_MODE_OVERLAP, c) for c in cands}
         if c_model not in t:
             t[c_model] = phase(MOE_MODE_OVERLAP, c_model)
-        row = {"layer": layer, "valid_rows": int(counts.sum()),
+        row = {"layer": layer, "valid_rows": int(counts.sum()), "counts": counts.tolist(),
                "remote_rows": int(counts.sum() - counts[:, sh.r_self].sum()),
                "c_model": int(c_model), "predicted_ms": round(pred * 1e3, 4),
                "partition_ms": {str(c): round(v, 4) for c, v in sorted(t.items())},
@@ -184,6 +190,114 @@ def layer_sweep(sh, w, make_logits, torch, ops, modes, reps=5, cands=(8, 16, 24,
                          "per_layer_best_c": tot(lambda r: min(r["partition_ms"][str(c)] for c in cands)),
                          "role_switch": tot(lambda r: r["role_switch_ms"]),
                          "sequential": tot(lambda r: r["sequential_ms"])}}
+
+
+# Table 2 of the tile-signalling paper: shape grid of its overlap-vs-baseline
+# study. Its expert GEMM (K = 2048 -> N) is the output projection that
+# raises the flags, so a shape is a non-gated FFN with F = K and H = N.
+# Router modes (named, not defined on the pages): balanced = unbiased logits,
+# moderate / stress = logits biased by ln Zipf(s) over the expert id with
+# s = 0.6 / 1.2 (the hottest experts local to the timed rank).
+TABLE2_SKEWS = (("balanced", "normal", 0.0), ("moderate_skew", "zipf", 0.6), ("stress_skew", "zipf", 1.2))
+
+
+def table2_sweep(args, torch, reps=5):
+    from synth import Workload, make_logits
+    from combine_overlap_amd import (MOE_CONSUMER_AUTO, MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH,
+                                     MOE_MODE_SEQUENTIAL)
+    from combine_overlap_amd.share import MoEShare
+    dev = torch.device("cuda:0")
+    R, K, topk, tb = 4, 2048, 2, 64
+    Ns = (8192, 4096)
+    rows = []
+    for N in Ns:
+        for E_l in (4, 8, 16, 32, 64):
+            # activations and weights from a seeded device generator (timing only:
+            # no oracle reads them); std 0.02 as for the other small-std workloads
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(2000 + N + E_l)
+            w1 = (torch.randn((E_l, K, N), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            w2 = (torch.randn((E_l, N, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            for tpr in (8192, 16384):
+                x = torch.randn((R, tpr, N), generator=gen, device=dev).to(torch.bfloat16)
+                for skew, routing, zs in TABLE2_SKEWS:
+                    w = Workload(f"table2_{skew}_tpr{tpr}_n{N}_e{E_l}", R, tpr, N, K, R * E_l, topk, False,
+                                 "softmax", routing, zipf_s=zs or 1.2)
+                    sh = MoEShare(R, tpr, N, K, R * E_l, topk, False, "softmax", r_self=0, tb_m=tb,
+                                  device=dev, fused_gather=True)
+                    sh.allocate(torch.from_numpy(make_logits(w, 0)).to(dev), x, w1, None, w2)
+                    for _ in range(2):
+                        sh.layer(MOE_MODE_OVERLAP)
+                    torch.cuda.synchronize()
+                    if sh.status() != 0:
+                        raise RuntimeError(f"{w.name}: device status {sh.status()}")
+                    c_model, pred = sh.auto_consumer_cu()
+                    counts = sh.buf.counts.cpu().numpy()
+                    M = int(counts.sum())
+                    remote = int(M - counts[:, 0].sum())
+
+                    # layer steps: blocks of `reps` back-to-back steps, the forms taken in
+                    # turn over 3 rounds, median block per form
+                    forms = (("sequential", MOE_MODE_SEQUENTIAL), ("cu_partition", MOE_MODE_OVERLAP),
+                             ("role_switch", MOE_MODE_ROLE_SWITCH))
+                    blocks = {m: [] for m, _ in forms}
+                    for _ in range(3):
+                        for m, v in forms:
+                            torch.cuda.synchronize()
+                            t0 = time.perf_counter()
+                            for _ in range(reps):
+                                sh.layer(v)
+                            torch.cuda.synchronize()
+                            blocks[m].append((time.perf_counter() - t0) / reps * 1e3)
+                    layer = {m: float(np.median(b)) for m, b in blocks.items()}
+                    sh.ctx.set_timing(True)
+
+                    def phase(mode, c):   # (operator = output projection + transfer, expert phase, exposed)
+                        d = []
+                        for i in range(reps + 2):
+                            sh.expert_forward(mode, n_consumer_cu=c)
+                            if i >= 2:
+                                d.append(sh.ctx.timings())
+                        return tuple(float(np.median([t[k] for t in d]))
+                                     for k in ("producer_start_to_consumer_end", "total", "exposed"))
+                    seq = phase(MOE_MODE_SEQUENTIAL, MOE_CONSUMER_AUTO)
+                    rs = phase(MOE_MODE_ROLE_SWITCH, MOE_CONSUMER_AUTO)
+                    by_c = {c: phase(MOE_MODE_OVERLAP, c) for c in (8, 16, 24, 32, 40, 48)}
+                    mgb0 = sh.shape.mgb
+                    sh.set_routing(mgb=3 - mgb0)   # the other segment size, same c
+                    sh.permute()
+                    alt = phase(MOE_MODE_OVERLAP, c_model)
+                    sh.set_routing(mgb=mgb0)
+                    sh.permute()
+                    sh.ctx.set_timing(False)
+                    ovl = by_c[c_model]
+                    c_best = min(by_c, key=lambda c: by_c[c][0])
+                    row = {"N": N, "E": E_l, "tpr": tpr, "router": skew, "valid_rows": M, "remote_rows": remote,
+                           "c_model": c_model, "c_best": c_best, "mgb": mgb0, "counts": counts.tolist(),
+                           "operator_ms": {"sequential": round(seq[0], 4), "cu_partition": round(ovl[0], 4),
+                                           "cu_partition_best_c": round(by_c[c_best][0], 4),
+                                           "cu_partition_other_mgb": round(alt[0], 4),
+                                           "role_switch": round(rs[0], 4)},
+                           "expert_phase_ms": {"sequential": round(seq[1], 4), "cu_partition": round(ovl[1], 4),
+                                               "role_switch": round(rs[1], 4)},
+                           "operator_ms_by_c": {str(c): round(v[0], 4) for c, v in by_c.items()},
+                           "layer_ms": {k: round(v, 4) for k, v in layer.items()},
+                           "operator_speedup": round(seq[0] / ovl[0], 4),
+                           "layer_speedup": round(layer["sequential"] / layer["cu_partition"], 4),
+                           "overlap_ratio": round(1.0 - min(1.0, ovl[2] / seq[2]), 4) if seq[2] > 0 else None}
+                    rows.append(row)
+                    log(f"[table2] N={N} E={E_l} tpr={tpr} {skew}: rows {M} (remote {remote}), c model "
+                        f"{c_model} / best {c_best}; operator seq {seq[0]:.3f} ovl {ovl[0]:.3f} "
+                        f"rs {rs[0]:.3f} ms; layer seq {layer['sequential']:.3f} ovl "
+                        f"{layer['cu_partition']:.3f} rs {layer['role_switch']:.3f} ms; overlap ratio "
+                        f"{row['overlap_ratio']}")
+                    del sh
+                    torch.cuda.empty_cache()
+            del w1, w2
+            torch.cuda.empty_cache()
+    return {"reading": "expert GEMM = output projection of a non-gated FFN, F = K = 2048, H = N; R = 4, "
+                       "top-2 softmax; gather fused; router modes as TABLE2_SKEWS",
+            "configs": rows}
 
 
 def main():
@@ -373,6 +487,11 @@ def main():
         out["layer_sweep"] = layer_sweep(sh, w, make_logits, torch, ops,
                                          (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
         log("[bench] layer sweep totals " + json.dumps(out["layer_sweep"]["total_ms"]))
+    if args.table2_sweep:
+        log("[bench] Table-2 sweep")
+        del sh
+        torch.cuda.empty_cache()
+        out["table2_sweep"] = table2_sweep(args, torch)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, inp, tb, args.cpu_seconds)

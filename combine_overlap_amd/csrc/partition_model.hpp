@@ -34,16 +34,18 @@ namespace moe {
 constexpr int kModelTileRows = 256;   // GEMM row-tile height
 constexpr int kModelTileCols = 256;   // output-projection column tile
 
-// calibration measured on MI355X over the five synthetic workloads:
-// 3.6-4.4 TFLOP/s per producer CU on the output projection; the consumer
-// moves 121, 208, 309 and 407 GB/s with 8, 16, 32 and 48 CUs beside it
+// calibration measured on MI355X: 3.6-4.4 TFLOP/s per producer CU on the
+// output projection; b, B and the copy's tail fitted to the measured best c
+// of 76 shapes (the Table-2 grid of the tile-signalling paper at N = 4096 and
+// 8192, and the 16 layers of the dynamic-split workload): BW(c) = 133, 229,
+// 356, 436 GB/s at c = 8, 16, 32, 48, plus 30 us for the last batch
 inline moe_calib_t default_calib(int n_cu) {
   moe_calib_t k;
   k.gemm_flops_per_cu = 3.5e12;
   k.gemm_m_half = 0.0;
-  k.copy_bw_per_cu = 17.8e9;
+  k.copy_bw_per_cu = 20e9;
   k.copy_bw_max = 800e9;
-  k.seg_latency_s = 10e-6;
+  k.seg_latency_s = 30e-6;
   k.n_cu = n_cu;
   k.c_max = n_cu - 1 < 48 ? n_cu - 1 : 48;
   k.c_min = k.c_max < 8 ? (k.c_max > 1 ? k.c_max : 1) : 8;
