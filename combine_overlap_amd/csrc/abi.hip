@@ -341,7 +341,8 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   auto rec = [&](int i, hipStream_t st) { return tm ? hip_rc(hipEventRecord(ctx->tev[i], st)) : MOE_OK; };
   if ((rc = rec(0, ps)) != MOE_OK) return rc;
   if ((rc = hip_rc(launch_gemm1(g, a, gathered ? p.row_src : nullptr, gathered ? zero_row_of(g, ws) : nullptr,
-                                w1, w3, h, p, ncu, ps))) != MOE_OK)
+                                w1, w3, h, p, mode == MOE_MODE_SEQUENTIAL ? nullptr : flags, ncu, ps))) !=
+      MOE_OK)
     return rc;
   if ((rc = rec(1, ps)) != MOE_OK) return rc;
   if (mode == MOE_MODE_SEQUENTIAL) {

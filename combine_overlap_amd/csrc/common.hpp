@@ -110,10 +110,11 @@ hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_
 hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
                          uint16_t* x_perm, const moe_plan_t& p, hipStream_t st);
 // a_rows null: A = x_perm (packed rows); else A = x and packed row r reads x row
-// a_rows[r] (a_zero for padding), the gather fused into the tile loads
+// a_rows[r] (a_zero for padding), the gather fused into the tile loads.
+// flags (may be null): the output projection's ready flags, cleared here
 hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t* a_rows,
                         const uint16_t* a_zero, const uint16_t* w1, const uint16_t* w3, uint16_t* h,
-                        const moe_plan_t& p, int grid, hipStream_t st);
+                        const moe_plan_t& p, uint32_t* flags, int grid, hipStream_t st);
 // split_grid: the producer grid the K-split tail is sized for (the overlapped
 // run's n_cu - c in both modes, so that both compute identical bits)
 // copy_bufs: non-null gives the launch the consumer's duty as well (role

@@ -119,7 +119,8 @@ struct GemmArgs {
   int32_t* my_ctr;             // this launch's 8 per-XCD queue counters
   int32_t* other_ctr;          // the other launch's counters (zeroed here)
   float* partial;              // fp32 partial tiles of split tail tiles, [8 * kTailSlots][BM * BN]
-  uint32_t* flags;             // output projection in overlap mode, else null
+  uint32_t* flags;             // output projection: the ready flags it raises (null: none);
+                               // first projection: the flags it clears for the output projection
   // role switching (output projection): the consumer's copy duty between tiles
   int copy_duty;
   int32_t* my_copy;            // [0] next remote segment to claim
@@ -131,6 +132,7 @@ struct GemmArgs {
   const int32_t* seg_src_row;
   const int32_t* seg_dst_row;
   const int32_t* seg_dest;
+  int flags_n;                 // first projection: flags per row tile of the output projection
   uint64_t* trace;             // optional timeline: [0] start, [8 + t] tile t done
   // CU-partition overlap inside one launch: workgroups [0, n_cons) run the
   // consumer (one per CU, n_cons / 8 per XCD), the others the tiles;
@@ -393,8 +395,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   // the other launch's queue and tail counters (this launch's were cleared by it)
   if (blockIdx.x == 0 && tid < kXcds * kCtrStride) a.other_ctr[tid] = 0;
   if (blockIdx.x == 0 && tid < kCtrStride) a.other_copy[tid] = 0;
-  if (EPI != EPI_PLAIN && blockIdx.x == 0 && tid < 4)   // the output projection's stamps
-    const_cast<int32_t*>(a.meta)[META_T_PROD + tid] = 0;
+  if constexpr (EPI != EPI_PLAIN) {
+    // the output projection's clock stamps, and its ready flags: every call
+    // starts from zero flags, so a replayed call (same epoch) never sees a
+    // previous call's flags
+    if (blockIdx.x == 0 && tid < 4) const_cast<int32_t*>(a.meta)[META_T_PROD + tid] = 0;
+    if (a.flags != nullptr) {
+      const int nf = a.meta[META_NTILES] * a.flags_n;
+      for (int i = blockIdx.x * C::NT + tid; i < nf; i += gridDim.x * C::NT) a.flags[i] = 0u;
+    }
+  }
   const int px = max(1, a.px > 0 ? a.px : ((int)gridDim.x - a.meta[META_CAUTO]) / kXcds);
   if (a.trace != nullptr && blockIdx.x == 0 && tid == 0) a.trace[0] = wall_clock64();
   if constexpr (CONS) {
@@ -784,7 +794,7 @@ static hipError_t dispatch(GemmArgs a, int bm, int bn, int grid, hipStream_t st)
 
 hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t* a_rows,
                         const uint16_t* a_zero, const uint16_t* w1, const uint16_t* w3, uint16_t* h,
-                        const moe_plan_t& p, int grid, hipStream_t st) {
+                        const moe_plan_t& p, uint32_t* flags, int grid, hipStream_t st) {
   GemmArgs a{};
   a.A = a_src;
   a.a_rows = a_rows;
@@ -803,7 +813,8 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t*
   a.my_copy = p.tile_ctr + kCopyCtrOffset;
   a.other_copy = p.tile_ctr + kCopyCtrOffset + kCtrStride;
   a.partial = p.partial;
-  a.flags = nullptr;
+  a.flags = flags;
+  a.flags_n = g.tiles2;
   a.trace = nullptr;
   a.epoch = 0;
   a.K = g.H;

@@ -271,9 +271,12 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *   combine_buf host array of R device pointers; combine_buf[s] for s != r_self
  *            is [recv_rows_max, H] bf16 (out): rows returned to rank s;
  *            combine_buf[r_self] is ignored (may be NULL)
- *   flags    [max_flags] uint32, zero-initialised once by the caller and then
- *            reused: tile t is ready when flags[t] == epoch
- *   epoch    nonzero, different from the previous call's epoch on these flags
+ *   flags    [max_flags] uint32 (OVERLAP, ROLE_SWITCH; may be NULL in
+ *            SEQUENTIAL): the first projection clears them, the output
+ *            projection sets flags[t] = epoch once tile t is stored
+ *   epoch    nonzero. Every call starts from cleared flags, so repeated
+ *            calls may reuse one epoch (a captured call replayed from a HIP
+ *            graph does)
  *   n_consumer_cu  c: OVERLAP 1..64, SEQUENTIAL 0..64, and < device CUs; or
  *            MOE_CONSUMER_AUTO (OVERLAP, SEQUENTIAL): the c the preceding
  *            moe_permute chose on the device, with no host round trip. The
