@@ -83,13 +83,10 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, tb: int, gathered: bool):
-    """HBM-side bytes per launch of the first-projection GEMM from the committed
-    FETCH_SIZE / WRITE_SIZE summary for this workload, band height and A-row
-    source, or None when there is none or the GEMM sources changed since it
-    was taken."""
-    path = os.path.join(ROOT, "profiles",
-                        f"pmc_gemm1{'_gathered' if gathered else ''}_{workload}_tb{tb}.md")
+def stored_figures(name: str):
+    """The "- key: value" figures of a committed counter summary under profiles/,
+    or None when there is none or the GEMM sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -100,8 +97,27 @@ def stored_traffic(workload: str, tb: int, gathered: bool):
                 kv[k.strip()] = v.strip().strip("`")
     if kv.get("gemm_source_sha256_16") != gemm_source_hash():
         return None
+    return kv
+
+
+def stored_traffic(workload: str, tb: int, gathered: bool):
+    """HBM-side bytes per launch of the first-projection GEMM from the committed
+    FETCH_SIZE / WRITE_SIZE summary for this workload, band height and A-row
+    source, or None."""
+    kv = stored_figures(f"pmc_gemm1{'_gathered' if gathered else ''}_{workload}_tb{tb}.md")
     try:
-        return float(kv["traffic_bytes_per_launch"])
+        return float(kv["traffic_bytes_per_launch"]) if kv else None
+    except (KeyError, ValueError):
+        return None
+
+
+def stored_mfma(workload: str, tb: int, gathered: bool):
+    """(MFMA-busy fraction of elapsed cycles, running clock in GHz) of the
+    first-projection GEMM from the committed counter summary, or None."""
+    kv = stored_figures(f"pmc_mfma_{workload}_tb{tb}.md")
+    g = "fused" if gathered else "materialized"
+    try:
+        return (float(kv[f"mfma_busy_gemm1_{g}"]), float(kv[f"clock_ghz_gemm1_{g}"])) if kv else None
     except (KeyError, ValueError):
         return None
 
@@ -422,6 +438,7 @@ def main():
     g1 = med(b_fused, b_mode, "gemm1")
     ach1 = flops1 / (g1 * 1e-3) / 1e12
     traffic = stored_traffic(w.name, tb, b_fused)
+    mfma = stored_mfma(w.name, tb, b_fused)
 
     layer = {
         "valid_rows": M, "remote_rows": remote, "padded_rows": m_pad,
@@ -479,7 +496,14 @@ def main():
                      "bound": "mfma", "achieved": round(ach1, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach1 / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "traffic_unit": "bytes per launch",
-                     "algorithmic_bytes": gemm1_bytes[b_fused], "launch_ms": round(g1, 4)},
+                     "algorithmic_bytes": gemm1_bytes[b_fused], "launch_ms": round(g1, 4),
+                     # hardware counters of the same kernel (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE):
+                     # the clock it runs at under load and the share of those cycles the matrix
+                     # cores are busy; frac_at_running_clock prices achieved against that clock
+                     "mfma_busy_pmc": mfma[0] if mfma else None,
+                     "clock_ghz_pmc": mfma[1] if mfma else None,
+                     "frac_at_running_clock": (round(ach1 / (PEAK_BF16_TFLOPS * mfma[1] / 2.4), 4)
+                                               if mfma else None)},
     }
     if args.layer_sweep and w.layers > 1:
         log(f"[bench] layer sweep (gather {gname[b_fused]})")
