@@ -160,6 +160,45 @@ def cpu_baseline(w, inp, tb, target_s):
                        f"{len(experts)} local experts ({flops / 1e9:.1f} GFLOP in {t_ffn:.2f} s)")}
 
 
+def hbm_phases(sh, w, torch, M, m_pad, remote, bulk_copy_ms, reps=20):
+    """The HBM-bound steps timed alone (HIP events on the stream they run on),
+    each against the 8 TB/s HBM peak with its algorithmic bytes per launch:
+    route (logits read, ids and gates written), the gather into x_perm (valid
+    rows read, padded rows written), combine (the local rows read once, the
+    share written) and the baseline's bulk copy (remote rows read and written)."""
+    s = torch.cuda.current_stream()
+    RT, H = w.R * w.T, w.H
+    b_route = RT * (4 * w.E + 8 * w.k)
+    b_gather = 2 * H * (M + m_pad) + 4 * (RT * w.k + m_pad)
+    b_combine = 2 * H * (M + RT) + 12 * RT * w.k
+    b_bulk = 4 * H * remote
+
+    def time_it(fn):
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(s)
+            fn()
+            b.record(s)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+    fused = sh.fused_gather
+    sh.fused_gather = False
+    out = {}
+    for name, fn, nbytes in (("route", lambda: sh.route(s), b_route),
+                             ("permute_materialized", lambda: sh.permute(s), b_gather),
+                             ("combine", lambda: sh.combine(s), b_combine)):
+        out[name] = {"us": time_it(fn) * 1e3, "bytes": nbytes}
+    sh.fused_gather = fused
+    sh.permute(s)
+    out["bulk_copy"] = {"us": bulk_copy_ms * 1e3, "bytes": b_bulk}
+    for d in out.values():
+        gbs = d["bytes"] / (d["us"] * 1e-6) / 1e9
+        d.update({"us": round(d["us"], 2), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    return out
+
+
 def layer_sweep(sh, w, make_logits, torch, ops, modes, reps=5, cands=(8, 16, 24, 32, 40, 48)):
     """Expert-phase times (ms, median of reps after 2 warmups) per layer and form.
 
@@ -440,6 +479,9 @@ def main():
     traffic = stored_traffic(w.name, tb, b_fused)
     mfma = stored_mfma(w.name, tb, b_fused)
 
+    hbm = hbm_phases(sh, w, torch, M, m_pad, remote, med(b_fused, MOE_MODE_SEQUENTIAL, "exposed"))
+    log("[bench] HBM-bound steps: " + ", ".join(f"{k} {v['us']:.1f} us {v['GB/s']:.0f} GB/s ({v['frac']:.2f})"
+                                                for k, v in hbm.items()))
     layer = {
         "valid_rows": M, "remote_rows": remote, "padded_rows": m_pad,
         "algorithmic_tflop": round(flops / 1e12, 4),
@@ -491,6 +533,7 @@ def main():
                    "consumer_cus": c_used, "mgb": mgb_used,
                    "parallelism": "one EP rank share on one GPU"},
         "layer": layer,
+        "hbm_kernels": hbm,
         "roofline": {"kernel": "k_gemm first projection (x W1^T, x W3^T, SiLU gate)" +
                      (", rows gathered from x" if b_fused else ""),
                      "bound": "mfma", "achieved": round(ach1, 2), "peak": PEAK_BF16_TFLOPS,
