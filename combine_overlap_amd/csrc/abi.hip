@@ -15,6 +15,7 @@ struct moe_ctx {
   uint64_t* trace;          // device timeline (see moe_ctx_set_trace) or null
   int32_t trace_flags;      // max_flags of the shape the trace was sized for
   const int32_t* timed_meta;   // workspace meta words of the last timed call (device stamps)
+  uint64_t wait_ticks;      // bound on each wait for a ready flag (100 MHz ticks)
 };
 
 namespace moe {
@@ -189,6 +190,7 @@ int moe_ctx_create(moe_ctx_t** out) {
   c->timed = 0;
   c->trace = nullptr;
   c->trace_flags = 0;
+  c->wait_ticks = moe::kDefaultWaitTicks;
   if (hipGetDevice(&c->device) != hipSuccess ||
       hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess) {
     delete c;
@@ -264,6 +266,12 @@ int moe_ctx_destroy(moe_ctx_t* ctx) {
 }
 
 int moe_ctx_num_cus(const moe_ctx_t* ctx) { return ctx ? ctx->n_cu : MOE_ERR_INVALID_ARG; }
+
+int moe_ctx_set_wait_limit(moe_ctx_t* ctx, uint64_t ticks) {
+  if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
+  ctx->wait_ticks = ticks == 0 ? moe::kDefaultWaitTicks : ticks;
+  return MOE_OK;
+}
 
 int moe_route(const moe_shape_t* shape, const float* logits, int32_t* topk_ids, float* gates,
               int32_t* counts, void* ws, void* stream) {
@@ -347,7 +355,8 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   if ((rc = rec(1, ps)) != MOE_OK) return rc;
   if (mode == MOE_MODE_SEQUENTIAL) {
     if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu,
-                                  auto_c ? 0 : ncu - n_consumer_cu, nullptr, 0, nullptr, ps))) != MOE_OK)
+                                  auto_c ? 0 : ncu - n_consumer_cu, nullptr, 0, nullptr, ctx->wait_ticks,
+                                  ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
     if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 4 * ncu, ps))) != MOE_OK) return rc;
@@ -360,7 +369,7 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   if (mode == MOE_MODE_ROLE_SWITCH) {
     // one launch on every CU does both duties; the split is sized for all CUs
     if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu, ncu, &bufs, 0, nullptr,
-                                  ps))) != MOE_OK)
+                                  ctx->wait_ticks, ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
     if ((rc = rec(3, ps)) != MOE_OK) return rc;
@@ -372,7 +381,7 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   // CU partition: one launch on every CU, workgroups [0, c) the consumer
   if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu,
                                 auto_c ? 0 : ncu - n_consumer_cu, nullptr, auto_c ? -1 : n_consumer_cu, &bufs,
-                                ps))) != MOE_OK)
+                                ctx->wait_ticks, ps))) != MOE_OK)
     return rc;
   if ((rc = rec(2, ps)) != MOE_OK) return rc;
   if ((rc = rec(3, ps)) != MOE_OK) return rc;

@@ -42,6 +42,9 @@ constexpr int kCopyCtrOffset = 2 * kXcds * kCtrStride;
 // each with a tb_m x 256 fp32 partial tile; word 1 + t of the XCD's counter
 // block counts the arrivals of tail tile t
 constexpr int kTailSlots = kCtrStride - 1;
+// bound on every wait for a ready flag, in ticks of the 100 MHz constant
+// clock, unless the context sets another (moe_ctx_set_wait_limit)
+constexpr uint64_t kDefaultWaitTicks = 200000000ull;   // 2 s
 
 struct Geometry {
   int32_t R, T, H, F, E, k, r_self, gated, gate_kind, tb_m, mgb;
@@ -122,11 +125,12 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t*
 // tiles are all flagged, and once the tiles run out it drains the rest
 // n_cons != 0: workgroups [0, n_cons) of the launch are the consumer (copying
 // into cons_bufs), the others the producer (the CU-partition overlap in one
-// launch); n_cons = -1 and split_grid = 0 take the plan's consumer count
+// launch); n_cons = -1 and split_grid = 0 take the plan's consumer count.
+// wait_ticks bounds each wait of either copying role for a ready flag.
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
                         int grid, int split_grid, const BufPtrs* copy_bufs, int n_cons,
-                        const BufPtrs* cons_bufs, hipStream_t st);
+                        const BufPtrs* cons_bufs, uint64_t wait_ticks, hipStream_t st);
 hipError_t launch_bulk_copy(const Geometry& g, const uint16_t* y, BufPtrs bufs,
                             const moe_plan_t& p, int grid, hipStream_t st);
 hipError_t launch_combine(const Geometry& g, BufPtrs bufs, const uint16_t* y, const float* gates,

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void k_bulk_copy(const uint16_t* __restrict__ 
 }
 
 ConsumerArgs consumer_args(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
-                           const uint32_t* flags, uint32_t epoch, uint64_t* trace) {
+                           const uint32_t* flags, uint32_t epoch, uint64_t* trace, uint64_t wait_ticks) {
   ConsumerArgs c{};
   c.y = y;
   c.bufs = bufs;
@@ -73,6 +73,7 @@ ConsumerArgs consumer_args(const Geometry& g, const uint16_t* y, BufPtrs bufs, c
   c.trace_seg = 8 + g.max_flags;
   c.tiles2 = g.tiles2;
   c.H = g.H;
+  c.wait_ticks = wait_ticks;
   return c;
 }
 

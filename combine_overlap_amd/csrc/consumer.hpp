@@ -12,7 +12,7 @@
 // loads, which pair with the producer's device-scope stores and completion
 // wait; no L2 invalidate is issued per segment.
 //
-// Every wait is bounded: after kWaitTicks of the 100 MHz constant clock the
+// Every wait is bounded: after wait_ticks of the 100 MHz constant clock the
 // device status word becomes MOE_ERR_TIMEOUT and the workgroup returns.
 #pragma once
 
@@ -24,7 +24,6 @@
 
 namespace moe {
 
-constexpr uint64_t kWaitTicks = 200000000ull;   // 2 s at 100 MHz
 // segment tables staged in LDS: unit0 [kSegLds + 1], then rows, src_row,
 // dst_row, dest, tile0, tile1 [kSegLds]; segments past kSegLds are read from
 // global memory
@@ -48,10 +47,11 @@ struct ConsumerArgs {
   int trace_seg;
   int tiles2;                 // column tiles per row tile (flags per row tile)
   int H;
+  uint64_t wait_ticks;        // bound on one wait for a segment's flags (100 MHz ticks)
 };
 
 ConsumerArgs consumer_args(const Geometry& g, const uint16_t* y, BufPtrs bufs, const moe_plan_t& p,
-                           const uint32_t* flags, uint32_t epoch, uint64_t* trace);
+                           const uint32_t* flags, uint32_t epoch, uint64_t* trace, uint64_t wait_ticks);
 
 template <int NT, int BATCH, int ROUND>
 __device__ void consume(const ConsumerArgs& c, int wg, int nwg, int* s_tab, int* s_abort) {
@@ -115,7 +115,7 @@ __device__ void consume(const ConsumerArgs& c, int wg, int nwg, int* s_tab, int*
             ok &= (__hip_atomic_load(f + i, MOE_DEVICE_SCOPE_PUBLISH ? __ATOMIC_RELAXED : __ATOMIC_ACQUIRE,
                                      __HIP_MEMORY_SCOPE_AGENT) == c.epoch);
           if (__ballot(!ok) == 0ull) break;
-          if (wall_clock64() - t_start > kWaitTicks) { timed_out = true; break; }
+          if (wall_clock64() - t_start > c.wait_ticks) { timed_out = true; break; }
           __builtin_amdgcn_s_sleep(2);
         }
         if (timed_out) {

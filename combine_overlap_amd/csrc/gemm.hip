@@ -140,6 +140,7 @@ struct GemmArgs {
   int n_cons;
   ConsumerArgs cons;
   uint32_t epoch;
+  uint64_t wait_ticks;         // bound on one wait of the copy duty for a segment's flags
   int K, Nw, Nout, tiles_n;
   int xb, xn;                  // XCD grid: xcd = (row tile % xb) * xn + (column tile % xn)
   int gp, gq;                  // blocks of gp row tiles x gq column tiles inside an XCD queue
@@ -264,7 +265,6 @@ __device__ __forceinline__ int xcc_id() {
   return v & (kXcds - 1);
 }
 
-constexpr uint64_t kCopyWaitTicks = 200000000ull;   // 2 s at the 100 MHz constant clock
 
 // Copies remote segment sg's valid rows (y rows published by other
 // workgroups) into its owner's combine buffer with all NT threads.
@@ -344,7 +344,7 @@ __device__ void copy_duty(const GemmArgs& a, bool wait, int tid, int* s_copy) {
           d0 = sg;
           d1 = sg + 1;
           while (!tiles_ready(t0, t1)) {
-            if (wall_clock64() - t_start > kCopyWaitTicks) {
+            if (wall_clock64() - t_start > a.wait_ticks) {
               if (lane == 0) {
                 int expected = 0;
                 __hip_atomic_compare_exchange_strong(const_cast<int32_t*>(a.meta) + META_STATUS, &expected,
@@ -829,7 +829,7 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t*
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
                         int grid, int split_grid, const BufPtrs* copy_bufs, int n_cons,
-                        const BufPtrs* cons_bufs, hipStream_t st) {
+                        const BufPtrs* cons_bufs, uint64_t wait_ticks, hipStream_t st) {
   GemmArgs a{};
   a.A = h;
   a.B0 = w2;
@@ -857,7 +857,7 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
   }
   if (n_cons != 0) {
     a.n_cons = n_cons;
-    a.cons = consumer_args(g, y, *cons_bufs, p, flags, epoch, trace);
+    a.cons = consumer_args(g, y, *cons_bufs, p, flags, epoch, trace, wait_ticks);
   }
   a.flags = flags;
   a.trace = trace;
@@ -867,6 +867,7 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
   a.Nout = g.H;
   a.tiles_n = g.tiles2;
   a.px = split_grid > 0 ? split_grid / kXcds : 0;
+  a.wait_ticks = wait_ticks;
   return dispatch<EPI_PLAIN>(a, g.tile_m, g.bn2, grid, st);
 }
 

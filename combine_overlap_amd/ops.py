@@ -55,6 +55,11 @@ class Context:
         self.handle = h
         self.num_cus = lib().moe_ctx_num_cus(h)
 
+    def set_wait_limit(self, ticks: int):
+        """Bound on each wait of a copying role for ready flags, in 100 MHz
+        ticks (0: the default of 2 s); see moe_ctx_set_wait_limit."""
+        check("moe_ctx_set_wait_limit", lib().moe_ctx_set_wait_limit(self.handle, int(ticks)))
+
     def set_timing(self, enable: bool):
         check("moe_ctx_set_timing", lib().moe_ctx_set_timing(self.handle, int(bool(enable))))
 

@@ -186,6 +186,18 @@ int moe_ctx_create(moe_ctx_t** out);
 int moe_ctx_destroy(moe_ctx_t* ctx);
 int moe_ctx_num_cus(const moe_ctx_t* ctx);
 
+/* Bound on every wait of a copying role for the ready flags of a segment's
+ * row tiles (the consumer of the CU-partition overlap, the copy duty of role
+ * switching), in ticks of the 100 MHz constant clock; 0 restores the default
+ * of 2 s. A wait that runs out sets the device status word (moe_read_status)
+ * to MOE_ERR_TIMEOUT, and the waiting workgroups stop copying and exit; the
+ * producer's tiles, and so y_perm, are unaffected, and the next moe_permute
+ * clears the status. Applies to later moe_expert_forward_* calls on ctx.
+ * A flag can only stay unset if the producer never reaches its tile (for
+ * instance a preempted or failed launch); a tiny bound forces the error path
+ * from the host. Returns MOE_ERR_INVALID_ARG for a NULL ctx. */
+int moe_ctx_set_wait_limit(moe_ctx_t* ctx, uint64_t ticks);
+
 /* Phase timing of moe_expert_forward_overlap with HIP events recorded on the
  * streams the kernels run on (off by default; enabling creates 5 events).
  * moe_ctx_timings waits for the last timed call and writes, in ms:

@@ -101,6 +101,7 @@ def test_entry_points_reject_bad_args_before_hip():
                  None) == _abi.MOE_ERR_INVALID_ARG
     st = C.c_int32()
     assert L.moe_read_status(C.byref(sh), mis, C.byref(st), None) == _abi.MOE_ERR_WORKSPACE
+    assert L.moe_ctx_set_wait_limit(None, 1) == _abi.MOE_ERR_INVALID_ARG
     assert L.moe_plan_view(C.byref(sh), mis, C.byref(_abi.MoePlan())) == _abi.MOE_ERR_WORKSPACE
 
 
