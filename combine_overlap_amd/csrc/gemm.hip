@@ -76,7 +76,12 @@ enum { EPI_PLAIN = 0, EPI_SILU = 1, EPI_GATED = 2 };
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kMaxSplit = 4;        // K chunks per split tail tile
+// K chunks per split tail tile. In the first projection the last chunk to
+// arrive reduces the whole tile, so few chunks pay; in the output projection
+// every chunk reduces and stores its own share of the tile's accumulator
+// blocks, so up to one chunk per block.
+constexpr int kMaxSplitSerial = 4;
+constexpr int kMaxSplitShared = 8;
 constexpr int kMinSplitSteps = 8;   // k-steps per chunk at least
 
 template <int BM, int BN, int BK, int NS, int WM, int WN>
@@ -173,13 +178,17 @@ __device__ __forceinline__ int queue_tile(const GemmArgs& a, int n_rt, int x, in
 
 // Work item i of XCD queue x, served by px workgroups: the first T - tail
 // items are whole tiles in queue order; the tail's tiles are split into
-// nsplit consecutive K chunks. slot = index among the split items (< kTailSlots),
+// nsplit consecutive K chunks. tail * nsplit <= px: a chunk that waits for
+// its tile's other chunks never waits for an item no workgroup is free to
+// take (the chunks of all queues together are at most the producer's
+// workgroups, and a workgroup holds one chunk at a time). slot = index among the split items (< kTailSlots),
 // slot / nsplit = the tail tile's arrival counter.
 struct Item {
   int tile, chunk, nsplit, slot;
 };
 
-__device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int x, int i, int px, int nk) {
+__device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int x, int i, int px, int nk,
+                                           int max_split) {
   Item it{-1, 0, 1, 0};
   const int bx = x / a.xn, nx = x - (x / a.xn) * a.xn;
   if (bx >= n_rt || nx >= a.tiles_n) return it;
@@ -188,7 +197,7 @@ __device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int x, i
   const int T = nb * nn;
   const int tail = T % px;
   int s = tail > 0 ? px / tail : 1;
-  s = min(s, min(kMaxSplit, nk / kMinSplitSteps));
+  s = min(s, min(max_split, nk / kMinSplitSteps));
   if (tail * s > kTailSlots) s = kTailSlots / tail;
   if (s < 2) {
     if (i < T) it.tile = queue_tile(a, n_rt, x, i);
@@ -386,6 +395,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
   __shared__ int s_item[5];   // tile, chunk, nsplit, slot, queue
   __shared__ int s_copy[2];   // copy duty: claimed segments [s_copy[0], s_copy[1])
+  // output projection: the chunks of a split tail tile share its reduction
+  constexpr bool kShared = EPI == EPI_PLAIN;
+  constexpr int kBlocks = C::FM * C::FN;   // 32x32 accumulator blocks per wave
+  constexpr int kMaxSplit = kShared ? (kMaxSplitShared < kBlocks ? kMaxSplitShared : kBlocks) : kMaxSplitSerial;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -449,7 +462,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       while (tried < kXcds) {
         const int i = __hip_atomic_fetch_add(a.my_ctr + q * kCtrStride, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-        it = queue_item(a, n_rt, q, i, px, nk);
+        it = queue_item(a, n_rt, q, i, px, nk, kMaxSplit);
         if (it.tile >= 0) break;
         q = (q + 1) & (kXcds - 1);
         ++tried;
@@ -606,9 +619,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     if (fm_act == C::FM) kloop(std::false_type{});
     else kloop(std::true_type{});
 
-    // split tail tile: publish this chunk's accumulators; the last chunk to
-    // arrive adds the others and finishes the tile
+    // split tail tile: publish this chunk's accumulators. First projection:
+    // the last chunk to arrive adds the others and finishes the tile. Output
+    // projection: once every chunk has arrived, chunk c adds the partials of
+    // accumulator blocks q in [q0, q1) (q = j * FM + i, the same share in
+    // every wave) and stores them; the last chunk to store raises the flag.
+    int q0 = 0, q1 = kBlocks;
+    int32_t* tail_ctr = nullptr;
     if (nsplit > 1) {
+      tail_ctr = a.my_ctr + iq * kCtrStride + 1 + slot / nsplit;
       // lane-native layout: ((wave * FM + i) * FN + j) * 8 + pair, then 64 lanes x 2 floats
       uint64_t* mine = reinterpret_cast<uint64_t*>(a.partial) +
                        (size_t)(iq * kTailSlots + slot) * (BM * BN / 2) +
@@ -633,41 +652,104 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 #endif
       __syncthreads();
       if (tid == 0)
-        s_item[0] = __hip_atomic_fetch_add(a.my_ctr + iq * kCtrStride + 1 + slot / nsplit, 1,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_item[0] = __hip_atomic_fetch_add(tail_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       const int arrived = s_item[0];
-      __syncthreads();   // s_item is rewritten by the next item
-      if (arrived != nsplit - 1) continue;
+      __syncthreads();   // s_item is rewritten below and by the next item
+      if constexpr (kShared) {
+        // wait (bounded) until every chunk's partial is out. The other chunks
+        // are running or about to (see queue_item), so this bound is not the
+        // copy roles' settable one.
+        if (tid == 0) {
+          int ok = 1;
+          if (arrived != nsplit - 1) {
+            const uint64_t t_start = wall_clock64();
+            while (__hip_atomic_load(tail_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nsplit) {
+              if (wall_clock64() - t_start > kDefaultWaitTicks) {
+                int expected = 0;
+                __hip_atomic_compare_exchange_strong(const_cast<int32_t*>(a.meta) + META_STATUS, &expected,
+                                                     MOE_ERR_TIMEOUT, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+          }
+          s_item[0] = ok;
+        }
+        __syncthreads();
+        const int ok = s_item[0];
+        __syncthreads();
+        if (!ok) continue;
+        q0 = chunk * kBlocks / nsplit;
+        q1 = (chunk + 1) * kBlocks / nsplit;
+      } else {
+        if (arrived != nsplit - 1) continue;
+      }
 #if !MOE_DEVICE_SCOPE_PUBLISH
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #endif
-      // sum every chunk's partial (this one's included) in chunk order, so the
-      // tile's bits do not depend on which chunk arrived last
+      // sum the chunks' partials of this item's blocks in chunk order (this
+      // chunk's own included), so the tile's bits do not depend on arrivals
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-      for (int c2 = 0; c2 < nsplit; ++c2) {
-        const uint64_t* part = reinterpret_cast<const uint64_t*>(a.partial) +
-                               (size_t)(iq * kTailSlots + slot - chunk + c2) * (BM * BN / 2) +
-                               (size_t)wave * (C::FM * C::FN * 512) + lane;
+      const uint64_t* part0 = reinterpret_cast<const uint64_t*>(a.partial) +
+                              (size_t)(iq * kTailSlots + slot - chunk) * (BM * BN / 2) +
+                              (size_t)wave * (C::FM * C::FN * 512) + lane;
+      if (kShared && q1 - q0 < kBlocks) {
+        // a few blocks: the partials of up to four chunks of a block in flight
+        // at once (clamped loads, so none is predicated), added in chunk order
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j) {
+            const int q = j * C::FM + i;
+            if (q < q0 || q >= q1) continue;
+            for (int cb = 0; cb < nsplit; cb += 4) {
+              uint64_t v[4][8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              const uint64_t v = __hip_atomic_load(part + ((i * C::FN + j) * 8 + r) * 64, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-              acc[i][j][2 * r] += __uint_as_float((uint32_t)v);
-              acc[i][j][2 * r + 1] += __uint_as_float((uint32_t)(v >> 32));
+              for (int u = 0; u < 4; ++u) {
+                const uint64_t* part = part0 + (size_t)min(cb + u, nsplit - 1) * (BM * BN / 2);
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                  v[u][r] = __hip_atomic_load(part + ((i * C::FN + j) * 8 + r) * 64, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+              }
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                if (cb + u >= nsplit) break;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                  acc[i][j][2 * r] += __uint_as_float((uint32_t)v[u][r]);
+                  acc[i][j][2 * r + 1] += __uint_as_float((uint32_t)(v[u][r] >> 32));
+                }
+              }
+              __builtin_amdgcn_sched_barrier(0);
             }
-            // one 32x32 block of loads in flight at a time (the accumulators stay live)
-            __builtin_amdgcn_sched_barrier(0);
           }
+      } else {
+        for (int c2 = 0; c2 < nsplit; ++c2) {
+          const uint64_t* part = part0 + (size_t)c2 * (BM * BN / 2);
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                const uint64_t v = __hip_atomic_load(part + ((i * C::FN + j) * 8 + r) * 64, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                acc[i][j][2 * r] += __uint_as_float((uint32_t)v);
+                acc[i][j][2 * r + 1] += __uint_as_float((uint32_t)(v >> 32));
+              }
+              // one 32x32 block of loads in flight at a time (the accumulators stay live)
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        }
       }
     }
 
@@ -698,6 +780,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
           const int c = wn * C::WTN + j * 32 + ncol;
+          if (j * C::FM + i < q0 || j * C::FM + i >= q1) continue;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int m = wm * C::WTM + i * 32 + (r >> 2) * 8 + mrow + (r & 3);
@@ -711,9 +794,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     constexpr int CH = OUTW / 8;   // 16-byte chunks per output row
     uint16_t* cbase = a.C + (size_t)row0 * a.Nout + (size_t)tn * OUTW;
     const bool signal = (EPI == EPI_PLAIN) && a.flags != nullptr;
-#pragma unroll 4
-    for (int q = tid; q < vrows * CH; q += C::NT) {
-      const int m = q / CH, cc = q - (q / CH) * CH;
+    auto store_chunk = [&](int m, int cc) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(lds + m * LROW + cc * 8);
       uint16_t* dst = cbase + (size_t)m * a.Nout + cc * 8;
 #if MOE_DEVICE_SCOPE_PUBLISH
@@ -724,10 +805,43 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
                            __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(d64 + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-        continue;
+        return;
       }
 #endif
       *reinterpret_cast<u32x4*>(dst) = v;
+    };
+    const int nq = q1 - q0;
+    if (nq == kBlocks) {
+#pragma unroll 4
+      for (int x = tid; x < vrows * CH; x += C::NT) store_chunk(x / CH, x - (x / CH) * CH);
+    } else {
+      // this chunk's share: blocks q0..q1-1 of every wave, 32 rows x 4 chunks each
+      for (int x = tid; x < C::NW * nq * 128; x += C::NT) {
+        const int wb = x / (nq * 128);
+        const int rem = x - wb * (nq * 128);
+        const int q = q0 + (rem >> 7);
+        const int m = (wb / WN) * C::WTM + (q % C::FM) * 32 + ((rem & 127) >> 2);
+        if (m < vrows) store_chunk(m, ((wb % WN) * C::WTN + (q / C::FM) * 32) / 8 + (rem & 3));
+      }
+    }
+    // a shared tail tile is finished by the last of its chunks to store
+    bool last = true;
+    if (kShared && nsplit > 1) {
+#if MOE_DEVICE_SCOPE_PUBLISH
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#else
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#endif
+      __syncthreads();
+      if (tid == 0)
+        s_item[0] = __hip_atomic_fetch_add(tail_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      last = s_item[0] == 2 * nsplit - 1;
+      __syncthreads();
+      if (!last) continue;
+#if !MOE_DEVICE_SCOPE_PUBLISH
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
     }
     if (signal) {
 #if MOE_DEVICE_SCOPE_PUBLISH
