@@ -1,5 +1,5 @@
-// The consumer's copy loop as a device function, shared by the standalone
-// consumer kernel and the consumer role of the overlapped output projection.
+// The consumer's copy loop as a device function: the consumer role of the
+// overlapped output projection (its first c workgroups) runs it.
 //
 // Workgroup w of nwg copies the batches of BATCH consecutive 64 KiB copy
 // units starting at units (w + i nwg) BATCH, i = 0, 1, ... (the units of all

@@ -18,9 +18,11 @@
  *                   plan, transfer segments, gather of the routed rows
  *   moe_expert_forward_overlap
  *                   expert FFN as a persistent grouped GEMM; its output
- *                   projection raises one ready flag per tile while a
- *                   consumer kernel on a few CUs copies each ready segment
- *                   into its source rank's combine buffer
+ *                   projection raises one ready flag per tile while the
+ *                   same launch's consumer workgroups on a few CUs (or,
+ *                   role switching, the producer's own workgroups between
+ *                   tiles) copy each ready segment into its source rank's
+ *                   combine buffer
  *   moe_expert_forward_gathered
  *                   the same, its first projection reading the routed rows
  *                   straight from x (the gather fused into the tile loads)

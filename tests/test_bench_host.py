@@ -55,3 +55,16 @@ def test_committed_figures_are_physical(gathered):
         a_rows = 8219 if gathered else 8448
         compulsory = 2 * (a_rows * 4096 + 2 * 2 * 14336 * 4096 + 8448 * 14336)
         assert t >= compulsory
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    for f in bench.GEMM_SOURCES:
+        p = tmp_path / f
+        p.parent.mkdir(parents=True, exist_ok=True)
+        p.write_text("int a = 1;  // one\n\n// a note\nint b = 2;\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.gemm_source_hash()
+    (tmp_path / bench.GEMM_SOURCES[0]).write_text("int a = 1;  // the first\n// another note\nint b = 2;   \n")
+    assert bench.gemm_source_hash() == h0
+    (tmp_path / bench.GEMM_SOURCES[0]).write_text("int a = 1;\nint b = 3;\n")
+    assert bench.gemm_source_hash() != h0
