@@ -32,7 +32,8 @@ int make_geometry(const moe_shape_t* s, Geometry* g) {
     return MOE_ERR_INVALID_ARG;
   if (s->mgb < 1) return MOE_ERR_INVALID_ARG;
   if (s->H < 256 || s->H % 256 != 0 || s->F < 128 || s->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if (s->tb_m != 32 && s->tb_m != 64 && s->tb_m != 128 && s->tb_m != 256) return MOE_ERR_UNSUPPORTED;
+  if (s->tb_m != 16 && s->tb_m != 32 && s->tb_m != 64 && s->tb_m != 128 && s->tb_m != 256)
+    return MOE_ERR_UNSUPPORTED;
   if (s->E > 512) return MOE_ERR_UNSUPPORTED;
   const int El = s->E / s->R;
   if (El > 256 || (int64_t)El * s->R > 2048) return MOE_ERR_UNSUPPORTED;

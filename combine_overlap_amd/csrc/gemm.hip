@@ -496,7 +496,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     const int fidx = rt * a.tiles_n + tn;        // flag / trace index
 
     // wave-uniform global bases of this wave's DMA instructions (k offset added per stage);
-    // gathered A: each lane's own source row instead, its swizzled chunk included
+    // gathered A: each lane's own source row instead, its swizzled chunk included.
+    // A rows past the last 32-row block holding stored rows feed no MFMA: their
+    // DMA instructions still run (the stage waits count them) but read the
+    // tile's first rows (or the zero row) again, which the L2 already holds.
+    const int act_rows = min(BM, (vrows + 31) & ~31);
     const char* abase[C::A_PW];
     const char* bbase[C::B_PW];
     if constexpr (GATHER) {
@@ -510,16 +514,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       for (int i = 0; i < C::A_PW; ++i) {
         const int blk = wave_u * C::A_PW + i;
         const int r = row0 + blk * C::RPI + d_row;
-        const bool real = r < m_pad && (unsigned)src[i] < (unsigned)a.a_nrows;
+        const bool real = r < m_pad && (unsigned)src[i] < (unsigned)a.a_nrows && blk * C::RPI < act_rows;
         const uint64_t rp = real ? reinterpret_cast<uint64_t>(a.A) + (uint64_t)(uint32_t)src[i] * (uint64_t)(K * 2)
                                  : reinterpret_cast<uint64_t>(a.a_zero);
         abase[i] = reinterpret_cast<const char*>(rp + swz<C::CPR>((blk & 1) * C::RPI + d_row, d_pch) * 16);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < C::A_PW; ++i)
-        abase[i] = reinterpret_cast<const char*>(a.A) +
-                   ((size_t)(row0 + (wave_u * C::A_PW + i) * C::RPI) * K) * 2;
+      for (int i = 0; i < C::A_PW; ++i) {
+        const int rb = (wave_u * C::A_PW + i) * C::RPI;
+        abase[i] = reinterpret_cast<const char*>(a.A) + ((size_t)(row0 + (rb < act_rows ? rb : 0)) * K) * 2;
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::B_PW; ++i) {
@@ -579,9 +584,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       for (int j = 0; j < C::FN; ++j)
         fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + b_off[kk] + j * 32 * BK);
     };
-    // 32-row blocks of this wave inside the tile's stored rows (a short last
-    // row tile of an expert skips the MFMAs of the blocks past them)
-    const int fm_act = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (vrows - wm * C::WTM) / 32)));
+    // 32-row blocks of this wave that hold stored rows (a short last row tile
+    // of an expert skips the MFMAs of the blocks past them; with 16-row bands
+    // the last block may be half the next expert's rows, computed, not stored)
+    const int fm_act = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (vrows - wm * C::WTM + 31) / 32)));
     auto mfmas = [&](int buf, auto partial) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {

@@ -78,10 +78,10 @@ enum { MOE_MODE_OVERLAP = 0, MOE_MODE_SEQUENTIAL = 1, MOE_MODE_ROLE_SWITCH = 2 }
  *  gate_kind MOE_GATE_SOFTMAX: softmax over the k selected logits;
  *           MOE_GATE_SIGMOID: sigmoid of the k selected logits, normalised to sum 1
  *  tb_m     row-band height ([TLS] sec. 3.2.1): the padding unit of the owner
- *           groups and the transfer unit of the combine plan: 32, 64, 128 or
- *           256. The GEMMs run tiles of moe_sizes_t.tile_m (256) rows over
- *           each expert's tb_m-aligned rows, so the band can be smaller than
- *           the compute tile.
+ *           groups and the transfer unit of the combine plan: 16, 32, 64,
+ *           128 or 256. The GEMMs run tiles of moe_sizes_t.tile_m (256) rows
+ *           over each expert's tb_m-aligned rows, so the band can be smaller
+ *           than the compute tile (and, at 16, than one 32-row MFMA block).
  *  mgb      row bands per middle transfer segment ([TLS] sec. 3.3.2, Fig. 3(b)), >= 1
  */
 typedef struct {

@@ -66,7 +66,7 @@ def test_query_sizes_values():
     (dict(gate_kind=3), _abi.MOE_ERR_INVALID_ARG), (dict(mgb=0), _abi.MOE_ERR_INVALID_ARG),
     (dict(T=0), _abi.MOE_ERR_INVALID_ARG),
     (dict(H=384), _abi.MOE_ERR_UNSUPPORTED), (dict(F=200), _abi.MOE_ERR_UNSUPPORTED),
-    (dict(tb_m=16), _abi.MOE_ERR_UNSUPPORTED), (dict(tb_m=512), _abi.MOE_ERR_UNSUPPORTED),
+    (dict(tb_m=8), _abi.MOE_ERR_UNSUPPORTED), (dict(tb_m=512), _abi.MOE_ERR_UNSUPPORTED),
     (dict(E=1024, R=4), _abi.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_shapes_rejected(kw, code):

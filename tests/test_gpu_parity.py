@@ -33,6 +33,9 @@ CASES = [
     ("fine_mini_tb32", Workload("fine_mini", 8, 256, 512, 256, 64, 8, True, "sigmoid"), 0, 32, 2, 8, 0),
     ("zipf_mini_tb32", Workload("zipf_mini", 4, 512, 1024, 1024, 8, 2, True, "softmax", "zipf",
                                 w_std="fan_in"), 2, 32, 3, 8, 0),
+    # 16-row bands: an expert's last 32-row MFMA block may hold the next expert's rows
+    ("fine_mini_tb16", Workload("fine_mini", 8, 256, 512, 256, 64, 8, True, "sigmoid"), 1, 16, 2, 8, 0),
+    ("ragged_tb16", Workload("ragged", 3, 300, 256, 128, 6, 3, True, "softmax"), 2, 16, 1, 3, 0),
 ]
 
 
