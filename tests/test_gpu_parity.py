@@ -36,24 +36,39 @@ CASES = [
     # 16-row bands: an expert's last 32-row MFMA block may hold the next expert's rows
     ("fine_mini_tb16", Workload("fine_mini", 8, 256, 512, 256, 64, 8, True, "sigmoid"), 1, 16, 2, 8, 0),
     ("ragged_tb16", Workload("ragged", 3, 300, 256, 128, 6, 3, True, "softmax"), 2, 16, 1, 3, 0),
+    # degenerate and limit cases: no row for this rank at all (empty layout,
+    # no tiles, no segments); the most source ranks (16) with k = 16; the most
+    # experts (512, 256 of them local); one token per rank
+    ("no_local_rows", Workload("nolocal", 4, 128, 256, 128, 8, 2, True, "softmax"), 1, 64, 1, 8, 0,
+     "no_local"),
+    ("max_ranks_k16", Workload("maxfan", 16, 64, 256, 128, 64, 16, True, "sigmoid"), 5, 16, 2, 8, 0),
+    ("max_experts", Workload("maxE", 2, 128, 256, 128, 512, 8, True, "softmax"), 1, 32, 1, 8, 0),
+    ("one_token_per_rank", Workload("one", 4, 1, 256, 128, 8, 2, True, "softmax"), 3, 64, 1, 2, 0),
 ]
 
 
-def _inputs(w, r_self, layer):
+def _inputs(w, r_self, layer, modifier=None):
     from synth import make_logits, make_x, make_local_weights
     from synth.workloads import ShareInputs
     W1, W3, W2 = make_local_weights(w, r_self)
-    return ShareInputs(w, r_self, make_logits(w, layer), make_x(w), W1, W3, W2)
+    logits = make_logits(w, layer)
+    if modifier == "no_local":
+        # this rank's experts are never among any token's top k
+        El = w.E // w.R
+        logits = logits.copy()
+        logits[:, r_self * El:(r_self + 1) * El] = -30.0
+    return ShareInputs(w, r_self, logits, make_x(w), W1, W3, W2)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_share_parity(case):
     import torch
     from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL
-    name, w, r_self, tb, mgb, c, layer = case
+    name, w, r_self, tb, mgb, c, layer = case[:7]
+    modifier = case[7] if len(case) > 7 else None
     say(f"[parity] {name}: R={w.R} T={w.T} H={w.H} F={w.F} E={w.E} k={w.k} r_self={r_self} "
         f"tb_m={tb} mgb={mgb} c={c}")
-    inp = _inputs(w, r_self, layer)
+    inp = _inputs(w, r_self, layer, modifier)
     ref = om.oracle_share(inp.logits, inp.x, inp.W1, inp.W3, inp.W2, R=w.R, T=w.T, E=w.E, k=w.k,
                           gate_kind=w.gate_kind, r_self=r_self, tb_m=tb, mgb=mgb)
     sh, _ = make_gpu_share(w, r_self, tb, mgb, inp)
