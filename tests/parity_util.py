@@ -51,7 +51,7 @@ def check_rows(got: np.ndarray, ref: np.ndarray, what: str, layer_output: bool =
     zero = nr == 0
     assert np.all(got[zero] == 0), f"{what}: rows with zero reference are not exactly zero"
     rel = np.linalg.norm(got - ref, axis=1)[~zero] / nr[~zero]
-    mae = float(np.mean(np.abs(got - bf16_round(ref))))
+    mae = float(np.mean(np.abs(got - bf16_round(ref)))) if got.size else 0.0
     mx = float(rel.max()) if rel.size else 0.0
     say(f"  {what}: max per-row rel {mx:.3e}, mean abs err {mae:.3e}")
     assert mx <= REL_TOL, f"{what}: max per-row relative distance {mx} > {REL_TOL}"
