@@ -521,7 +521,7 @@ def main():
     if not args.sequential_only:
         layer["pct_mfma_peak_layer"] = round(100 * flops / t_best / 1e12 / PEAK_BF16_TFLOPS, 2)
     out = {
-        "metric": "MoE-layer TFLOP/s per EP rank (overlapped combine), % of bf16 MFMA peak",
+        "metric": "MoE-layer time/TFLOP/s per EP rank (overlap vs non-overlap), % MFMA peak",
         "value": round(flops / t_best / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
