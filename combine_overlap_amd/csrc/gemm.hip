@@ -82,7 +82,10 @@ enum { EPI_PLAIN = 0, EPI_SILU = 1, EPI_GATED = 2 };
 // blocks, so up to one chunk per block.
 constexpr int kMaxSplitSerial = 4;
 constexpr int kMaxSplitShared = 8;
-constexpr int kMinSplitSteps = 8;   // k-steps per chunk at least
+constexpr int kMinSplitSteps = 8;
+// buffer offset of gathered padding rows: past any x a resource describes
+// (x must stay below 2 GiB for the buffer form, so offset + k offset < 2^32)
+constexpr uint32_t kBufOutOfRange = 0x80000000u;   // k-steps per chunk at least
 
 template <int BM, int BN, int BK, int NS, int WM, int WN>
 struct Tile {
@@ -264,6 +267,22 @@ __device__ __forceinline__ void dma16_v(const void* lane_addr, uint32_t lds_byte
       : "memory");
 }
 
+// The same copy through a buffer resource (base, byte size) with a per-lane
+// 32-bit offset: a lane whose offset is at or past the resource's size lands
+// zeros in the LDS without touching memory.
+typedef int moe_i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16_buf(uint32_t lane_off, moe_i32x4 rsrc, uint32_t lds_byte) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(lane_off), "s"(rsrc), "s"(lds_byte)
+      : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const LDS_AS void*)p));
 }
@@ -386,7 +405,7 @@ __device__ __forceinline__ void stamp_max(const int32_t* meta, int word) {
   __hip_atomic_fetch_max(w, (uint64_t)wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool COPY = false, bool GATHER = false,
+template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool COPY = false, int GATHER = 0,
           bool CONS = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   using C = Tile<BM, BN, BK, NS, WM, WN>;
@@ -454,6 +473,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 
   const int n_rt = a.meta[META_NTILES];   // row tiles, in schedule positions
   const int m_pad = GATHER ? a.meta[META_MPAD] : 0;
+  moe_i32x4 a_rsrc = {0, 0, 0, 0};
+  if constexpr (GATHER == 2) {
+    // x as a raw buffer: a_nrows rows of K bf16 (the host checks the size fits below kBufOutOfRange)
+    const uint64_t xa = reinterpret_cast<uint64_t>(a.A);
+    a_rsrc[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)xa);
+    a_rsrc[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(xa >> 32));
+    a_rsrc[2] = __builtin_amdgcn_readfirstlane((int)((uint32_t)a.a_nrows * (uint32_t)(K * 2)));
+    a_rsrc[3] = 0x00020000;   // 32-bit data format, no swizzle, no stride: byte-addressed raw buffer
+  }
   int q = xcc_id(), tried = 0;
   while (true) {
     if constexpr (COPY) copy_duty<C::NT>(a, false, tid, s_copy);
@@ -503,6 +531,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     const int act_rows = min(BM, (vrows + 31) & ~31);
     const char* abase[C::A_PW];
     const char* bbase[C::B_PW];
+    // GATHER 2: 32-bit offsets into x's buffer resource, padding rows at an
+    // offset past its end (zeros, no memory read)
+    uint32_t aoff[GATHER == 2 ? C::A_PW : 1];
     if constexpr (GATHER) {
       // every source index is loaded before any is used (one wait), with
       // unconditional clamped loads
@@ -515,9 +546,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
         const int blk = wave_u * C::A_PW + i;
         const int r = row0 + blk * C::RPI + d_row;
         const bool real = r < m_pad && (unsigned)src[i] < (unsigned)a.a_nrows && blk * C::RPI < act_rows;
-        const uint64_t rp = real ? reinterpret_cast<uint64_t>(a.A) + (uint64_t)(uint32_t)src[i] * (uint64_t)(K * 2)
-                                 : reinterpret_cast<uint64_t>(a.a_zero);
-        abase[i] = reinterpret_cast<const char*>(rp + swz<C::CPR>((blk & 1) * C::RPI + d_row, d_pch) * 16);
+        const uint32_t chunk_off = (uint32_t)swz<C::CPR>((blk & 1) * C::RPI + d_row, d_pch) * 16;
+        if constexpr (GATHER == 2) {
+          aoff[i] = real ? (uint32_t)src[i] * (uint32_t)(K * 2) + chunk_off : kBufOutOfRange;
+        } else {
+          const uint64_t rp = real ? reinterpret_cast<uint64_t>(a.A) + (uint64_t)(uint32_t)src[i] * (uint64_t)(K * 2)
+                                   : reinterpret_cast<uint64_t>(a.a_zero);
+          abase[i] = reinterpret_cast<const char*>(rp + chunk_off);
+        }
       }
     } else {
 #pragma unroll
@@ -547,7 +583,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < C::A_PW; ++i) {
         const int blk = wave_u * C::A_PW + i;
-        if constexpr (GATHER) dma16_v(abase[i] + ko, st + (uint32_t)(blk * C::RPI * BK * 2));
+        if constexpr (GATHER == 2) dma16_buf(aoff[i] + (uint32_t)ko, a_rsrc, st + (uint32_t)(blk * C::RPI * BK * 2));
+        else if constexpr (GATHER) dma16_v(abase[i] + ko, st + (uint32_t)(blk * C::RPI * BK * 2));
         else dma16(abase[i] + ko, lane_off[blk & 1], st + (uint32_t)(blk * C::RPI * BK * 2));
       }
 #pragma unroll
@@ -882,8 +919,13 @@ static hipError_t launch_t(const GemmArgs& a, int grid, hipStream_t st) {
       return hipGetLastError();
     }
   } else {
+    if (a.a_rows != nullptr && (uint64_t)a.a_nrows * (uint64_t)a.K * 2 < (uint64_t)kBufOutOfRange) {
+      hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI, false, 2>), dim3(grid), dim3(WM * WN * 64), 0,
+                         st, a);
+      return hipGetLastError();
+    }
     if (a.a_rows != nullptr) {
-      hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI, false, true>), dim3(grid), dim3(WM * WN * 64), 0,
+      hipLaunchKernelGGL((k_gemm<BM, BN, BK, NS, WM, WN, EPI, false, 1>), dim3(grid), dim3(WM * WN * 64), 0,
                          st, a);
       return hipGetLastError();
     }
