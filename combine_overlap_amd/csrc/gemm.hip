@@ -326,7 +326,10 @@ __device__ __forceinline__ void copy_segment(const GemmArgs& a, int sg, int tid)
 //  wait = true (no tiles left): take segments by ticket (fetch-and-add), so
 //    the workgroups claim in parallel; wait (bounded) for each one's flags and
 //    copy it; return once every segment is taken.
-constexpr int kMaxClaim = 16;
+// At most this many segments per claim: one segment per claim makes the
+// workgroups race on the claim word, and large claims leave single
+// workgroups with megabytes to copy before their next tile.
+constexpr int kMaxClaim = 4;
 
 template <int NT>
 __device__ void copy_duty(const GemmArgs& a, bool wait, int tid, int* s_copy) {
