@@ -22,11 +22,24 @@
 //  * Split tail: an XCD queue of T tiles served by P workgroups runs T / P
 //    full rounds; its last T mod P tiles would leave most of that XCD idle
 //    for a whole tile time, so each of them is cut into s = P / (T mod P)
-//    (at most 4) chunks along K. A chunk stores its fp32 accumulators as a
-//    partial tile (device-scope write-through stores), waits for them to
-//    complete and increments the tile's arrival counter; the chunk that
-//    arrives last adds the other partials (device-scope loads) and runs the
-//    tile's epilogue, flag included.
+//    chunks along K (at most 4 in the first projection, 8 in the output
+//    projection). A chunk stores its fp32 accumulators as a partial tile
+//    (device-scope write-through stores), waits for them to complete and
+//    increments the tile's arrival counter. First projection: the chunk that
+//    arrives last adds the other partials and runs the epilogue. Output
+//    projection: every chunk waits (bounded) for all partials, adds the
+//    partials of its share of the accumulator blocks and stores it; the last
+//    chunk to store raises the tile's flag. Partials are always added in
+//    chunk order, so the bits do not depend on the arrival order.
+//  * CU partition (optional, output projection): the launch's first c
+//    workgroups run the consumer (consumer.hpp) instead of tiles.
+//  * Gathered rows (optional, first projection): A row r of a tile is row
+//    row_src[r] of x, loaded through a buffer resource over x with 32-bit
+//    offsets; padding rows sit at an offset past the resource's end and land
+//    zeros. An x of 2 GiB or more uses per-lane 64-bit addresses and a zero
+//    row instead.
+//  * Short tiles: the 32-row blocks past an expert's last row skip their
+//    MFMAs, and their DMA re-reads the tile's first rows (L2 hits).
 //  * Role switching (optional, output projection): the workgroups also do
 //    the consumer's work. Before each tile a workgroup claims the next
 //    remote segment (one atomic) if all its row tiles are flagged and copies
