@@ -21,7 +21,8 @@
 //
 // With the gather fused into the first projection's tile loads the rows are
 // not copied: only the indexes are built (row_src, -1 for padding). The plan
-// also zeroes the one row of H zeros that padding rows read there.
+// also zeroes the one row of H zeros that padding rows read there when x is
+// too large for the buffer-resource loads (2 GiB or more).
 #include "common.hpp"
 #include "partition_model.hpp"
 
