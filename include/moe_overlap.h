@@ -356,7 +356,11 @@ int moe_combine(const moe_shape_t* shape, uint16_t* const* combine_buf,
 
 /* Copies the device status word of the workspace to *status (host) and
  * synchronises the stream. Returns *status (MOE_OK, MOE_ERR_TIMEOUT, ...)
- * or MOE_ERR_HIP. */
+ * or MOE_ERR_HIP. MOE_ERR_TIMEOUT: a bounded device wait ran out, either a
+ * copying role waiting for ready flags (moe_ctx_set_wait_limit) or a K-chunk
+ * of the output projection's split tail tiles waiting 2 s for the other
+ * chunks of its tile (only if workgroups of the launch were not resident);
+ * the outputs of that call are then incomplete. moe_permute clears it. */
 int moe_read_status(const moe_shape_t* shape, void* ws, int32_t* status, void* stream);
 
 #ifdef __cplusplus
