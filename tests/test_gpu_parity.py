@@ -44,6 +44,8 @@ CASES = [
     ("max_ranks_k16", Workload("maxfan", 16, 64, 256, 128, 64, 16, True, "sigmoid"), 5, 16, 2, 8, 0),
     ("max_experts", Workload("maxE", 2, 128, 256, 128, 512, 8, True, "softmax"), 1, 32, 1, 8, 0),
     ("one_token_per_rank", Workload("one", 4, 1, 256, 128, 8, 2, True, "softmax"), 3, 64, 1, 2, 0),
+    # non-gated FFN with F % 256 != 0: the first projection runs 256 x 128 tiles
+    ("nongated_f384", Workload("ng384", 4, 256, 512, 384, 8, 2, False, "softmax"), 2, 64, 1, 4, 0),
 ]
 
 
