@@ -46,6 +46,8 @@ CASES = [
     ("one_token_per_rank", Workload("one", 4, 1, 256, 128, 8, 2, True, "softmax"), 3, 64, 1, 2, 0),
     # non-gated FFN with F % 256 != 0: the first projection runs 256 x 128 tiles
     ("nongated_f384", Workload("ng384", 4, 256, 512, 384, 8, 2, False, "softmax"), 2, 64, 1, 4, 0),
+    # 16 experts: routing with one lane per token and 16 logits per lane
+    ("experts16_k4", Workload("e16", 4, 200, 256, 256, 16, 4, True, "softmax"), 1, 32, 1, 4, 0),
 ]
 
 
