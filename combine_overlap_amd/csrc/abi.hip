@@ -239,7 +239,8 @@ int moe_ctx_timings(moe_ctx_t* ctx, float* ms) {
     uint64_t st[2];
     if (hipMemcpy(st, ctx->timed_meta + META_T_PROD, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess)
       return MOE_ERR_HIP;
-    ms[4] = st[1] > st[0] ? (float)((double)(st[1] - st[0]) * 1e-5) : 0.f;
+    // st[0] stays 0 when no workgroup ran a tile (an empty layout)
+    ms[4] = st[0] != 0 && st[1] > st[0] ? (float)((double)(st[1] - st[0]) * 1e-5) : 0.f;
   }
   return MOE_OK;
 }

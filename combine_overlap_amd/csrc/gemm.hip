@@ -32,7 +32,8 @@
 //    chunk to store raises the tile's flag. Partials are always added in
 //    chunk order, so the bits do not depend on the arrival order.
 //  * CU partition (optional, output projection): the launch's first c
-//    workgroups run the consumer (consumer.hpp) instead of tiles.
+//    workgroups run the consumer (consumer.hpp) first; once their share of
+//    the copy is done they take tiles like the others.
 //  * Gathered rows (optional, first projection): A row r of a tile is row
 //    row_src[r] of x, loaded through a buffer resource over x with 32-bit
 //    offsets; padding rows sit at an offset past the resource's end and land
@@ -462,7 +463,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this workgroup's copies have completed
       __syncthreads();
       if (tid == 0) stamp_max(a.meta, META_T_CONS);
-      return;
+      // its segments copied, the workgroup joins the producer for the tiles
+      // still queued (the local ones come last); the tail split stays sized
+      // for the producer's n_cu - c workgroups, so the bits do not change
     }
   }
 
@@ -499,6 +502,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     a_rsrc[3] = 0x00020000;   // 32-bit data format, no swizzle, no stride: byte-addressed raw buffer
   }
   int q = xcc_id(), tried = 0;
+  bool did_tile = false;   // the producer's end is the end of its last tile
   while (true) {
     if constexpr (COPY) copy_duty<C::NT>(a, false, tid, s_copy);
     if (tid == 0) {
@@ -518,9 +522,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     const int tile = s_item[0];
     if (tile < 0) {
       if constexpr (COPY) copy_duty<C::NT>(a, true, tid, s_copy);
-      if constexpr (CONS) if (tid == 0) stamp_max(a.meta, META_T_PROD);
+      if constexpr (CONS) if (tid == 0 && did_tile) stamp_max(a.meta, META_T_PROD);
       break;
     }
+    did_tile = true;
     const int chunk = __builtin_amdgcn_readfirstlane(s_item[1]);
     const int nsplit = __builtin_amdgcn_readfirstlane(s_item[2]);
     const int slot = __builtin_amdgcn_readfirstlane(s_item[3]);
