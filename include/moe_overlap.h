@@ -304,12 +304,15 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *            once all its tiles are flagged, while the others run the tiles as
  *            persistent producers raising a flag per tile (one stream: the
  *            CU split comes from the roles of one grid, not from two kernels).
+ *            A consumer workgroup whose share of the copy is done takes
+ *            tiles still queued, as a producer.
  *            MOE_MODE_SEQUENTIAL (baseline, [TLS] sec. 4.1.3): both projections
  *            on all CUs, then one bulk copy of all remote rows on all CUs.
  *            MOE_MODE_ROLE_SWITCH: both projections on all CUs, the output
  *            projection's workgroups doing the consumer's work as well: before
- *            each tile a workgroup copies every remote segment whose tiles are
- *            all flagged (claimed in schedule order, one claim per segment),
+ *            each tile a workgroup copies the next remote segments whose tiles are
+ *            all flagged (claimed in schedule order, up to 4 segments whose
+ *            tiles are covered by the same flags per claim),
  *            and once the tiles run out the workgroups copy the rest (each
  *            wait bounded like the consumer's). No CU is reserved; c is
  *            ignored and the K-split is sized for all CUs (the same bits as
