@@ -48,6 +48,9 @@ CASES = [
     ("nongated_f384", Workload("ng384", 4, 256, 512, 384, 8, 2, False, "softmax"), 2, 64, 1, 4, 0),
     # 16 experts: routing with one lane per token and 16 logits per lane
     ("experts16_k4", Workload("e16", 4, 200, 256, 256, 16, 4, True, "softmax"), 1, 32, 1, 4, 0),
+    # top-1 routing; H = 768 (three output column tiles, a combine row of 96
+    # 16-byte steps) and gated F = 384 (three first-projection column tiles)
+    ("top1_h768_f384", Workload("top1", 4, 256, 768, 384, 8, 1, True, "softmax"), 2, 64, 1, 4, 0),
 ]
 
 
