@@ -5,8 +5,8 @@
 //
 // k_route: one routing group of G lanes (the fewest with at most 32 logits
 // each: G = 8 for 256 experts, 1 up to 32) owns a token; lane i of the group
-// holds the logits of experts i, i+G, i+2G, ... as order-preserving integer
-// keys. Each of the k rounds takes the lane's best key by a tournament, then
+// holds the logits of experts i NQ ... i NQ + NQ - 1 as order-preserving
+// integer keys (loaded 16 bytes at a time when E is a multiple of 4). Each of the k rounds takes the lane's best key by a tournament, then
 // the group's best by a butterfly (higher logit wins, equal logits go to the
 // lower expert id), and the winner's key drops to 0 (below every logit).
 // The width balances the per-token instruction count (vector-ALU issue
@@ -46,14 +46,27 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
   const bool active = g_tok < n_tok;
   const size_t g = active ? (size_t)g_tok : 0;
   const uint32_t* row = reinterpret_cast<const uint32_t*>(logits) + g * E;
-  // keys of experts gi + q G: unconditional loads with clamped indices
+  // keys of experts gi NQ + q: unconditional loads with clamped indices
   // (predicated ones would each wait for the previous), then the selection
+  const int e0 = gi * NQ;
   uint32_t key[NQ];
+  if ((E & 3) == 0) {
+    // rows are 16-byte aligned; a 4-expert chunk is wholly inside or past E
+    const u32x4* row4 = reinterpret_cast<const u32x4*>(row);
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) key[q] = row[min(gi + q * G, E - 1)];
+    for (int c = 0; c < NQ / 4; ++c) {
+      const int i4 = (e0 >> 2) + c;
+      const u32x4 v = row4[i4 < (E >> 2) ? i4 : 0];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[4 * c + j] = v[j];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) key[q] = row[min(e0 + q, E - 1)];
+  }
   // (an inactive token's group reads row 0 and writes nothing; experts past E get key 0)
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) key[q] = order_key(key[q]) & (0u - (uint32_t)(gi + q * G < E));
+  for (int q = 0; q < NQ; ++q) key[q] = order_key(key[q]) & (0u - (uint32_t)(e0 + q < E));
   uint32_t sel_k[16];
   int sel_id[16];
 #pragma unroll
@@ -71,14 +84,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
       for (int q = 0; q + st < NQ; q += 2 * st)
         if (tk[q + st] > tk[q]) { tk[q] = tk[q + st]; tq[q] = tq[q + st]; }
     uint32_t bk = tk[0];
-    int bid = gi + tq[0] * G;
+    int bid = e0 + tq[0];
 #pragma unroll
     for (int off = G >> 1; off > 0; off >>= 1) {   // across the group: larger key, then lower id
       const uint32_t ok = __shfl_xor(bk, off, G);
       const int oid = __shfl_xor(bid, off, G);
       if (ok > bk || (ok == bk && oid < bid)) { bk = ok; bid = oid; }
     }
-    const int wq = ((bid & (G - 1)) == gi) ? bid / G : -1;   // the winner leaves the candidates
+    const int wq = (bid / NQ == gi) ? bid - e0 : -1;   // the winner leaves the candidates
 #pragma unroll
     for (int q = 0; q < NQ; ++q) key[q] = (q == wq) ? 0u : key[q];
     sel_k[r] = bk;
