@@ -114,10 +114,10 @@ class Layout:
     M_e: np.ndarray           # [E_l] rows of X_e (remote groups padded, local group not)
     expert_base: np.ndarray   # [E_l + 1] first row of X_e in the packed buffer
     m_pad: int                # rows of the packed buffer
-    row_src: np.ndarray       # [m_pad] global token index s*T+t of each row, -1 for zero rows
+    row_src: Optional[np.ndarray]   # [m_pad] global token index s*T+t of each row, -1 for zero rows
     recv_off: np.ndarray      # [R, E_l] first row of (e, s) in rank s's receive buffer
     recv_rows: np.ndarray     # [R] rows of rank s's receive buffer from this rank
-    recv_row: np.ndarray      # [R*T, k] where slot j of token g is found, -1 if not local
+    recv_row: Optional[np.ndarray]  # [R*T, k] where slot j of token g is found, -1 if not local
 
 
 def group_order(R: int, r_self: int) -> List[int]:
@@ -126,14 +126,15 @@ def group_order(R: int, r_self: int) -> List[int]:
     return [s for s in range(R) if s != r_self] + [r_self]
 
 
-def row_layout(ids: np.ndarray, R: int, T: int, E_l: int, r_self: int, tb_m: int) -> Layout:
-    """Build the per-expert row layouts X_e of [TLS] sec. 3.2.1 / Algorithm 1.
+def counts_layout(counts: np.ndarray, R: int, T: int, E_l: int, r_self: int, tb_m: int) -> Layout:
+    """The parts of the row layout that follow from the counts alone ([TLS]
+    sec. 3.2.1, Algorithm 1): padded group sizes, group and expert offsets,
+    receive offsets. row_src and recv_row are left as None (row_layout fills
+    them from the routing).
 
-    For each local expert: rows grouped by the owner rank of their token,
-    remote owners first (ascending), the local owner last; a remote group whose
-    size is not a multiple of tb_m is padded with zero rows up to the next
-    multiple; the local group is not padded. Rows inside a group keep the
-    ascending token order of the owner rank (reading: a stable counting sort).
+    For each local expert: owner groups in the order of group_order, a remote
+    group whose size is not a multiple of tb_m padded with zero rows up to the
+    next multiple, the local group not padded.
 
     Placement reading: [TLS] sec. 3.2 keeps a separate A matrix per expert;
     here X_e sits in one packed buffer at expert_base[e], the exclusive prefix
@@ -144,7 +145,7 @@ def row_layout(ids: np.ndarray, R: int, T: int, E_l: int, r_self: int, tb_m: int
     not overlap): rank s's buffer holds this rank's rows for s ordered by
     (local expert, token), so recv_off[s][e] = sum_{e' < e} count[e'][s].
     """
-    counts = local_histogram(ids, R, T, E_l, r_self)
+    counts = np.asarray(counts, dtype=np.int64).reshape(E_l, R)
     order = group_order(R, r_self)
     padded = counts.copy()
     for e in range(E_l):
@@ -171,25 +172,40 @@ def row_layout(ids: np.ndarray, R: int, T: int, E_l: int, r_self: int, tb_m: int
             recv_off[s, e] = acc
             acc += int(counts[e, s])
     recv_rows = counts.sum(axis=0)
+    return Layout(R, T, E_l, r_self, tb_m, counts, padded, order, group_row, M_e,
+                  expert_base, m_pad, None, recv_off, recv_rows, None)
 
+
+def row_layout(ids: np.ndarray, R: int, T: int, E_l: int, r_self: int, tb_m: int) -> Layout:
+    """Build the per-expert row layouts X_e of [TLS] sec. 3.2.1 / Algorithm 1.
+
+    The group sizes, padding and offsets are those of counts_layout for the
+    histogram of the routing. Rows inside a group keep the ascending token
+    order of the owner rank (reading: a stable counting sort); row_src maps
+    every packed row to its token (-1 for zero rows) and recv_row maps every
+    local (token, slot) to where its expert row is found: the combine-buffer
+    row for a remote owner, the packed row for r_self.
+    """
+    lay = counts_layout(local_histogram(ids, R, T, E_l, r_self), R, T, E_l, r_self, tb_m)
     k = ids.shape[1]
-    row_src = np.full(m_pad, -1, dtype=np.int64)
+    row_src = np.full(lay.m_pad, -1, dtype=np.int64)
     recv_row = np.full((R * T, k), -1, dtype=np.int64)
     first = r_self * E_l
     for e in range(E_l):
-        for s in order:
+        for s in lay.group_order:
             blk = ids[s * T:(s + 1) * T] == first + e          # [T, k]
             toks = np.nonzero(blk.any(axis=1))[0]              # ascending t
             slots = np.argmax(blk[toks], axis=1)               # the one slot holding e
-            rows = int(group_row[e, s]) + np.arange(toks.size)
+            rows = int(lay.group_row[e, s]) + np.arange(toks.size)
             g = s * T + toks
             row_src[rows] = g
             if s == r_self:
                 recv_row[g, slots] = rows
             else:
-                recv_row[g, slots] = int(recv_off[s, e]) + np.arange(toks.size)
-    return Layout(R, T, E_l, r_self, tb_m, counts, padded, order, group_row, M_e,
-                  expert_base, m_pad, row_src, recv_off, recv_rows, recv_row)
+                recv_row[g, slots] = int(lay.recv_off[s, e]) + np.arange(toks.size)
+    lay.row_src = row_src
+    lay.recv_row = recv_row
+    return lay
 
 
 def gather_rows(x_bits: np.ndarray, lay: Layout) -> np.ndarray:

@@ -11,7 +11,7 @@ import pytest
 from oracle import moe_share as om
 from synth import Workload, WORKLOADS, make_share_inputs
 from parity_util import (assert_plan_equal, bits, check_row_tiles, check_rows, make_gpu_share,
-                         oracle_plan_arrays, say, widen)
+                         oracle_plan_arrays, say, stated_default_calib, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -146,18 +146,32 @@ def test_share_parity(case):
 
 def check_auto_partition(sh, name):
     """The plan kernel's evaluation of the CU-split model (MOE_CONSUMER_AUTO)
-    picks the host model's c with a bit-identical predicted time whenever
-    the plan's segments are the host model's (shape mgb = its mgb), and a
-    valid candidate otherwise."""
+    against the oracle's event simulation of the model on the same counts and
+    segment size, with the library's stated default calibration: the same c
+    (an argmin of the oracle's times) and the predicted time to 1e-9. The
+    host function moe_plan_partition against the oracle with the model's own
+    segment size."""
+    from oracle import partition as op
     c_dev, t_dev = sh.auto_consumer_cu()
+    counts = sh.buf.counts.cpu().numpy()
+    shp = sh.shape
+    cal = stated_default_calib(sh.ctx.num_cus)
+    kw = dict(R=shp.R, H=shp.H, F=shp.F, tb_m=shp.tb_m, r_self=shp.r_self, calib=cal)
+    ref = op.partition_model(counts, mgb=shp.mgb, **kw)
+    say(f"  {name}: CU split device c={c_dev} ({t_dev:.9e} s), oracle c={ref.c} ({ref.predicted_s:.9e} s)")
+    assert t_dev != -1.0, f"{name}: the plan's model tables overflowed"
+    assert c_dev in ref.times, f"{name}: device c {c_dev} is not a candidate"
+    best = min(ref.times.values())
+    assert ref.times[c_dev] == pytest.approx(best, rel=1e-9), f"{name}: device c {c_dev} is not the argmin"
+    runner_up = min([t for c, t in ref.times.items() if c != ref.c], default=float("inf"))
+    if runner_up > best * (1 + 1e-9):
+        assert c_dev == ref.c, f"{name}: device c {c_dev} != oracle c {ref.c}"
+    assert t_dev == pytest.approx(ref.predicted_s, rel=1e-9), f"{name}: predicted {t_dev!r} != {ref.predicted_s!r}"
     c_host, g_host, t_host = sh.partition()
-    say(f"  {name}: CU split device c={c_dev} ({t_dev:.6e} s), host c={c_host} ({t_host:.6e} s), "
-        f"mgb {sh.shape.mgb} / model {g_host}")
-    assert c_dev in range(8, 49, 8), f"{name}: device c {c_dev}"
-    assert t_dev > 0 or (t_dev == 0 and t_host == 0)
-    if g_host == sh.shape.mgb and sh.ctx.num_cus == 256:
-        assert c_dev == c_host, f"{name}: device c {c_dev} != host c {c_host}"
-        assert t_dev == t_host, f"{name}: predicted {t_dev!r} != {t_host!r}"
+    ref_h = op.partition_model(counts, **kw)
+    assert g_host == ref_h.mgb
+    assert ref_h.times[c_host] == pytest.approx(min(ref_h.times.values()), rel=1e-9)
+    assert t_host == pytest.approx(ref_h.predicted_s, rel=1e-9)
 
 
 def check_fused_gather(sh, ref, w, name, c, y_bits, share_bits):

@@ -100,3 +100,57 @@ def test_ascending_expert_order_is_caught(monkeypatch):
 
 
 ORIG_SCHED = om.tile_schedule
+
+
+# ------------------------------------------------ source-level planted mistakes
+
+import inspect
+import textwrap
+
+from oracle import partition as op
+import test_partition_model as PM
+
+
+def _mutated(func, old, new):
+    """A copy of func with one source fragment replaced (compiled in func's
+    own module namespace, so it sees the same helpers)."""
+    src = textwrap.dedent(inspect.getsource(func))
+    assert old in src, f"mutation anchor not found in {func.__name__}: {old!r}"
+    ns = dict(func.__globals__)
+    exec(compile(src.replace(old, new, 1), f"<mutated {func.__name__}>", "exec"), ns)
+    return ns[func.__name__]
+
+
+def test_ties_by_expert_id_is_caught(monkeypatch):
+    """Rule (ii) with the remote-rows key dropped (ties by expert id)."""
+    bad = _mutated(om.tile_schedule, "key=lambda e: (-int(n_rb[e]), -int(n_rr[e]), e)",
+                   "key=lambda e: (-int(n_rb[e]), e)")
+    monkeypatch.setattr(om, "tile_schedule", bad)
+    with pytest.raises(AssertionError):
+        RL.test_schedule_equal_band_counts_more_remote_rows_first()
+
+
+PARTITION_MUTATIONS = {
+    # a row tile ready at the wave of its first instance, not its last
+    "ready_at_first_instance": ("ready[p] = t_prod", "ready[p] = ready[p] or t_prod",
+                                [PM.test_last_instance_sets_readiness]),
+    # a partial wave priced at its full length
+    "partial_wave_full_length": ("length * max(len(wave) / P, 1.0 / 3.0)", "length",
+                                 [PM.test_single_tile_single_segment_closed_form,
+                                  PM.test_whole_waves_of_identical_tiles]),
+    # a segment's copy not queued behind the previous one
+    "copies_in_parallel": ("t_copy = max(t_copy, start) +", "t_copy = start +",
+                           [PM.test_segmented_group_closed_form]),
+    # the copy moves only H bytes per row (a dropped factor 2 of bf16)
+    "copy_bytes_halved": ("2.0 * H * int(segs.rows[i]) / bw", "H * int(segs.rows[i]) / bw",
+                          [PM.test_single_tile_single_segment_closed_form]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PARTITION_MUTATIONS))
+def test_partition_planted_mistake_is_caught(name, monkeypatch):
+    old, new, pins = PARTITION_MUTATIONS[name]
+    monkeypatch.setattr(op, "expert_phase_time", _mutated(op.expert_phase_time, old, new))
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            pin()

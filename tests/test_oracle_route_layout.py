@@ -294,3 +294,23 @@ def test_page_padding_bound_per_expert_at_scale():
         lay = om.row_layout(ids, 4, 2048, 16, 0, tb)
         pad = (lay.padded - lay.counts).sum(axis=1)
         assert np.all(pad <= 3 * (tb - 1))
+
+
+def test_schedule_equal_band_counts_more_remote_rows_first():
+    """[TLS] sec. 3.2.2 rule (ii) on a tie of Algorithm 1's band count: the
+    expert with more remote rows goes first (tests/golden fixture)."""
+    with open(os.path.join(GOLDEN, "rule2_equal_bands_more_rows_first.json")) as f:
+        fx = json.load(f)
+    R, T, E, r_self, tb = fx["R"], fx["T"], fx["E"], fx["r_self"], fx["tb_m"]
+    ids = np.array(fx["ids"], dtype=np.int32)
+    E_l = E // R
+    lay = om.row_layout(ids, R, T, E_l, r_self, tb)
+    b = om.tile_schedule(lay)
+    first = r_self * E_l
+    remote = b.expert[:b.n_remote] + first
+    for e, n in fx["expected_remote_band_counts_by_expert"].items():
+        assert int(np.sum(remote == int(e))) == n
+        assert int(b.valid[:b.n_remote][remote == int(e)].sum()) == fx["expected_remote_rows_by_expert"][e]
+    assert [k for k, _ in itertools.groupby(remote.tolist())] == fx["expected_remote_expert_order_global"]
+    local = [k for k, _ in itertools.groupby((b.expert[b.n_remote:] + first).tolist())]
+    assert local == fx["expected_local_expert_order_global"]
