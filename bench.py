@@ -2,18 +2,20 @@
 """Benchmark: one EP rank's MoE-layer share on one MI355X, overlap vs non-overlap.
 
 A step is one pass of the whole share over one batch of synthetic input:
-route -> counts to host -> partition (consumer CUs, segment size) ->
-permute -> expert FFN with the overlapped combine transfer -> weighted
-reduction. Inputs are resident in HBM before the timed region.
+route -> permute (the plan kernel also picks the consumer CU count) ->
+expert FFN with the overlapped combine transfer -> weighted reduction.
+Inputs are resident in HBM before the timed region; no step waits on the host.
 
-Three forms of the expert phase are timed in the same run: the overlap with
-a consumer on its own CU partition (the paper's design), the role-switching
+Every workload of the path is measured in one run (default: all five), each
+with three forms of the expert phase timed side by side: the overlap with a
+consumer on its own CU partition (the paper's design), the role-switching
 overlap (the producer's workgroups do the copy between tiles), and the
-non-overlapped baseline (GEMMs on all CUs, then one bulk copy), each with the
-routed rows gathered into x_perm by the permute step and with the gather
-fused into the first projection's tile loads. `value` is the fastest
-overlapped form (config.overlap_mode, config.gather); the sequential baseline
-it is compared with uses the same gather.
+non-overlapped baseline (GEMMs on all CUs, then one bulk copy); each form
+with the routed rows gathered into x_perm by the permute step and with the
+gather fused into the first projection's tile loads. The headline `value`
+is the largest single layer (the Zipf-skewed Mixtral-shaped workload): the
+algorithmic TFLOP/s of its fastest overlapped form. The other workloads are
+reported under `configs`.
 
 Prints ONE JSON line on stdout (details on stderr).
 """
@@ -22,6 +24,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -34,7 +37,9 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 # band height per workload: the fastest measured overlapped layer step
 DEFAULT_TB = {1: 64, 2: 64, 3: 256, 4: 32, 5: 64}
-# sources whose change invalidates stored hardware-counter traffic figures
+# the headline workload: the largest single layer that fits one GPU
+HEADLINE = 3
+# sources whose change invalidates stored hardware-counter figures
 GEMM_SOURCES = ("combine_overlap_amd/csrc/gemm.hip", "combine_overlap_amd/csrc/common.hpp",
                 "combine_overlap_amd/csrc/consumer.hpp")
 
@@ -43,35 +48,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, help="workload id (1-5); 2 = Mixtral-shaped")
-    ap.add_argument("--layer", type=int, default=0, help="layer of the layered workload")
+    ap.add_argument("--configs", default="1,2,3,4,5",
+                    help="workload ids to measure (1-5); the headline is 3 when listed, else the first")
+    ap.add_argument("--config", type=int, default=0, help="measure this one workload only")
+    ap.add_argument("--layer", type=int, default=0, help="layer of the layered workload (5)")
     ap.add_argument("--tb", type=int, default=0, help="band height (0 = per-workload default)")
-    ap.add_argument("--c", type=int, default=0, help="consumer CUs (0 = cost model)")
+    ap.add_argument("--c", type=int, default=0, help="consumer CUs (0 = the plan's model choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sequential-only", action="store_true",
-                    help="run only the non-overlapped path (for counter collection, which "
-                         "serialises kernels and so cannot run the concurrent consumer)")
+                    help="run only the non-overlapped path (for counter collection)")
     ap.add_argument("--gather", choices=("both", "materialized", "fused"), default="both",
                     help="A rows of the first projection: the materialized x_perm, the gather "
                          "fused into its tile loads, or both (timed side by side)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-layer-sweep", action="store_true",
+                    help="skip the 16-layer sweep of the layered workload")
+    ap.add_argument("--c-sweep", default="",
+                    help="comma-separated consumer CU counts: expert phase of the CU partition at each")
+    ap.add_argument("--timeline", default="",
+                    help="write a device-timeline summary (markdown) of the headline workload's CU-partition "
+                         "expert phase to this path")
     ap.add_argument("--table2-sweep", action="store_true",
                     help="the shape sweep of the tile-signalling paper's Table 2 on this GPU (tokens per "
                          "rank 8192/16384, K = 2048, N = 4096/8192, experts per rank 4..64, three router "
-                         "skews): per shape the sequential baseline, the CU-partition overlap at the "
-                         "model's c and at c = 8..48, the other segment size, and role switching; adds a "
-                         "'table2_sweep' object to the JSON line")
-    ap.add_argument("--layer-sweep", action="store_true",
-                    help="layered workload: per layer, the CU-partition overlap at the partition "
-                         "model's consumer count and at every candidate count, the role-switching "
-                         "overlap and the sequential baseline (expert phase, HIP events); adds a "
-                         "'layer_sweep' object to the JSON line")
-    return ap.parse_args()
+                         "skews); adds a 'table2_sweep' object to the JSON line")
+    ap.add_argument("--table2-subset", action="store_true",
+                    help="with --table2-sweep: N = 8192, tokens per rank 16384, E in {4, 16, 64} only")
+    return ap.parse_args(argv)
 
 
 def gemm_source_hash() -> str:
@@ -128,42 +135,49 @@ def stored_mfma(workload: str, tb: int, gathered: bool):
         return None
 
 
-def cpu_baseline(w, inp, tb, target_s):
-    """Times the CPU oracle (as it is) on a bounded sample of the same workload."""
+def host_info():
+    """CPU model (lscpu), the BLAS numpy calls and its thread count."""
+    model = "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    blas, threads = "unknown", None
+    try:
+        import threadpoolctl
+        for d in threadpoolctl.threadpool_info():
+            if d.get("user_api") == "blas":
+                blas = f"{d.get('internal_api')} {d.get('version')} ({d.get('architecture')})"
+                threads = int(d.get("num_threads"))
+                break
+    except Exception:
+        pass
+    return model, blas, threads
+
+
+def cpu_baseline(w, inp, tb, layer):
+    """The CPU oracle, as it stands, on the whole workload: route -> layout ->
+    schedule -> segments -> fp64 expert FFN -> transfer -> weighted reduction
+    (oracle_share end to end; input generation excluded)."""
     from oracle import moe_share as om
-    cores = len(os.sched_getaffinity(0))
+    model, blas, threads = host_info()
     t0 = time.perf_counter()
-    ids, gates = om.route(inp.logits, w.k, w.gate_kind)
-    lay = om.row_layout(ids, w.R, w.T, w.E_local, inp.r_self, tb)
-    t_route = time.perf_counter() - t0
-    # expert FFN on the first n rows of every non-empty local expert
-    x_perm = om.gather_rows(inp.x, lay)
-    experts = [e for e in range(w.E_local) if lay.M_e[e] > 0]
-    wts = {}
-    for e in experts:
-        wts[e] = (om.widen_bf16(inp.W1[e]), om.widen_bf16(inp.W3[e]) if inp.W3 is not None else None,
-                  om.widen_bf16(inp.W2[e]))
-    per_row = (6 if w.gated else 4) * w.H * w.F
-    n = 8
-    flops = 0.0
-    t_ffn = 0.0
-    while True:
-        flops = 0.0
-        t0 = time.perf_counter()
-        for e in experts:
-            lo = int(lay.expert_base[e])
-            m = min(n, int(lay.M_e[e]))
-            om.expert_ffn(x_perm[lo:lo + m], *wts[e])
-            flops += per_row * m
-        t_ffn = time.perf_counter() - t0
-        if t_ffn >= target_s / 4 or n >= 4096:
-            break
-        n *= 2
-    val = flops / t_ffn / 1e12
-    return {"value": round(val, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle: routing+layout of all {w.R * w.T} tokens ({t_route:.2f} s, "
-                       f"not in value) and the expert FFN on the first {n} rows of each of "
-                       f"{len(experts)} local experts ({flops / 1e9:.1f} GFLOP in {t_ffn:.2f} s)")}
+    res = om.oracle_share(inp.logits, inp.x, inp.W1, inp.W3, inp.W2, R=w.R, T=w.T, E=w.E, k=w.k,
+                          gate_kind=w.gate_kind, r_self=inp.r_self, tb_m=tb)
+    wall = time.perf_counter() - t0
+    M = int(res.layout.counts.sum())
+    flops = float((6 if w.gated else 4) * w.H * w.F) * M
+    return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": (f"the whole workload{f' (layer {layer})' if w.layers > 1 else ''}: oracle_share end to end "
+                       f"(fp64 NumPy, {M} valid rows, {flops / 1e12:.3f} TFLOP) in {wall:.2f} s; "
+                       f"value = the layer's algorithmic FLOPs / that wall time"),
+            "wall_s": round(wall, 3), "cpu_model": model, "blas": blas,
+            "host_cpus_in_affinity": len(os.sched_getaffinity(0))}
 
 
 def hbm_phases(sh, w, torch, M, m_pad, remote, bulk_copy_ms, reps=20):
@@ -205,6 +219,16 @@ def hbm_phases(sh, w, torch, M, m_pad, remote, bulk_copy_ms, reps=20):
     return out
 
 
+def phase_times(sh, mode, c, reps, warm=2):
+    """Per-phase device times (ms, medians) of `reps` expert-phase calls."""
+    d = []
+    for i in range(reps + warm):
+        sh.expert_forward(mode, n_consumer_cu=c)
+        if i >= warm:
+            d.append(sh.ctx.timings())
+    return {k: float(np.median([t[k] for t in d])) for k in d[0]}
+
+
 def layer_sweep(sh, w, make_logits, torch, ops, modes, reps=5, cands=(8, 16, 24, 32, 40, 48)):
     """Expert-phase times (ms, median of reps after 2 warmups) per layer and form.
 
@@ -212,31 +236,24 @@ def layer_sweep(sh, w, make_logits, torch, ops, modes, reps=5, cands=(8, 16, 24,
     single count over all layers and with the best count of each layer."""
     MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL = modes
     sh.ctx.set_timing(True)
-
-    def phase(mode, c):
-        d = []
-        for i in range(reps + 2):
-            sh.expert_forward(mode, n_consumer_cu=c)
-            if i >= 2:
-                d.append(sh.ctx.timings()["total"])
-        return float(np.median(d))
     rows = []
     for layer in range(w.layers):
         sh.buf.logits.copy_(torch.from_numpy(make_logits(w, layer)))
         sh.route()
         sh.permute()
-        torch.cuda.synchronize()
+        c_model, pred = sh.auto_consumer_cu()
         counts = sh.buf.counts.cpu().numpy()
-        c_model, _, pred = ops.moe_plan_partition(sh.shape, counts)
-        t = {c: phase(MOE_MODE_OVERLAP, c) for c in cands}
+        t = {c: phase_times(sh, MOE_MODE_OVERLAP, c, reps)["total"] for c in cands}
         if c_model not in t:
-            t[c_model] = phase(MOE_MODE_OVERLAP, c_model)
+            t[c_model] = phase_times(sh, MOE_MODE_OVERLAP, c_model, reps)["total"]
+        rs = phase_times(sh, MOE_MODE_ROLE_SWITCH, c_model, reps)
         row = {"layer": layer, "valid_rows": int(counts.sum()), "counts": counts.tolist(),
                "remote_rows": int(counts.sum() - counts[:, sh.r_self].sum()),
                "c_model": int(c_model), "predicted_ms": round(pred * 1e3, 4),
                "partition_ms": {str(c): round(v, 4) for c, v in sorted(t.items())},
-               "role_switch_ms": round(phase(MOE_MODE_ROLE_SWITCH, c_model), 4),
-               "sequential_ms": round(phase(MOE_MODE_SEQUENTIAL, c_model), 4)}
+               "role_switch_ms": round(rs["total"], 4),
+               "role_switch_exposed_us": round(rs["exposed"] * 1e3, 2),
+               "sequential_ms": round(phase_times(sh, MOE_MODE_SEQUENTIAL, c_model, reps)["total"], 4)}
         rows.append(row)
         log(f"[sweep] layer {layer:2d}: rows {row['valid_rows']}, model c={c_model} "
             f"{t[c_model]:.3f} ms, best c={min(cands, key=t.get)} {min(t[c] for c in cands):.3f} ms, "
@@ -251,6 +268,256 @@ def layer_sweep(sh, w, make_logits, torch, ops, modes, reps=5, cands=(8, 16, 24,
                          "per_layer_best_c": tot(lambda r: min(r["partition_ms"][str(c)] for c in cands)),
                          "role_switch": tot(lambda r: r["role_switch_ms"]),
                          "sequential": tot(lambda r: r["sequential_ms"])}}
+
+
+def c_sweep(sh, cands, modes, reps=8):
+    """The CU-partition expert phase at each consumer CU count (HIP events):
+    expert phase, output-projection launch and exposed copy."""
+    MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL = modes
+    sh.ctx.set_timing(True)
+    seq = phase_times(sh, MOE_MODE_SEQUENTIAL, 0, reps)
+    out = {"sequential": {"expert_phase_ms": round(seq["total"], 4), "gemm2_ms": round(seq["producer"], 4),
+                          "bulk_copy_us": round(seq["exposed"] * 1e3, 2)},
+           "cu_partition": {}}
+    for c in cands:
+        t = phase_times(sh, MOE_MODE_OVERLAP, c, reps)
+        out["cu_partition"][str(c)] = {"expert_phase_ms": round(t["total"], 4),
+                                       "output_projection_launch_ms": round(t["producer"], 4),
+                                       "exposed_copy_us": round(t["exposed"] * 1e3, 2)}
+        log(f"[c-sweep] c={c}: expert phase {t['total']:.3f} ms, launch {t['producer']:.3f} ms, "
+            f"exposed {t['exposed'] * 1e3:.1f} us (sequential {seq['total']:.3f} ms)")
+    sh.ctx.set_timing(False)
+    return out
+
+
+def timeline(sh, torch, path, name, mode_overlap):
+    """One CU-partition expert phase with the device trace on: per output tile
+    its flag time, per segment of consumer workgroup 0 its wait, readiness and
+    copy end (100 MHz device clock). Writes a markdown summary."""
+    v = sh.sizes
+    words = 8 + int(v.max_flags) + 3 * int(v.max_bands)
+    tr = torch.zeros(words, dtype=torch.int64, device=sh.device)
+    sh.ctx.set_trace(sh.shape, tr)
+    sh.expert_forward(mode_overlap, n_consumer_cu=sh.auto_consumer_cu()[0])
+    torch.cuda.synchronize()
+    sh.ctx.set_trace(sh.shape, None)
+    t = tr.cpu().numpy().astype(np.int64)
+    plan = sh.plan_arrays()
+    n_t, n_rt, n_seg = plan["n_tiles"], plan["n_remote_tiles"], plan["n_seg"]
+    tiles2 = int(v.max_flags) // int(v.max_tiles)
+    t0 = int(t[0])
+    us = lambda x: (int(x) - t0) * 1e-2   # 100 MHz ticks -> us
+    flag = t[8:8 + n_t * tiles2].reshape(n_t, tiles2)
+    sched = plan["tile_sched"]
+    remote_done = [us(flag[sched[p]].max()) for p in range(n_rt)]
+    all_done = us(flag.max())
+    seg0 = 8 + int(v.max_flags)
+    segs = t[seg0:seg0 + 3 * n_seg].reshape(n_seg, 3)
+    mine = [i for i in range(n_seg) if segs[i, 0] != 0]
+    lines = [f"# Device timeline: {name}, CU-partition expert phase (output projection launch)", "",
+             f"Command: `python bench.py --config <id> --timeline <path>` (bench.py `timeline()`); clock "
+             f"wall_clock64 at 100 MHz, times in microseconds from the output projection's start.", "",
+             f"- consumer CUs: {sh.auto_consumer_cu()[0]}",
+             f"- row tiles: {n_t} ({n_rt} holding remote bands), column tiles per row tile: {tiles2}",
+             f"- segments: {n_seg}; traced by consumer workgroup 0: {len(mine)}",
+             f"- first remote row tile complete: {remote_done[0]:.1f}" if remote_done else "- no remote tiles",
+             f"- last remote row tile complete: {max(remote_done):.1f}" if remote_done else "",
+             f"- last tile complete (producer end): {all_done:.1f}",
+             f"- consumer start: {us(t[1]):.1f}"]
+    if mine:
+        done = [us(segs[i, 2]) for i in mine if segs[i, 2] != 0]
+        before = sum(1 for x in done if x < all_done)
+        lines += [f"- workgroup 0's copies finished before the producer's end: {before} of {len(done)}",
+                  f"- workgroup 0's last copy end: {max(done):.1f}" if done else "", "",
+                  "| segment | wait begins | flags seen | copy done |", "|---|---|---|---|"]
+        pick = mine if len(mine) <= 24 else [mine[int(q)] for q in np.linspace(0, len(mine) - 1, 24)]
+        for i in pick:
+            lines.append(f"| {i} | {us(segs[i, 0]):.1f} | {us(segs[i, 1]):.1f} | "
+                         f"{us(segs[i, 2]) if segs[i, 2] else float('nan'):.1f} |")
+    with open(path, "w") as f:
+        f.write("\n".join(l for l in lines if l is not None) + "\n")
+    log(f"[bench] timeline written to {path}")
+
+
+def bench_workload(wid, args, torch, want_cpu, headline):
+    from synth import WORKLOADS, make_logits, make_x, make_local_weights
+    from synth.workloads import ShareInputs
+    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL
+    from combine_overlap_amd.share import MoEShare, bf16_tensor
+    from combine_overlap_amd import ops
+
+    w = WORKLOADS[wid]
+    tb = args.tb or DEFAULT_TB[wid]
+    layer = args.layer if w.layers > 1 else 0
+    r_self = 0
+    log(f"[bench] workload {w.name} layer {layer} tb_m={tb}: generating inputs")
+    W1, W3, W2 = make_local_weights(w, r_self)
+    inp = ShareInputs(w, r_self, make_logits(w, layer), make_x(w), W1, W3, W2)
+    dev = torch.device("cuda:0")
+    sh = MoEShare(w.R, w.T, w.H, w.F, w.E, w.k, w.gated, w.gate_kind, r_self=r_self, tb_m=tb, device=dev)
+    sh.allocate(torch.from_numpy(inp.logits).to(dev), bf16_tensor(inp.x, dev), bf16_tensor(W1, dev),
+                bf16_tensor(W3, dev) if W3 is not None else None, bf16_tensor(W2, dev))
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: buffers ready")
+
+    def step(mode):
+        sh.layer(mode, n_consumer_cu=args.c or None)
+
+    gathers = {"both": (False, True), "materialized": (False,), "fused": (True,)}[args.gather]
+    sh.fused_gather = gathers[0]
+    main_mode = MOE_MODE_SEQUENTIAL if args.sequential_only else MOE_MODE_OVERLAP
+    for _ in range(max(1, args.warmup)):
+        step(main_mode)
+    torch.cuda.synchronize()
+    if sh.status() != 0:
+        raise RuntimeError(f"{w.name}: device status {sh.status()} after warmup")
+    c_model, pred = sh.auto_consumer_cu()
+    c_used = args.c or c_model
+    mgb_used = sh.shape.mgb
+    counts = sh.buf.counts.cpu().numpy()
+    M = int(counts.sum())
+    remote = int(counts.sum() - counts[:, r_self].sum())
+    flops = float((6 if w.gated else 4) * w.H * w.F) * M
+    flops1 = float((4 if w.gated else 2) * w.H * w.F) * M
+    plan = sh.plan_arrays()
+    m_pad = plan["m_pad"]
+    # compulsory HBM bytes of the first-projection GEMM: its A rows (x_perm, or
+    # the valid rows of x when gathered: padding reads no memory), W1 (+W3) of
+    # the experts that received rows, h
+    n_w = (2 if w.gated else 1) * int((counts.sum(axis=1) > 0).sum())
+    gemm1_bytes = {False: 2 * (m_pad * w.H + n_w * w.F * w.H + m_pad * w.F),
+                   True: 2 * (M * w.H + n_w * w.F * w.H + m_pad * w.F)}
+    log(f"[bench] {w.name}: valid rows {M}, remote rows {remote}, padded rows {m_pad}, bands "
+        f"{plan['n_bands']}, segments {plan['n_seg']}, c={c_used} (model {c_model}, predicted "
+        f"{pred * 1e3:.3f} ms), mgb={mgb_used}")
+
+    def timed(mode, k):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(k):
+            step(mode)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / k
+
+    modes = ((MOE_MODE_SEQUENTIAL,) if args.sequential_only else
+             (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
+    mname = {MOE_MODE_OVERLAP: "cu_partition", MOE_MODE_ROLE_SWITCH: "role_switch",
+             MOE_MODE_SEQUENTIAL: "sequential"}
+    gname = {False: "materialized", True: "fused"}
+    t_step = {}
+    for fused in gathers:
+        sh.fused_gather = fused
+        for mode in modes:
+            for _ in range(args.warmup):
+                step(mode)
+            t_step[(fused, mode)] = timed(mode, args.steps)
+            log(f"[bench] {w.name} gather {gname[fused]}, {mname[mode]}: layer step "
+                f"{t_step[(fused, mode)] * 1e3:.3f} ms")
+
+    # per-phase device times (HIP events on the stream the kernels run on)
+    sh.ctx.set_timing(True)
+    ph = {}
+    for fused in gathers:
+        sh.fused_gather = fused
+        sh.permute()
+        for mode in modes:
+            ph[(fused, mode)] = phase_times(sh, mode, c_used, max(3, args.steps))
+    sh.ctx.set_timing(False)
+    torch.cuda.synchronize()
+    if sh.status() != 0:
+        raise RuntimeError(f"{w.name}: device status {sh.status()} after the timed runs")
+
+    overlapped = [k for k in t_step if k[1] != MOE_MODE_SEQUENTIAL] or list(t_step)
+    best = min(overlapped, key=t_step.get)
+    b_fused, b_mode = best
+    t_best = t_step[best]
+    t_seq = t_step[(b_fused, MOE_MODE_SEQUENTIAL)]
+    g1 = ph[best]["gemm1"]
+    ach1 = flops1 / (g1 * 1e-3) / 1e12
+    traffic = stored_traffic(w.name, tb, b_fused)
+    mfma = stored_mfma(w.name, tb, b_fused)
+    hbm = hbm_phases(sh, w, torch, M, m_pad, remote, ph[(b_fused, MOE_MODE_SEQUENTIAL)]["exposed"])
+    log(f"[bench] {w.name} HBM-bound steps: " + ", ".join(
+        f"{k} {v['us']:.1f} us {v['GB/s']:.0f} GB/s ({v['frac']:.2f})" for k, v in hbm.items()))
+
+    layer_d = {"valid_rows": M, "remote_rows": remote, "padded_rows": m_pad,
+               "algorithmic_tflop": round(flops / 1e12, 4),
+               "step_ms": {gname[f]: {mname[m]: round(t_step[(f, m)] * 1e3, 4) for m in modes} for f in gathers},
+               "sequential_ms": round(t_seq * 1e3, 4),
+               "speedup_vs_sequential": round(t_seq / t_best, 4),
+               "best_form": {"overlap_mode": mname[b_mode], "gather": gname[b_fused]},
+               "consumer_cus": c_used, "consumer_cus_model": c_model,
+               "predicted_expert_phase_ms": round(pred * 1e3, 4), "mgb": mgb_used}
+    for fused in gathers:
+        s = ph[(fused, MOE_MODE_SEQUENTIAL)]
+        seq_copy, seq_g2 = s["exposed"], s["producer"]
+        d = {"sequential": {"expert_phase_ms": round(s["total"], 4), "gemm1_ms": round(s["gemm1"], 4),
+                            "gemm2_ms": round(seq_g2, 4), "bulk_copy_us": round(seq_copy * 1e3, 2)}}
+        for mode in modes:
+            if mode == MOE_MODE_SEQUENTIAL:
+                continue
+            p = ph[(fused, mode)]
+            launch, exposed = p["producer"], p["exposed"]
+            d[mname[mode]] = {
+                "expert_phase_ms": round(p["total"], 4), "gemm1_ms": round(p["gemm1"], 4),
+                "output_projection_launch_ms": round(launch, 4),
+                # the copy's end after the producer's end (device clock stamps of the launch)
+                "exposed_copy_us": round(exposed * 1e3, 2),
+                "exposed_copy_fraction": round(exposed / seq_copy, 4) if seq_copy > 0 else None,
+                # the launch against the GEMM alone: what overlapping the copy cost the layer
+                "launch_minus_gemm2_us": round((launch - seq_g2) * 1e3, 2),
+                "launch_excess_fraction_of_bulk_copy": (round((launch - seq_g2) / seq_copy, 4)
+                                                        if seq_copy > 0 else None),
+                "launch_vs_gemm2_plus_bulk_copy": round(launch / (seq_g2 + seq_copy), 4)}
+            if mode == MOE_MODE_OVERLAP:
+                d[mname[mode]]["consumer_cus"] = c_used
+        layer_d["gather_" + gname[fused]] = d
+        log(f"[bench] {w.name} gather {gname[fused]}: " + json.dumps(d))
+    if not args.sequential_only:
+        layer_d["pct_mfma_peak_layer"] = round(100 * flops / t_best / 1e12 / PEAK_BF16_TFLOPS, 2)
+    roofline = {"kernel": "k_gemm first projection (x W1^T, x W3^T, SiLU gate)" +
+                          (", rows gathered from x" if b_fused else ""),
+                "bound": "mfma", "achieved": round(ach1, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach1 / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "traffic_unit": "bytes per launch",
+                "algorithmic_bytes": gemm1_bytes[b_fused],
+                "traffic_over_algorithmic": round(traffic / gemm1_bytes[b_fused], 3) if traffic else None,
+                "launch_ms": round(g1, 4), "algorithmic_flop_per_launch": flops1,
+                # hardware counters of the same kernel (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE):
+                # the clock it runs at under load and the share of those cycles the matrix
+                # cores are busy; frac_at_running_clock prices achieved against that clock
+                "mfma_busy_pmc": mfma[0] if mfma else None,
+                "clock_ghz_pmc": mfma[1] if mfma else None,
+                "frac_at_running_clock": (round(ach1 / (PEAK_BF16_TFLOPS * mfma[1] / 2.4), 4) if mfma else None)}
+    out = {"workload": w.name, "layer": layer, "tb_m": tb,
+           "value_tflops": round(flops / t_best / 1e12, 3), "ms_per_step": round(t_best * 1e3, 4),
+           "layer_detail": layer_d, "hbm_kernels": hbm, "roofline": roofline,
+           "config": {"workload": w.name, "layer": layer, "R": w.R, "T": w.T, "H": w.H, "F": w.F,
+                      "E": w.E, "k": w.k, "r_self": r_self, "tb_m": tb, "overlap_mode": mname[b_mode],
+                      "gather": gname[b_fused], "consumer_cus": c_used, "mgb": mgb_used,
+                      "parallelism": "one EP rank share on one GPU"}}
+    if args.c_sweep:
+        sh.fused_gather = b_fused
+        sh.permute()
+        out["c_sweep"] = c_sweep(sh, [int(c) for c in args.c_sweep.split(",")],
+                                 (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
+    if headline and args.timeline:
+        sh.fused_gather = b_fused
+        sh.permute()
+        timeline(sh, torch, args.timeline, w.name, MOE_MODE_OVERLAP)
+    if w.layers > 1 and not args.no_layer_sweep and not args.sequential_only:
+        log(f"[bench] {w.name}: layer sweep (gather {gname[b_fused]})")
+        sh.fused_gather = b_fused
+        out["layer_sweep"] = layer_sweep(sh, w, make_logits, torch, ops,
+                                         (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
+        log(f"[bench] {w.name}: layer sweep totals " + json.dumps(out["layer_sweep"]["total_ms"]))
+    del sh
+    torch.cuda.empty_cache()
+    if want_cpu:
+        log(f"[bench] {w.name}: timing the CPU oracle on the whole workload")
+        out["cpu_baseline"] = cpu_baseline(w, inp, tb, layer)
+        log(f"[bench] {w.name}: CPU oracle {json.dumps(out['cpu_baseline'])}")
+    return out
 
 
 # Table 2 of the tile-signalling paper: shape grid of its overlap-vs-baseline
@@ -269,17 +536,18 @@ def table2_sweep(args, torch, reps=5):
     from combine_overlap_amd.share import MoEShare
     dev = torch.device("cuda:0")
     R, K, topk, tb = 4, 2048, 2, 64
-    Ns = (8192, 4096)
+    Ns, Es, tprs = ((8192,), (4, 16, 64), (16384,)) if args.table2_subset else \
+        ((8192, 4096), (4, 8, 16, 32, 64), (8192, 16384))
     rows = []
     for N in Ns:
-        for E_l in (4, 8, 16, 32, 64):
+        for E_l in Es:
             # activations and weights from a seeded device generator (timing only:
             # no oracle reads them); std 0.02 as for the other small-std workloads
             gen = torch.Generator(device=dev)
             gen.manual_seed(2000 + N + E_l)
             w1 = (torch.randn((E_l, K, N), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
             w2 = (torch.randn((E_l, N, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-            for tpr in (8192, 16384):
+            for tpr in tprs:
                 x = torch.randn((R, tpr, N), generator=gen, device=dev).to(torch.bfloat16)
                 for skew, routing, zs in TABLE2_SKEWS:
                     w = Workload(f"table2_{skew}_tpr{tpr}_n{N}_e{E_l}", R, tpr, N, K, R * E_l, topk, False,
@@ -314,13 +582,8 @@ def table2_sweep(args, torch, reps=5):
                     sh.ctx.set_timing(True)
 
                     def phase(mode, c):   # (operator = output projection + transfer, expert phase, exposed)
-                        d = []
-                        for i in range(reps + 2):
-                            sh.expert_forward(mode, n_consumer_cu=c)
-                            if i >= 2:
-                                d.append(sh.ctx.timings())
-                        return tuple(float(np.median([t[k] for t in d]))
-                                     for k in ("producer_start_to_consumer_end", "total", "exposed"))
+                        t = phase_times(sh, mode, c, reps)
+                        return (t["producer_start_to_consumer_end"], t["total"], t["exposed"])
                     seq = phase(MOE_MODE_SEQUENTIAL, MOE_CONSUMER_AUTO)
                     rs = phase(MOE_MODE_ROLE_SWITCH, MOE_CONSUMER_AUTO)
                     by_c = {c: phase(MOE_MODE_OVERLAP, c) for c in (8, 16, 24, 32, 40, 48)}
@@ -341,6 +604,9 @@ def table2_sweep(args, torch, reps=5):
                                            "role_switch": round(rs[0], 4)},
                            "expert_phase_ms": {"sequential": round(seq[1], 4), "cu_partition": round(ovl[1], 4),
                                                "role_switch": round(rs[1], 4)},
+                           "exposed_us": {"cu_partition": round(ovl[2] * 1e3, 2),
+                                          "role_switch": round(rs[2] * 1e3, 2),
+                                          "bulk_copy": round(seq[2] * 1e3, 2)},
                            "operator_ms_by_c": {str(c): round(v[0], 4) for c, v in by_c.items()},
                            "layer_ms": {k: round(v, 4) for k, v in layer.items()},
                            "operator_speedup": round(seq[0] / ovl[0], 4),
@@ -361,213 +627,48 @@ def table2_sweep(args, torch, reps=5):
             "configs": rows}
 
 
-def main():
-    args = parse()
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (this build runs on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     import torch
-    from synth import WORKLOADS, make_logits, make_x, make_local_weights
-    from synth.workloads import ShareInputs
-    from combine_overlap_amd import MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL
-    from combine_overlap_amd.share import MoEShare, bf16_tensor
-    from combine_overlap_amd import ops
-
-    w = WORKLOADS[args.config]
-    tb = args.tb or DEFAULT_TB[args.config]
-    r_self = 0
-    log(f"[bench] workload {w.name} layer {args.layer} tb_m={tb}: generating inputs")
-    W1, W3, W2 = make_local_weights(w, r_self)
-    inp = ShareInputs(w, r_self, make_logits(w, args.layer), make_x(w), W1, W3, W2)
-    dev = torch.device("cuda:0")
-    sh = MoEShare(w.R, w.T, w.H, w.F, w.E, w.k, w.gated, w.gate_kind, r_self=r_self, tb_m=tb,
-                  device=dev)
-    sh.allocate(torch.from_numpy(inp.logits).to(dev), bf16_tensor(inp.x, dev), bf16_tensor(W1, dev),
-                bf16_tensor(W3, dev) if W3 is not None else None, bf16_tensor(W2, dev))
-    torch.cuda.synchronize()
-    n_cu = sh.ctx.num_cus
-    log(f"[bench] device CUs {n_cu}; buffers ready")
-
-    def step(mode):
-        sh.layer(mode, n_consumer_cu=args.c or None)
-
-    gathers = {"both": (False, True), "materialized": (False,), "fused": (True,)}[args.gather]
-    sh.fused_gather = gathers[0]
-    main_mode = MOE_MODE_SEQUENTIAL if args.sequential_only else MOE_MODE_OVERLAP
-    # warmup + sanity
-    for _ in range(max(1, args.warmup)):
-        step(main_mode)
-    torch.cuda.synchronize()
-    if sh.status() != 0:
-        raise RuntimeError(f"device status {sh.status()} after warmup")
-    # consumer CUs: the plan kernel's choice (no host round trip in the step)
-    c_used = args.c or sh.auto_consumer_cu()[0]
-    mgb_used = sh.shape.mgb
-    counts = sh.buf.counts.cpu().numpy()
-    M = int(counts.sum())
-    remote = int(counts.sum() - counts[:, r_self].sum())
-    per_row = (6 if w.gated else 4) * w.H * w.F
-    flops = float(per_row) * M
-    flops1 = float((4 if w.gated else 2) * w.H * w.F) * M
-    plan = sh.plan_arrays()
-    m_pad = plan["m_pad"]
-    # compulsory HBM bytes of the first-projection GEMM: its A rows (x_perm, or
-    # the valid rows of x when gathered: padding reads one cached zero row),
-    # W1 (+W3) of the experts that received rows, h
-    n_w = (2 if w.gated else 1) * int((counts.sum(axis=1) > 0).sum())
-    gemm1_bytes = {False: 2 * (m_pad * w.H + n_w * w.F * w.H + m_pad * w.F),
-                   True: 2 * (M * w.H + n_w * w.F * w.H + m_pad * w.F)}
-    log(f"[bench] valid rows {M}, remote rows {remote}, padded rows {m_pad}, bands {plan['n_bands']}, "
-        f"segments {plan['n_seg']}, c={c_used}, mgb={mgb_used}")
-    log(f"[bench] first-projection algorithmic bytes: materialized {gemm1_bytes[False]}, "
-        f"fused {gemm1_bytes[True]}")
-
-    def timed(mode, k):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(k):
-            step(mode)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / k
-
-    modes = ((MOE_MODE_SEQUENTIAL,) if args.sequential_only else
-             (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
-    mname = {MOE_MODE_OVERLAP: "cu_partition", MOE_MODE_ROLE_SWITCH: "role_switch",
-             MOE_MODE_SEQUENTIAL: "sequential"}
-    gname = {False: "materialized", True: "fused"}
-    t_step = {}
-    for fused in gathers:
-        sh.fused_gather = fused
-        for mode in modes:
-            for _ in range(args.warmup):
-                step(mode)
-            t_step[(fused, mode)] = timed(mode, args.steps)
-            log(f"[bench] gather {gname[fused]}, {mname[mode]}: layer step "
-                f"{t_step[(fused, mode)] * 1e3:.3f} ms")
-
-    # per-phase device timings (HIP events on the kernels' own streams)
-    sh.ctx.set_timing(True)
-    ph = {}
-    for fused in gathers:
-        sh.fused_gather = fused
-        sh.permute()
-        for mode in modes:
-            ph[(fused, mode)] = []
-            for _ in range(max(3, args.steps)):
-                sh.expert_forward(mode, n_consumer_cu=c_used)
-                ph[(fused, mode)].append(sh.ctx.timings())
-    sh.ctx.set_timing(False)
-    torch.cuda.synchronize()
-    if sh.status() != 0:
-        raise RuntimeError(f"device status {sh.status()} after the timed runs")
-
-    def med(fused, mode, key):
-        return float(np.median([d[key] for d in ph[(fused, mode)]]))
-    for fused in gathers:
-        log(f"[bench] gather {gname[fused]}, sequential: gemm1 {med(fused, MOE_MODE_SEQUENTIAL, 'gemm1'):.3f} ms, "
-            f"gemm2 {med(fused, MOE_MODE_SEQUENTIAL, 'producer'):.3f} ms, bulk copy "
-            f"{med(fused, MOE_MODE_SEQUENTIAL, 'exposed') * 1e3:.1f} us, expert phase "
-            f"{med(fused, MOE_MODE_SEQUENTIAL, 'total'):.3f} ms")
-        if not args.sequential_only:
-            log(f"[bench] gather {gname[fused]}, overlap: gemm1 {med(fused, MOE_MODE_OVERLAP, 'gemm1'):.3f} ms, "
-                f"output projection + consumer {med(fused, MOE_MODE_OVERLAP, 'producer'):.3f} ms, expert phase "
-                f"{med(fused, MOE_MODE_OVERLAP, 'total'):.3f} ms, exposed copy "
-                f"{med(fused, MOE_MODE_OVERLAP, 'exposed') * 1e3:.1f} us; role switch: expert phase "
-                f"{med(fused, MOE_MODE_ROLE_SWITCH, 'total'):.3f} ms")
-    overlapped = [k for k in t_step if k[1] != MOE_MODE_SEQUENTIAL] or list(t_step)
-    best = min(overlapped, key=t_step.get)
-    b_fused, b_mode = best
-    t_best = t_step[best]
-    t_seq = t_step[(b_fused, MOE_MODE_SEQUENTIAL)]
-    g1 = med(b_fused, b_mode, "gemm1")
-    ach1 = flops1 / (g1 * 1e-3) / 1e12
-    traffic = stored_traffic(w.name, tb, b_fused)
-    mfma = stored_mfma(w.name, tb, b_fused)
-
-    hbm = hbm_phases(sh, w, torch, M, m_pad, remote, med(b_fused, MOE_MODE_SEQUENTIAL, "exposed"))
-    log("[bench] HBM-bound steps: " + ", ".join(f"{k} {v['us']:.1f} us {v['GB/s']:.0f} GB/s ({v['frac']:.2f})"
-                                                for k, v in hbm.items()))
-    layer = {
-        "valid_rows": M, "remote_rows": remote, "padded_rows": m_pad,
-        "algorithmic_tflop": round(flops / 1e12, 4),
-        "step_ms": {gname[f]: {mname[m]: round(t_step[(f, m)] * 1e3, 4) for m in modes} for f in gathers},
-        "sequential_ms": round(t_seq * 1e3, 4),
-        "speedup_vs_sequential": round(t_seq / t_best, 4),
-        "gemm1_ms": round(g1, 4),
-    }
-    for fused in gathers:
-        seq_copy = med(fused, MOE_MODE_SEQUENTIAL, "exposed")
-        d = {"sequential": {"expert_phase_ms": round(med(fused, MOE_MODE_SEQUENTIAL, "total"), 4),
-                            "gemm1_ms": round(med(fused, MOE_MODE_SEQUENTIAL, "gemm1"), 4),
-                            "gemm2_ms": round(med(fused, MOE_MODE_SEQUENTIAL, "producer"), 4),
-                            "bulk_copy_us": round(seq_copy * 1e3, 2)}}
-        if not args.sequential_only:
-            # one launch holds both roles: the producer ends where the exposed copy begins
-            launch = med(fused, MOE_MODE_OVERLAP, "producer")
-            exposed = med(fused, MOE_MODE_OVERLAP, "exposed")
-            prod = launch - exposed
-            d["cu_partition"] = {
-                "consumer_cus": c_used, "expert_phase_ms": round(med(fused, MOE_MODE_OVERLAP, "total"), 4),
-                "gemm1_ms": round(med(fused, MOE_MODE_OVERLAP, "gemm1"), 4),
-                "output_projection_launch_ms": round(launch, 4),
-                "producer_ms": round(prod, 4),
-                "producer_tflops": round(float(2 * w.H * w.F * M) / (prod * 1e-3) / 1e12, 2),
-                "exposed_copy_us": round(exposed * 1e3, 2),
-                "exposed_copy_fraction": round(exposed / seq_copy, 4) if seq_copy > 0 else None}
-            d["role_switch"] = {"expert_phase_ms": round(med(fused, MOE_MODE_ROLE_SWITCH, "total"), 4),
-                                "gemm2_and_copy_ms": round(med(fused, MOE_MODE_ROLE_SWITCH, "producer"), 4)}
-        layer["gather_" + gname[fused]] = d
-    if not args.sequential_only:
-        layer["pct_mfma_peak_layer"] = round(100 * flops / t_best / 1e12 / PEAK_BF16_TFLOPS, 2)
+    ids = [args.config] if args.config else [int(c) for c in args.configs.split(",") if c.strip()]
+    head = HEADLINE if HEADLINE in ids else ids[0]
+    results = {}
+    for wid in ids:
+        results[wid] = bench_workload(wid, args, torch, want_cpu=not args.no_cpu_baseline,
+                                      headline=wid == head)
+    h = results[head]
     out = {
         "metric": "MoE-layer time/TFLOP/s per EP rank (overlap vs non-overlap), % MFMA peak",
-        "value": round(flops / t_best / 1e12, 3),
+        "value": h["value_tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(t_best * 1e3, 4),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; random-init expert weights)",
-        "config": {"workload": w.name, "layer": args.layer, "R": w.R, "T": w.T, "H": w.H, "F": w.F,
-                   "E": w.E, "k": w.k, "r_self": r_self, "tb_m": tb, "overlap_mode": mname[b_mode],
-                   "gather": gname[b_fused],
-                   "consumer_cus": c_used, "mgb": mgb_used,
-                   "parallelism": "one EP rank share on one GPU"},
-        "layer": layer,
-        "hbm_kernels": hbm,
-        "roofline": {"kernel": "k_gemm first projection (x W1^T, x W3^T, SiLU gate)" +
-                     (", rows gathered from x" if b_fused else ""),
-                     "bound": "mfma", "achieved": round(ach1, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ach1 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "traffic_unit": "bytes per launch",
-                     "algorithmic_bytes": gemm1_bytes[b_fused], "launch_ms": round(g1, 4),
-                     # hardware counters of the same kernel (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE):
-                     # the clock it runs at under load and the share of those cycles the matrix
-                     # cores are busy; frac_at_running_clock prices achieved against that clock
-                     "mfma_busy_pmc": mfma[0] if mfma else None,
-                     "clock_ghz_pmc": mfma[1] if mfma else None,
-                     "frac_at_running_clock": (round(ach1 / (PEAK_BF16_TFLOPS * mfma[1] / 2.4), 4)
-                                               if mfma else None)},
+        "config": h["config"],
+        "layer": h["layer_detail"],
+        "hbm_kernels": h["hbm_kernels"],
+        "roofline": h["roofline"],
     }
-    if args.layer_sweep and w.layers > 1:
-        log(f"[bench] layer sweep (gather {gname[b_fused]})")
-        sh.fused_gather = b_fused
-        out["layer_sweep"] = layer_sweep(sh, w, make_logits, torch, ops,
-                                         (MOE_MODE_OVERLAP, MOE_MODE_ROLE_SWITCH, MOE_MODE_SEQUENTIAL))
-        log("[bench] layer sweep totals " + json.dumps(out["layer_sweep"]["total_ms"]))
+    if "cpu_baseline" in h:
+        out["cpu_baseline"] = h["cpu_baseline"]
+    for k in ("c_sweep", "layer_sweep"):
+        if k in h:
+            out[k] = h[k]
+    out["configs"] = {results[w]["workload"]: {k: v for k, v in results[w].items() if k != "workload"}
+                      for w in ids if w != head}
     if args.table2_sweep:
         log("[bench] Table-2 sweep")
-        del sh
-        torch.cuda.empty_cache()
         out["table2_sweep"] = table2_sweep(args, torch)
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(w, inp, tb, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -61,7 +61,8 @@ class MoeCalib(C.Structure):
 
 
 EXPORTS = ("moe_error_string", "moe_query_sizes", "moe_plan_view", "moe_ctx_create",
-           "moe_ctx_destroy", "moe_ctx_num_cus", "moe_ctx_set_wait_limit", "moe_ctx_set_timing", "moe_ctx_timings", "moe_ctx_set_trace", "moe_route", "moe_permute",
+           "moe_ctx_destroy", "moe_ctx_num_cus", "moe_ctx_set_wait_limit", "moe_ctx_set_debug",
+           "moe_ctx_set_timing", "moe_ctx_timings", "moe_ctx_set_trace", "moe_route", "moe_permute",
            "moe_plan_partition", "moe_expert_forward_overlap", "moe_expert_forward_gathered",
            "moe_combine", "moe_read_status")
 
@@ -86,6 +87,7 @@ def lib() -> C.CDLL:
     L.moe_ctx_destroy.argtypes = [vp]
     L.moe_ctx_num_cus.argtypes = [vp]
     L.moe_ctx_set_wait_limit.argtypes = [vp, C.c_uint64]
+    L.moe_ctx_set_debug.argtypes = [vp, u32, i32, C.c_int64]
     L.moe_ctx_set_timing.argtypes = [vp, C.c_int]
     L.moe_ctx_timings.argtypes = [vp, C.POINTER(C.c_float)]
     L.moe_ctx_set_trace.argtypes = [vp, pshape, vp, C.c_int64]

@@ -16,6 +16,7 @@ struct moe_ctx {
   int32_t trace_flags;      // max_flags of the shape the trace was sized for
   const int32_t* timed_meta;   // workspace meta words of the last timed call (device stamps)
   uint64_t wait_ticks;      // bound on each wait for a ready flag (100 MHz ticks)
+  moe::GemmKnobs knobs;     // test knobs of the GEMM launches (moe_ctx_set_debug)
 };
 
 namespace moe {
@@ -66,8 +67,11 @@ int make_geometry(const moe_shape_t* s, Geometry* g) {
   if (flags >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   g->max_flags = (int32_t)flags;
   g->recv_rows_max = (int32_t)((int64_t)s->T * (s->k < El ? s->k : El));
-  // the consumer addresses a segment's 16-byte words with 32-bit offsets
+  // the consumer addresses a segment's 16-byte words with 32-bit offsets, and
+  // the copying roles read a segment (at most mgb bands) through a buffer
+  // resource with 32-bit byte offsets
   if ((int64_t)g->recv_rows_max * (s->H / 8) >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)s->mgb * s->tb_m * s->H * 2 >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -192,6 +196,7 @@ int moe_ctx_create(moe_ctx_t** out) {
   c->trace = nullptr;
   c->trace_flags = 0;
   c->wait_ticks = moe::kDefaultWaitTicks;
+  c->knobs = moe::GemmKnobs{0u, 0, moe::kDefaultTailWaitTicks};
   if (hipGetDevice(&c->device) != hipSuccess ||
       hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device) != hipSuccess) {
     delete c;
@@ -233,13 +238,14 @@ int moe_ctx_timings(moe_ctx_t* ctx, float* ms) {
   ms[2] = t13;
   ms[3] = t04;
   ms[4] = t23 > 0.f ? t23 : 0.f;
-  if (ctx->timed_mode == MOE_MODE_OVERLAP) {
+  if (ctx->timed_mode == MOE_MODE_OVERLAP || ctx->timed_mode == MOE_MODE_ROLE_SWITCH) {
     // one launch holds both roles: the exposed transfer comes from its device
-    // clock stamps (100 MHz) of the last producer exit and consumer completion
+    // clock stamps (100 MHz) of the last tile's completion and the last copy's
     uint64_t st[2];
     if (hipMemcpy(st, ctx->timed_meta + META_T_PROD, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess)
       return MOE_ERR_HIP;
-    // st[0] stays 0 when no workgroup ran a tile (an empty layout)
+    // st[0] stays 0 when no workgroup ran a tile (an empty layout), st[1]
+    // when nothing was copied
     ms[4] = st[0] != 0 && st[1] > st[0] ? (float)((double)(st[1] - st[0]) * 1e-5) : 0.f;
   }
   return MOE_OK;
@@ -272,6 +278,14 @@ int moe_ctx_num_cus(const moe_ctx_t* ctx) { return ctx ? ctx->n_cu : MOE_ERR_INV
 int moe_ctx_set_wait_limit(moe_ctx_t* ctx, uint64_t ticks) {
   if (ctx == nullptr) return MOE_ERR_INVALID_ARG;
   ctx->wait_ticks = ticks == 0 ? moe::kDefaultWaitTicks : ticks;
+  return MOE_OK;
+}
+
+int moe_ctx_set_debug(moe_ctx_t* ctx, uint32_t delay_seed, int32_t reverse_schedule, int64_t tail_wait_ticks) {
+  if (ctx == nullptr || (reverse_schedule != 0 && reverse_schedule != 1)) return MOE_ERR_INVALID_ARG;
+  ctx->knobs.delay_seed = delay_seed;
+  ctx->knobs.reverse = reverse_schedule;
+  ctx->knobs.tail_wait_ticks = tail_wait_ticks < 0 ? moe::kDefaultTailWaitTicks : (uint64_t)tail_wait_ticks;
   return MOE_OK;
 }
 
@@ -351,14 +365,15 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   auto rec = [&](int i, hipStream_t st) { return tm ? hip_rc(hipEventRecord(ctx->tev[i], st)) : MOE_OK; };
   if ((rc = rec(0, ps)) != MOE_OK) return rc;
   if ((rc = hip_rc(launch_gemm1(g, a, gathered ? p.row_src : nullptr, gathered ? zero_row_of(g, ws) : nullptr,
-                                w1, w3, h, p, mode == MOE_MODE_SEQUENTIAL ? nullptr : flags, ncu, ps))) !=
+                                w1, w3, h, p, mode == MOE_MODE_SEQUENTIAL ? nullptr : flags, ncu, ctx->knobs,
+                                ps))) !=
       MOE_OK)
     return rc;
   if ((rc = rec(1, ps)) != MOE_OK) return rc;
   if (mode == MOE_MODE_SEQUENTIAL) {
     if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, nullptr, 0, ctx->trace, ncu,
                                   auto_c ? 0 : ncu - n_consumer_cu, nullptr, 0, nullptr, ctx->wait_ticks,
-                                  ps))) != MOE_OK)
+                                  ctx->knobs, ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
     if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 4 * ncu, ps))) != MOE_OK) return rc;
@@ -371,11 +386,12 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   if (mode == MOE_MODE_ROLE_SWITCH) {
     // one launch on every CU does both duties; the split is sized for all CUs
     if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu, ncu, &bufs, 0, nullptr,
-                                  ctx->wait_ticks, ps))) != MOE_OK)
+                                  ctx->wait_ticks, ctx->knobs, ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
     if ((rc = rec(3, ps)) != MOE_OK) return rc;
     if ((rc = rec(4, ps)) != MOE_OK) return rc;
+    ctx->timed_meta = p.meta;
     ctx->timed = tm;
     ctx->timed_mode = mode;
     return MOE_OK;
@@ -383,7 +399,7 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   // CU partition: one launch on every CU, workgroups [0, c) the consumer
   if ((rc = hip_rc(launch_gemm2(g, h, w2, y_perm, p, flags, epoch, ctx->trace, ncu,
                                 auto_c ? 0 : ncu - n_consumer_cu, nullptr, auto_c ? -1 : n_consumer_cu, &bufs,
-                                ctx->wait_ticks, ps))) != MOE_OK)
+                                ctx->wait_ticks, ctx->knobs, ps))) != MOE_OK)
     return rc;
   if ((rc = rec(2, ps)) != MOE_OK) return rc;
   if ((rc = rec(3, ps)) != MOE_OK) return rc;

@@ -45,6 +45,10 @@ constexpr int kTailSlots = kCtrStride - 1;
 // bound on every wait for a ready flag, in ticks of the 100 MHz constant
 // clock, unless the context sets another (moe_ctx_set_wait_limit)
 constexpr uint64_t kDefaultWaitTicks = 200000000ull;   // 2 s
+// bound on a split tail chunk's wait for the other chunks of its tile in the
+// output projection (100 MHz ticks); past it the chunk leaves its share to
+// the last chunk to arrive
+constexpr uint64_t kDefaultTailWaitTicks = 100000ull;   // 1 ms
 
 struct Geometry {
   int32_t R, T, H, F, E, k, r_self, gated, gate_kind, tb_m, mgb;
@@ -86,15 +90,32 @@ struct BufPtrs { uint16_t* p[MOE_MAX_RANKS]; };
 
 #define GLOBAL_AS __attribute__((address_space(1)))
 
-// 16-byte load of rows another workgroup published with device-scope
-// write-through stores: device-scope (sc1) loads, two 8-byte halves, which
-// miss in this XCD's L2 unless the line is coherent. (Explicit global address
-// space: generic "flat" atomics would each wait for all earlier accesses.)
-__device__ __forceinline__ u32x4 load16_device(const u32x4* a) {
-  const GLOBAL_AS uint64_t* s64 = (const GLOBAL_AS uint64_t*)a;
-  const uint64_t x = __hip_atomic_load(s64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t y = __hip_atomic_load(s64 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return u32x4{(uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32)};
+// A raw buffer resource over `bytes` bytes at p (p wave-uniform; the words are
+// taken from the first lane so they sit in scalar registers). 16-byte loads and
+// stores through it take a per-lane 32-bit byte offset; loads at or past
+// `bytes` return zeros and stores there are dropped, without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
+// cache policy of a buffer access: sc1 = device scope. A device-scope store
+// writes through this XCD's L2 to the device's coherence point; a
+// device-scope load misses in this XCD's L2 unless the line is coherent, so
+// it sees rows another XCD published that way.
+constexpr int kCpolDevice = 16;
+
+// 16-byte load of rows another workgroup published with device-scope stores
+__device__ __forceinline__ u32x4 load16_device(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCpolDevice);
+}
+
+// 16-byte device-scope store (publication of a tile's rows)
+__device__ __forceinline__ void store16_device(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, kCpolDevice);
 }
 
 __device__ __forceinline__ void store16_nt(u32x4* a, u32x4 v) {
@@ -115,9 +136,20 @@ hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* id
 // a_rows null: A = x_perm (packed rows); else A = x and packed row r reads x row
 // a_rows[r] (a_zero for padding), the gather fused into the tile loads.
 // flags (may be null): the output projection's ready flags, cleared here
+// Test knobs of the GEMM launches (timing only, never the results):
+// delay_seed != 0 delays each work item by a seeded number of sleeps before
+// its stores; reverse walks the tile queues in reverse schedule order;
+// tail_wait_ticks bounds how long a split tail chunk of the output projection
+// waits for its tile's other chunks (past it the last chunk to arrive
+// reduces its share).
+struct GemmKnobs {
+  uint32_t delay_seed;
+  int reverse;
+  uint64_t tail_wait_ticks;
+};
 hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t* a_rows,
                         const uint16_t* a_zero, const uint16_t* w1, const uint16_t* w3, uint16_t* h,
-                        const moe_plan_t& p, uint32_t* flags, int grid, hipStream_t st);
+                        const moe_plan_t& p, uint32_t* flags, int grid, const GemmKnobs& kn, hipStream_t st);
 // split_grid: the producer grid the K-split tail is sized for (the overlapped
 // run's n_cu - c in both modes, so that both compute identical bits)
 // copy_bufs: non-null gives the launch the consumer's duty as well (role
@@ -130,7 +162,7 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t*
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
                         int grid, int split_grid, const BufPtrs* copy_bufs, int n_cons,
-                        const BufPtrs* cons_bufs, uint64_t wait_ticks, hipStream_t st);
+                        const BufPtrs* cons_bufs, uint64_t wait_ticks, const GemmKnobs& kn, hipStream_t st);
 hipError_t launch_bulk_copy(const Geometry& g, const uint16_t* y, BufPtrs bufs,
                             const moe_plan_t& p, int grid, hipStream_t st);
 hipError_t launch_combine(const Geometry& g, BufPtrs bufs, const uint16_t* y, const float* gates,

@@ -9,8 +9,9 @@
 // (consecutive segments mostly share row tiles, which are polled once).
 // Workgroups therefore never wait for one another; each keeps ROUND 16-byte
 // loads per thread in flight. Flags and rows are read with device-scope
-// loads, which pair with the producer's device-scope stores and completion
-// wait; no L2 invalidate is issued per segment.
+// loads (rows: 16-byte buffer loads with the sc1 policy), which pair with
+// the producer's device-scope stores and completion wait; no L2 invalidate
+// is issued per segment.
 //
 // Every wait is bounded: after wait_ticks of the 100 MHz constant clock the
 // device status word becomes MOE_ERR_TIMEOUT and the workgroup returns.
@@ -136,48 +137,45 @@ __device__ void consume(const ConsumerArgs& c, int wg, int nwg, int* s_tab, int*
     __syncthreads();
     if (*s_abort) return;
     if (!MOE_DEVICE_SCOPE_PUBLISH) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // the batch's units (a missing unit reads row 0 of y and stores nothing)
-    const u32x4* src[BATCH];
+    // the batch's units: a buffer resource over each unit's source bytes (a
+    // missing unit has none: its loads return zeros and nothing is stored)
+    __amdgpu_buffer_rsrc_t src[BATCH];
     u32x4* dst[BATCH];
-    uint32_t lo[BATCH], hi[BATCH], last_ld[BATCH];   // 16-byte words in the segment
+    uint32_t n16[BATCH];   // 16-byte words of the unit
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
       const int u = u0 + k;
-      src[k] = reinterpret_cast<const u32x4*>(c.y);
+      const uint16_t* sp = c.y;
       dst[k] = reinterpret_cast<u32x4*>(c.bufs.p[0]);
-      lo[k] = 0;
-      hi[k] = 0;
-      last_ld[k] = 0;
+      n16[k] = 0;
       if (u < u1) {
         while (seg + 1 < n_seg && unit0(seg + 1) <= u) ++seg;
         const uint32_t words = (uint32_t)field(t_rows, c.seg_rows, seg) * (uint32_t)(H / 8);
-        lo[k] = (uint32_t)(u - unit0(seg)) * (uint32_t)kUnit16;
-        hi[k] = lo[k] + (uint32_t)kUnit16 < words ? lo[k] + (uint32_t)kUnit16 : words;
-        last_ld[k] = hi[k] - 1;
-        src[k] = reinterpret_cast<const u32x4*>(c.y + (size_t)field(t_src, c.seg_src_row, seg) * H);
+        const uint32_t lo = (uint32_t)(u - unit0(seg)) * (uint32_t)kUnit16;
+        n16[k] = lo + (uint32_t)kUnit16 < words ? (uint32_t)kUnit16 : words - lo;
+        sp = c.y + (size_t)field(t_src, c.seg_src_row, seg) * H + (size_t)lo * 8;
         dst[k] = reinterpret_cast<u32x4*>(c.bufs.p[field(t_dest, c.seg_dest, seg)] +
-                                          (size_t)field(t_dst, c.seg_dst_row, seg) * H);
+                                          (size_t)field(t_dst, c.seg_dst_row, seg) * H) + lo;
       }
+      src[k] = buf_rsrc(sp, n16[k] * 16u);
     }
-    // rounds of ROUND loads per thread: the loads are unconditional (indices
-    // clamped into the unit) so the compiler keeps them all in flight; only
-    // the stores are predicated
+    // rounds of ROUND loads per thread, all in flight before the stores;
+    // only the stores are predicated
 #pragma unroll
     for (int z0 = 0; z0 < kSlots; z0 += ROUND) {
       u32x4 v[ROUND];
 #pragma unroll
       for (int z = 0; z < ROUND; ++z) {
         const int k = (z0 + z) / kPer, q = (z0 + z) % kPer;
-        const uint32_t i = lo[k] + (uint32_t)(q * NT + tid);
-        const u32x4* a = src[k] + (i < last_ld[k] ? i : last_ld[k]);
-        if constexpr (MOE_DEVICE_SCOPE_PUBLISH) v[z] = load16_device(a);
-        else v[z] = *(const GLOBAL_AS u32x4*)a;
+        const uint32_t i = (uint32_t)(q * NT + tid);
+        v[z] = __builtin_amdgcn_raw_buffer_load_b128(src[k], i * 16u, 0,
+                                                     MOE_DEVICE_SCOPE_PUBLISH ? kCpolDevice : 0);
       }
 #pragma unroll
       for (int z = 0; z < ROUND; ++z) {
         const int k = (z0 + z) / kPer, q = (z0 + z) % kPer;
-        const uint32_t i = lo[k] + (uint32_t)(q * NT + tid);
-        if (i < hi[k]) store16_nt(dst[k] + i, v[z]);
+        const uint32_t i = (uint32_t)(q * NT + tid);
+        if (i < n16[k]) store16_nt(dst[k] + i, v[z]);
       }
     }
     if (c.trace != nullptr && wg == 0) {

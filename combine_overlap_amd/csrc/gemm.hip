@@ -96,10 +96,16 @@ enum { EPI_PLAIN = 0, EPI_SILU = 1, EPI_GATED = 2 };
 // blocks, so up to one chunk per block.
 constexpr int kMaxSplitSerial = 4;
 constexpr int kMaxSplitShared = 8;
-constexpr int kMinSplitSteps = 8;
+constexpr int kMinSplitSteps = 8;   // k-steps per chunk at least
 // buffer offset of gathered padding rows: past any x a resource describes
 // (x must stay below 2 GiB for the buffer form, so offset + k offset < 2^32)
-constexpr uint32_t kBufOutOfRange = 0x80000000u;   // k-steps per chunk at least
+constexpr uint32_t kBufOutOfRange = 0x80000000u;
+// split tail tiles per XCD queue at most (tail * nsplit <= kTailSlots with
+// nsplit >= 2): word 1 + t of the queue's counter block counts tile t's
+// chunk arrivals and stored shares, word 1 + kTailTiles + t its claimed shares
+constexpr int kTailTiles = kTailSlots / 2;
+static_assert(1 + 2 * kTailTiles <= kCtrStride, "tail words fit the counter block");
+
 
 template <int BM, int BN, int BK, int NS, int WM, int WN>
 struct Tile {
@@ -168,6 +174,13 @@ struct GemmArgs {
   int gp, gq;                  // blocks of gp row tiles x gq column tiles inside an XCD queue
   int px;                      // workgroups per XCD queue the tail split is sized for;
                                // 0: (grid - meta[META_CAUTO]) / 8
+  uint64_t tail_wait_ticks;    // output projection: bound on a split tail chunk's wait for
+                               // its tile's other chunks (then the last to arrive takes its share)
+  // test knobs (timing only; the results do not change): a nonzero seed
+  // delays each work item by a seeded number of sleeps before its stores;
+  // reverse walks every queue's whole tiles in reverse schedule order
+  uint32_t dbg_seed;
+  int dbg_reverse;
 };
 
 // Queue index i of XCD x -> tile (row-tile schedule position * tiles_n + column tile).
@@ -216,13 +229,15 @@ __device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int x, i
   int s = tail > 0 ? px / tail : 1;
   s = min(s, min(max_split, nk / kMinSplitSteps));
   if (tail * s > kTailSlots) s = kTailSlots / tail;
+  // test knob: the whole tiles in reverse queue order (the split tail tiles
+  // stay the same tiles, so every tile is summed as without the knob)
   if (s < 2) {
-    if (i < T) it.tile = queue_tile(a, n_rt, x, i);
+    if (i < T) it.tile = queue_tile(a, n_rt, x, a.dbg_reverse ? T - 1 - i : i);
     return it;
   }
   const int full = T - tail;
   if (i < full) {
-    it.tile = queue_tile(a, n_rt, x, i);
+    it.tile = queue_tile(a, n_rt, x, a.dbg_reverse ? full - 1 - i : i);
     return it;
   }
   const int j = i - full;
@@ -309,27 +324,39 @@ __device__ __forceinline__ int xcc_id() {
 
 
 // Copies remote segment sg's valid rows (y rows published by other
-// workgroups) into its owner's combine buffer with all NT threads.
+// workgroups) into its owner's combine buffer with all NT threads: rounds of
+// kRound device-scope 16-byte loads per thread through a buffer resource
+// over the segment's bytes (loads past its end return zeros and are not
+// stored; a segment is below 2 GiB, which the host checks).
 template <int NT>
 __device__ __forceinline__ void copy_segment(const GemmArgs& a, int sg, int tid) {
   constexpr int kRound = 16;   // 16-byte loads per thread in flight
   const int H = a.Nout;
   const uint32_t words = (uint32_t)a.seg_rows[sg] * (uint32_t)(H / 8);
-  const u32x4* src = reinterpret_cast<const u32x4*>(a.C + (size_t)a.seg_src_row[sg] * H);
+  const uint16_t* src = a.C + (size_t)a.seg_src_row[sg] * H;
   u32x4* dst = reinterpret_cast<u32x4*>(a.bufs.p[a.seg_dest[sg]] + (size_t)a.seg_dst_row[sg] * H);
+  const __amdgpu_buffer_rsrc_t r = buf_rsrc(src, words * 16u);
   for (uint32_t w0 = 0; w0 < words; w0 += NT * kRound) {
     u32x4 v[kRound];
 #pragma unroll
-    for (int z = 0; z < kRound; ++z) {   // unconditional loads, index clamped into the segment
-      const uint32_t i = w0 + (uint32_t)(z * NT + tid);
-      v[z] = load16_device(src + (i < words ? i : words - 1));
-    }
+    for (int z = 0; z < kRound; ++z)
+      v[z] = __builtin_amdgcn_raw_buffer_load_b128(r, (w0 + (uint32_t)(z * NT + tid)) * 16u, 0,
+                                                   MOE_DEVICE_SCOPE_PUBLISH ? kCpolDevice : 0);
 #pragma unroll
     for (int z = 0; z < kRound; ++z) {
       const uint32_t i = w0 + (uint32_t)(z * NT + tid);
       if (i < words) store16_nt(dst + i, v[z]);
     }
   }
+}
+
+// device clock stamps of an overlapped output projection (100 MHz ticks),
+// cleared by the first projection: META_T_PROD the latest completion of a
+// tile, META_T_CONS the latest completion of a copy (consumer workgroups of
+// the CU partition, the copy duty of role switching)
+__device__ __forceinline__ void stamp_max(const int32_t* meta, int word) {
+  uint64_t* w = reinterpret_cast<uint64_t*>(const_cast<int32_t*>(meta) + word);
+  __hip_atomic_fetch_max(w, (uint64_t)wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The copy duty, segments in schedule order.
@@ -411,15 +438,11 @@ __device__ void copy_duty(const GemmArgs& a, bool wait, int tid, int* s_copy) {
     if (d0 < 0) return;
     if (!MOE_DEVICE_SCOPE_PUBLISH) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     for (int sg = d0; sg < d1; ++sg) copy_segment<NT>(a, sg, tid);
+    // these copies have completed: the latest such stamp is the transfer's end
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) stamp_max(a.meta, META_T_CONS);
   }
-}
-
-// device clock stamps of an overlapped output projection (100 MHz ticks),
-// cleared by the first projection: the last producer workgroup's exit and
-// the last consumer workgroup's completion
-__device__ __forceinline__ void stamp_max(const int32_t* meta, int word) {
-  uint64_t* w = reinterpret_cast<uint64_t*>(const_cast<int32_t*>(meta) + word);
-  __hip_atomic_fetch_max(w, (uint64_t)wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BM, int BN, int BK, int NS, int WM, int WN, int EPI, bool COPY = false, int GATHER = 0,
@@ -491,6 +514,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   }
 
   const int n_rt = a.meta[META_NTILES];   // row tiles, in schedule positions
+  const int n_rrt = a.meta[META_NRTILES];  // the first n_rrt of them hold a remote band
   const int m_pad = GATHER ? a.meta[META_MPAD] : 0;
   moe_i32x4 a_rsrc = {0, 0, 0, 0};
   if constexpr (GATHER == 2) {
@@ -502,7 +526,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     a_rsrc[3] = 0x00020000;   // 32-bit data format, no swizzle, no stride: byte-addressed raw buffer
   }
   int q = xcc_id(), tried = 0;
-  bool did_tile = false;   // the producer's end is the end of its last tile
   while (true) {
     if constexpr (COPY) copy_duty<C::NT>(a, false, tid, s_copy);
     if (tid == 0) {
@@ -522,10 +545,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     const int tile = s_item[0];
     if (tile < 0) {
       if constexpr (COPY) copy_duty<C::NT>(a, true, tid, s_copy);
-      if constexpr (CONS) if (tid == 0 && did_tile) stamp_max(a.meta, META_T_PROD);
       break;
     }
-    did_tile = true;
     const int chunk = __builtin_amdgcn_readfirstlane(s_item[1]);
     const int nsplit = __builtin_amdgcn_readfirstlane(s_item[2]);
     const int slot = __builtin_amdgcn_readfirstlane(s_item[3]);
@@ -683,88 +704,126 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     if (fm_act == C::FM) kloop(std::false_type{});
     else kloop(std::true_type{});
 
-    // split tail tile: publish this chunk's accumulators. First projection:
-    // the last chunk to arrive adds the others and finishes the tile. Output
-    // projection: once every chunk has arrived, chunk c adds the partials of
-    // accumulator blocks q in [q0, q1) (q = j * FM + i, the same share in
-    // every wave) and stores them; the last chunk to store raises the flag.
-    int q0 = 0, q1 = kBlocks;
-    int32_t* tail_ctr = nullptr;
-    if (nsplit > 1) {
-      tail_ctr = a.my_ctr + iq * kCtrStride + 1 + slot / nsplit;
-      // lane-native layout: ((wave * FM + i) * FN + j) * 8 + pair, then 64 lanes x 2 floats
-      uint64_t* mine = reinterpret_cast<uint64_t*>(a.partial) +
-                       (size_t)(iq * kTailSlots + slot) * (BM * BN / 2) +
-                       (size_t)wave * (C::FM * C::FN * 512) + lane;
+    if (a.dbg_seed != 0u) {
+      // test knob: a seeded delay before this item's results go out
+      uint32_t h = a.dbg_seed ^ ((uint32_t)fidx * 0x9E3779B1u) ^ ((uint32_t)chunk * 0x85EBCA77u);
+      h ^= h >> 15; h *= 0x2C1B3C6Du; h ^= h >> 12;
+      const int n = __builtin_amdgcn_readfirstlane((int)(h % 24u));
+      for (int z = 0; z < n; ++z) __builtin_amdgcn_s_sleep(127);
+    }
+
+    // ---- epilogue
+    // Rows of a tile holding a remote band are published for the copying
+    // roles (sec. 3.3.1: store, then flag): device-scope 16-byte stores,
+    // which write through this XCD's L2, and once they have completed the
+    // tile's ready flag. Tiles holding only this rank's own rows are never
+    // copied: plain stores and no flag.
+    const bool pub = (EPI == EPI_PLAIN) && a.flags != nullptr && st < n_rrt;
+    constexpr int OUTW = (EPI == EPI_GATED) ? BN / 2 : BN;
+    constexpr int LROW = OUTW + 8;
+    constexpr int CH = OUTW / 8;   // 16-byte chunks per output row
+    const int ncol = lane & 31;
+    const int mrow = (lane >> 5) * 4;
+    uint16_t* cbase = a.C + (size_t)row0 * a.Nout + (size_t)tn * OUTW;
+    // accumulator blocks q in [q0, q1) of every wave (q = j * FM + i) -> LDS ->
+    // the tile's rows. 32x32 accumulator layout: lane l holds column l%32 and
+    // rows 8*(r/4) + 4*(l/32) + r%4, r = 0..15. The bf16 tile is staged in LDS
+    // (row stride OUTW + 8 keeps the two row groups of a store on disjoint
+    // banks) and leaves as 16-byte row chunks.
+    auto store_blocks = [&](int q0, int q1) {
+      __syncthreads();   // every wave is done reading the ring (or the last staging)
+      if constexpr (EPI == EPI_GATED) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
+        for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+          for (int p = 0; p < C::FN / 2; ++p) {
+            const int c = wn * (C::WTN / 2) + p * 32 + ncol;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const uint64_t v = (uint64_t)__float_as_uint(acc[i][j][2 * r]) |
-                               ((uint64_t)__float_as_uint(acc[i][j][2 * r + 1]) << 32);
-            __hip_atomic_store(mine + ((i * C::FN + j) * 8 + r) * 64, v, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          }
-      // same ordering as a tile's publication: the write-through stores have
-      // completed before the arrival is counted (fence-based form: release
-      // before, acquire after the count)
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#if !MOE_DEVICE_SCOPE_PUBLISH
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-#endif
-      __syncthreads();
-      if (tid == 0)
-        s_item[0] = __hip_atomic_fetch_add(tail_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      const int arrived = s_item[0];
-      __syncthreads();   // s_item is rewritten below and by the next item
-      if constexpr (kShared) {
-        // wait (bounded) until every chunk's partial is out. The other chunks
-        // are running or about to (see queue_item), so this bound is not the
-        // copy roles' settable one.
-        if (tid == 0) {
-          int ok = 1;
-          if (arrived != nsplit - 1) {
-            const uint64_t t_start = wall_clock64();
-            while (__hip_atomic_load(tail_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nsplit) {
-              if (wall_clock64() - t_start > kDefaultWaitTicks) {
-                int expected = 0;
-                __hip_atomic_compare_exchange_strong(const_cast<int32_t*>(a.meta) + META_STATUS, &expected,
-                                                     MOE_ERR_TIMEOUT, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                ok = 0;
-                break;
-              }
-              __builtin_amdgcn_s_sleep(2);
+            for (int r = 0; r < 16; ++r) {
+              const int m = wm * C::WTM + i * 32 + (r >> 2) * 8 + mrow + (r & 3);
+              lds[m * LROW + c] = f32_to_bf16_rne(silu_f32(acc[i][2 * p][r]) * acc[i][2 * p + 1][r]);
             }
           }
-          s_item[0] = ok;
-        }
-        __syncthreads();
-        const int ok = s_item[0];
-        __syncthreads();
-        if (!ok) continue;
-        q0 = chunk * kBlocks / nsplit;
-        q1 = (chunk + 1) * kBlocks / nsplit;
       } else {
-        if (arrived != nsplit - 1) continue;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) {
+            const int c = wn * C::WTN + j * 32 + ncol;
+            if (j * C::FM + i < q0 || j * C::FM + i >= q1) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = wm * C::WTM + i * 32 + (r >> 2) * 8 + mrow + (r & 3);
+              float v = acc[i][j][r];
+              if constexpr (EPI == EPI_SILU) v = silu_f32(v);
+              lds[m * LROW + c] = f32_to_bf16_rne(v);
+            }
+          }
       }
-#if !MOE_DEVICE_SCOPE_PUBLISH
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(cbase, (uint32_t)vrows * (uint32_t)a.Nout * 2u);
+      auto store_chunk = [&](int m, int cc) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + m * LROW + cc * 8);
+#if MOE_DEVICE_SCOPE_PUBLISH
+        if (pub) {
+          store16_device(rs, ((uint32_t)m * (uint32_t)a.Nout + (uint32_t)(cc * 8)) * 2u, v);
+          return;
+        }
 #endif
-      // sum the chunks' partials of this item's blocks in chunk order (this
-      // chunk's own included), so the tile's bits do not depend on arrivals
+        *reinterpret_cast<u32x4*>(cbase + (size_t)m * a.Nout + cc * 8) = v;
+      };
+      const int nq = q1 - q0;
+      if (nq == kBlocks) {
+#pragma unroll 4
+        for (int x = tid; x < vrows * CH; x += C::NT) store_chunk(x / CH, x - (x / CH) * CH);
+      } else {
+        // a share of a split tile: blocks q0..q1-1 of every wave, 32 rows x 4 chunks each
+        for (int x = tid; x < C::NW * nq * 128; x += C::NT) {
+          const int wb = x / (nq * 128);
+          const int rem = x - wb * (nq * 128);
+          const int q = q0 + (rem >> 7);
+          const int m = (wb / WN) * C::WTM + (q % C::FM) * 32 + ((rem & 127) >> 2);
+          if (m < vrows) store_chunk(m, ((wb % WN) * C::WTN + (q / C::FM) * 32) / 8 + (rem & 3));
+        }
+      }
+    };
+    // the tile's rows are all stored (by this workgroup or, for a split tile,
+    // by the chunks before it): raise the flag, stamp the tile's end
+    auto finish_tile = [&]() {
+      if (pub) {
+#if MOE_DEVICE_SCOPE_PUBLISH
+        // all of this workgroup's device-scope stores have completed
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(a.flags + fidx, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0)
+          __hip_atomic_store(a.flags + fidx, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+#endif
+      } else if (COPY || CONS || (EPI == EPI_PLAIN && a.trace != nullptr)) {
+        __syncthreads();
+      }
+      if constexpr (COPY || CONS) {
+        if (tid == 0) stamp_max(a.meta, META_T_PROD);
+      }
+      if (EPI == EPI_PLAIN && a.trace != nullptr && tid == 0) a.trace[8 + fidx] = wall_clock64();
+    };
+    // fp32 partials of split tail tiles: lane-native layout ((wave * FM + i) *
+    // FN + j) * 8 + pair, then 64 lanes x 2 floats
+    const uint64_t* part0 = reinterpret_cast<const uint64_t*>(a.partial) +
+                            (size_t)(iq * kTailSlots + slot - chunk) * (BM * BN / 2) +
+                            (size_t)wave * (C::FM * C::FN * 512) + lane;
+    // acc of blocks [q0, q1) = the sum of every chunk's partials, in chunk order
+    // (so the tile's bits do not depend on the order of arrivals or on who sums)
+    auto reduce_blocks = [&](int q0, int q1) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-      const uint64_t* part0 = reinterpret_cast<const uint64_t*>(a.partial) +
-                              (size_t)(iq * kTailSlots + slot - chunk) * (BM * BN / 2) +
-                              (size_t)wave * (C::FM * C::FN * 512) + lane;
       if (kShared && q1 - q0 < kBlocks) {
         // a few blocks: the partials of up to four chunks of a block in flight
         // at once (clamped loads, so none is predicated), added in chunk order
@@ -815,114 +874,109 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
             }
         }
       }
-    }
-
-    // epilogue. 32x32 accumulator layout: lane l holds column l%32 and rows
-    // 8*(r/4) + 4*(l/32) + r%4, r = 0..15. The bf16 tile is staged in LDS
-    // (row stride OUTW + 8 keeps the two row groups of a store on disjoint
-    // banks) and leaves as 16-byte row chunks.
-    constexpr int OUTW = (EPI == EPI_GATED) ? BN / 2 : BN;
-    constexpr int LROW = OUTW + 8;
-    const int ncol = lane & 31;
-    const int mrow = (lane >> 5) * 4;
-    __syncthreads();   // every wave is done reading the ring
-    if constexpr (EPI == EPI_GATED) {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int p = 0; p < C::FN / 2; ++p) {
-          const int c = wn * (C::WTN / 2) + p * 32 + ncol;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = wm * C::WTM + i * 32 + (r >> 2) * 8 + mrow + (r & 3);
-            lds[m * LROW + c] = f32_to_bf16_rne(silu_f32(acc[i][2 * p][r]) * acc[i][2 * p + 1][r]);
-          }
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const int c = wn * C::WTN + j * 32 + ncol;
-          if (j * C::FM + i < q0 || j * C::FM + i >= q1) continue;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = wm * C::WTM + i * 32 + (r >> 2) * 8 + mrow + (r & 3);
-            float v = acc[i][j][r];
-            if constexpr (EPI == EPI_SILU) v = silu_f32(v);
-            lds[m * LROW + c] = f32_to_bf16_rne(v);
-          }
-        }
-    }
-    __syncthreads();
-    constexpr int CH = OUTW / 8;   // 16-byte chunks per output row
-    uint16_t* cbase = a.C + (size_t)row0 * a.Nout + (size_t)tn * OUTW;
-    const bool signal = (EPI == EPI_PLAIN) && a.flags != nullptr;
-    auto store_chunk = [&](int m, int cc) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + m * LROW + cc * 8);
-      uint16_t* dst = cbase + (size_t)m * a.Nout + cc * 8;
-#if MOE_DEVICE_SCOPE_PUBLISH
-      if (signal) {
-        // device-scope (sc1) stores write through this XCD's L2
-        uint64_t* d64 = reinterpret_cast<uint64_t*>(dst);
-        __hip_atomic_store(d64, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(d64 + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        return;
-      }
-#endif
-      *reinterpret_cast<u32x4*>(dst) = v;
     };
-    const int nq = q1 - q0;
-    if (nq == kBlocks) {
-#pragma unroll 4
-      for (int x = tid; x < vrows * CH; x += C::NT) store_chunk(x / CH, x - (x / CH) * CH);
-    } else {
-      // this chunk's share: blocks q0..q1-1 of every wave, 32 rows x 4 chunks each
-      for (int x = tid; x < C::NW * nq * 128; x += C::NT) {
-        const int wb = x / (nq * 128);
-        const int rem = x - wb * (nq * 128);
-        const int q = q0 + (rem >> 7);
-        const int m = (wb / WN) * C::WTM + (q % C::FM) * 32 + ((rem & 127) >> 2);
-        if (m < vrows) store_chunk(m, ((wb % WN) * C::WTN + (q / C::FM) * 32) / 8 + (rem & 3));
-      }
-    }
-    // a shared tail tile is finished by the last of its chunks to store
-    bool last = true;
-    if (kShared && nsplit > 1) {
-#if MOE_DEVICE_SCOPE_PUBLISH
+
+    // Split tail tile: publish this chunk's accumulators as a partial tile
+    // (device-scope stores), wait for them to complete, count the arrival.
+    //  * first projection: the last chunk to arrive sums all partials and
+    //    finishes the tile; the others are done;
+    //  * output projection: the accumulator blocks are cut into nsplit
+    //    shares. A chunk that sees every chunk arrive (waiting at most
+    //    tail_wait_ticks) claims its own share; the last chunk to arrive
+    //    claims its own and then every share still unclaimed, so no chunk
+    //    depends on another workgroup being resident. Each share is summed
+    //    in chunk order and stored by the one chunk that claimed it; the
+    //    chunk storing the tile's last share raises the flag.
+    const bool split = nsplit > 1;
+    constexpr bool kSplitShares = kShared;
+    bool last_arrival = true;
+    int32_t* tail_ctr = a.my_ctr + iq * kCtrStride + 1 + slot / nsplit;
+    if (split) {
+      uint64_t* mine = reinterpret_cast<uint64_t*>(a.partial) +
+                       (size_t)(iq * kTailSlots + slot) * (BM * BN / 2) +
+                       (size_t)wave * (C::FM * C::FN * 512) + lane;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const uint64_t v = (uint64_t)__float_as_uint(acc[i][j][2 * r]) |
+                               ((uint64_t)__float_as_uint(acc[i][j][2 * r + 1]) << 32);
+            __hip_atomic_store(mine + ((i * C::FN + j) * 8 + r) * 64, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#else
+#if !MOE_DEVICE_SCOPE_PUBLISH
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 #endif
       __syncthreads();
       if (tid == 0)
         s_item[0] = __hip_atomic_fetch_add(tail_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
-      last = s_item[0] == 2 * nsplit - 1;
-      __syncthreads();
-      if (!last) continue;
+      const int arrived = s_item[0];
+      __syncthreads();   // s_item is rewritten below and by the next item
+      last_arrival = arrived == nsplit - 1;
+      if (!kSplitShares && !last_arrival) continue;
+      if (kSplitShares && !last_arrival) {
+        if (tid == 0) {
+          int ok = 1;
+          const uint64_t t_start = wall_clock64();
+          while (__hip_atomic_load(tail_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nsplit) {
+            if (wall_clock64() - t_start > a.tail_wait_ticks) { ok = 0; break; }
+            __builtin_amdgcn_s_sleep(2);
+          }
+          s_item[0] = ok;
+        }
+        __syncthreads();
+        const int ok = s_item[0];
+        __syncthreads();
+        if (!ok) continue;   // the last chunk to arrive takes this share
+      }
 #if !MOE_DEVICE_SCOPE_PUBLISH
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #endif
     }
-    if (signal) {
+    // the tile's shares this workgroup stores: a whole tile (or the first
+    // projection's reduced split tile) is one share of every block
+    const int n_sh = (kSplitShares && split) ? nsplit : 1;
+    for (int k2 = 0; k2 < n_sh; ++k2) {
+      if (k2 > 0 && !last_arrival) break;
+      int q0 = 0, q1 = kBlocks;
+      if (kSplitShares && split) {
+        const int sh = chunk + k2 < nsplit ? chunk + k2 : chunk + k2 - nsplit;
+        uint32_t* claimed = reinterpret_cast<uint32_t*>(a.my_ctr + iq * kCtrStride + 1 + kTailTiles + slot / nsplit);
+        if (tid == 0)
+          s_item[0] = (int)((__hip_atomic_fetch_or(claimed, 1u << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >>
+                             sh) & 1u);
+        __syncthreads();
+        const int taken = s_item[0];
+        __syncthreads();
+        if (taken) continue;
+        q0 = sh * kBlocks / nsplit;
+        q1 = (sh + 1) * kBlocks / nsplit;
+      }
+      if (split) reduce_blocks(q0, q1);
+      store_blocks(q0, q1);
+      bool done = true;
+      if (kSplitShares && split) {
+        // count the stored share; the tile is done with its last share
 #if MOE_DEVICE_SCOPE_PUBLISH
-      // all of this thread's device-scope stores have completed
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (tid == 0) __hip_atomic_store(a.flags + fidx, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #else
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (tid == 0)
-        __hip_atomic_store(a.flags + fidx, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 #endif
-    }
-    if (EPI == EPI_PLAIN && a.trace != nullptr) {
-      if (!signal) __syncthreads();
-      if (tid == 0) a.trace[8 + fidx] = wall_clock64();
+        __syncthreads();
+        if (tid == 0)
+          s_item[0] = __hip_atomic_fetch_add(tail_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        done = s_item[0] == 2 * nsplit - 1;
+        __syncthreads();
+#if !MOE_DEVICE_SCOPE_PUBLISH
+        if (done) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#endif
+      }
+      if (done) finish_tile();
     }
   }
 }
@@ -977,8 +1031,11 @@ static hipError_t dispatch(GemmArgs a, int bm, int bn, int grid, hipStream_t st)
 
 hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t* a_rows,
                         const uint16_t* a_zero, const uint16_t* w1, const uint16_t* w3, uint16_t* h,
-                        const moe_plan_t& p, uint32_t* flags, int grid, hipStream_t st) {
+                        const moe_plan_t& p, uint32_t* flags, int grid, const GemmKnobs& kn, hipStream_t st) {
   GemmArgs a{};
+  a.dbg_seed = kn.delay_seed;
+  a.dbg_reverse = kn.reverse;
+  a.tail_wait_ticks = kn.tail_wait_ticks;
   a.A = a_src;
   a.a_rows = a_rows;
   a.a_zero = a_zero;
@@ -1012,8 +1069,11 @@ hipError_t launch_gemm1(const Geometry& g, const uint16_t* a_src, const int32_t*
 hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2, uint16_t* y,
                         const moe_plan_t& p, uint32_t* flags, uint32_t epoch, uint64_t* trace,
                         int grid, int split_grid, const BufPtrs* copy_bufs, int n_cons,
-                        const BufPtrs* cons_bufs, uint64_t wait_ticks, hipStream_t st) {
+                        const BufPtrs* cons_bufs, uint64_t wait_ticks, const GemmKnobs& kn, hipStream_t st) {
   GemmArgs a{};
+  a.dbg_seed = kn.delay_seed;
+  a.dbg_reverse = kn.reverse;
+  a.tail_wait_ticks = kn.tail_wait_ticks;
   a.A = h;
   a.B0 = w2;
   a.B1 = nullptr;

@@ -60,6 +60,12 @@ class Context:
         ticks (0: the default of 2 s); see moe_ctx_set_wait_limit."""
         check("moe_ctx_set_wait_limit", lib().moe_ctx_set_wait_limit(self.handle, int(ticks)))
 
+    def set_debug(self, delay_seed: int = 0, reverse_schedule: bool = False, tail_wait_ticks: int = -1):
+        """Test knobs (timing only; see moe_ctx_set_debug): seeded per-item
+        delays, reversed tile queues, the split tail chunks' wait bound."""
+        check("moe_ctx_set_debug", lib().moe_ctx_set_debug(self.handle, int(delay_seed) & 0xFFFFFFFF,
+                                                           int(bool(reverse_schedule)), int(tail_wait_ticks)))
+
     def set_timing(self, enable: bool):
         check("moe_ctx_set_timing", lib().moe_ctx_set_timing(self.handle, int(bool(enable))))
 

@@ -82,7 +82,8 @@ enum { MOE_MODE_OVERLAP = 0, MOE_MODE_SEQUENTIAL = 1, MOE_MODE_ROLE_SWITCH = 2 }
  *           128 or 256. The GEMMs run tiles of moe_sizes_t.tile_m (256) rows
  *           over each expert's tb_m-aligned rows, so the band can be smaller
  *           than the compute tile (and, at 16, than one 32-row MFMA block).
- *  mgb      row bands per middle transfer segment ([TLS] sec. 3.3.2, Fig. 3(b)), >= 1
+ *  mgb      row bands per middle transfer segment ([TLS] sec. 3.3.2, Fig. 3(b)), >= 1,
+ *           with mgb * tb_m * H * 2 < 2^31 (a segment below 2 GiB)
  */
 typedef struct {
   int32_t R, T, H, F, E, k, r_self;
@@ -200,6 +201,25 @@ int moe_ctx_num_cus(const moe_ctx_t* ctx);
  * from the host. Returns MOE_ERR_INVALID_ARG for a NULL ctx. */
 int moe_ctx_set_wait_limit(moe_ctx_t* ctx, uint64_t ticks);
 
+/* Test knobs of later moe_expert_forward_* calls on ctx. They change only
+ * when work happens, never the results, so outputs stay bit-identical to a
+ * call without them (the race tests rely on that):
+ *   delay_seed       nonzero: each GEMM work item sleeps a pseudo-random
+ *                    0..23 x ~3.4 us, drawn from (seed, tile, chunk), before
+ *                    its results are stored and flagged
+ *   reverse_schedule 1: every GEMM tile queue runs its whole tiles in reverse
+ *                    schedule order (the rank's own rows first, remote rows
+ *                    last; the K-split tail tiles stay the same tiles), 0: as
+ *                    scheduled ([TLS] sec. 3.2.2)
+ *   tail_wait_ticks  bound on how long a K-chunk of one of the output
+ *                    projection's split tail tiles waits for the tile's other
+ *                    chunks, in 100 MHz ticks (< 0: the default of 1 ms); a
+ *                    chunk that gives up leaves its share of the tile to the
+ *                    chunk that arrives last, so 0 makes the last chunk of
+ *                    every split tile reduce the whole tile
+ * Returns MOE_ERR_INVALID_ARG for a NULL ctx or reverse_schedule not 0/1. */
+int moe_ctx_set_debug(moe_ctx_t* ctx, uint32_t delay_seed, int32_t reverse_schedule, int64_t tail_wait_ticks);
+
 /* Phase timing of moe_expert_forward_overlap with HIP events recorded on the
  * streams the kernels run on (off by default; enabling creates 5 events).
  * moe_ctx_timings waits for the last timed call and writes, in ms:
@@ -209,9 +229,10 @@ int moe_ctx_set_wait_limit(moe_ctx_t* ctx, uint64_t ticks);
  *   ms[2] from the output projection's start to the end of the transfer
  *         (SEQUENTIAL: to the end of the bulk copy)
  *   ms[3] whole call
- *   ms[4] exposed transfer (OVERLAP: the last consumer completion minus the
- *         last producer exit, >= 0, from device clock stamps; SEQUENTIAL: the
- *         bulk copy's duration; ROLE_SWITCH: 0) 
+ *   ms[4] exposed transfer: OVERLAP and ROLE_SWITCH, the completion of the
+ *         last copy minus the completion of the last tile of the output
+ *         projection (>= 0; 0 when nothing is copied), from device clock
+ *         stamps of the same launch; SEQUENTIAL, the bulk copy's duration
  * Returns MOE_ERR_INVALID_ARG if timing is off or nothing was timed. */
 int moe_ctx_set_timing(moe_ctx_t* ctx, int enable);
 int moe_ctx_timings(moe_ctx_t* ctx, float* ms);
@@ -359,11 +380,11 @@ int moe_combine(const moe_shape_t* shape, uint16_t* const* combine_buf,
 
 /* Copies the device status word of the workspace to *status (host) and
  * synchronises the stream. Returns *status (MOE_OK, MOE_ERR_TIMEOUT, ...)
- * or MOE_ERR_HIP. MOE_ERR_TIMEOUT: a bounded device wait ran out, either a
- * copying role waiting for ready flags (moe_ctx_set_wait_limit) or a K-chunk
- * of the output projection's split tail tiles waiting 2 s for the other
- * chunks of its tile (only if workgroups of the launch were not resident);
- * the outputs of that call are then incomplete. moe_permute clears it. */
+ * or MOE_ERR_HIP. MOE_ERR_TIMEOUT: a copying role's bounded wait for ready
+ * flags ran out (moe_ctx_set_wait_limit); the combine buffers of that call
+ * are then incomplete (y_perm is complete: no GEMM work item ever waits
+ * without bound for another workgroup, so y_perm never depends on every
+ * workgroup of a launch being resident at once). moe_permute clears it. */
 int moe_read_status(const moe_shape_t* shape, void* ws, int32_t* status, void* stream);
 
 #ifdef __cplusplus

@@ -414,19 +414,22 @@ class ShareResult:
 
 def oracle_share(logits, x_bits, W1b, W3b, W2b, *, R: int, T: int, E: int, k: int,
                  gate_kind: str, r_self: int, tb_m: int, mgb: int = 1,
-                 with_ffn: bool = True) -> ShareResult:
+                 with_ffn: bool = True, with_rows: bool = True) -> ShareResult:
     """Route -> layout -> schedule/plan -> per-expert FFN -> transfer -> reduction.
 
     [TLS] sec. 2.1 (the five steps of a distributed MoE forward, with the
     dispatch modelled as a gather of this rank's rows) and sec. 3.2-3.3.
     W1b/W3b/W2b hold rank r_self's local experts only (bf16 bits).
+    with_ffn False stops after the plan and the gathered rows; with_rows
+    False (only without the FFN) also leaves out the gathered rows (x_perm
+    None), for shapes whose float64 rows would not fit in memory.
     """
     E_l = E // R
     ids, gates = route(logits, k, gate_kind)
     lay = row_layout(ids, R, T, E_l, r_self, tb_m)
     b = tile_schedule(lay)
     sg = segments(b, mgb)
-    x_perm = gather_rows(x_bits, lay)
+    x_perm = gather_rows(x_bits, lay) if (with_ffn or with_rows) else None
     if not with_ffn:
         return ShareResult(ids, gates, lay, b, sg, x_perm, None, None, None)
     y_perm = expert_outputs(x_perm, lay, W1b, W3b, W2b)
@@ -435,11 +438,12 @@ def oracle_share(logits, x_bits, W1b, W3b, W2b, *, R: int, T: int, E: int, k: in
     return ShareResult(ids, gates, lay, b, sg, x_perm, y_perm, bufs, y)
 
 
-def token_rows(res: ShareResult, W1b, W3b, W2b, tokens) -> np.ndarray:
+def token_rows(res: ShareResult, W1b, W3b, W2b, tokens, x_bits=None) -> np.ndarray:
     """y_share rows of selected tokens only, from the definition
     y[g] = sum_j gate_j * FFN_{e_j}(x_g) over the local slots of g (for sampled
     checks where the full share is too slow). Works one expert at a time so
-    only one expert's weights are widened to float64 at once.
+    only one expert's weights are widened to float64 at once. x_g comes from
+    the gathered rows, or from x_bits [R, T, H] when the result holds none.
     tokens: global token indices. Returns float64 [len, H]."""
     lay = res.layout
     H = W2b.shape[1]
@@ -450,7 +454,8 @@ def token_rows(res: ShareResult, W1b, W3b, W2b, tokens) -> np.ndarray:
     for q, g in enumerate(tokens):
         hit = np.nonzero(lay.row_src == g)[0]
         if hit.size:
-            xrow[g] = res.x_perm[hit[0]]
+            xrow[g] = (res.x_perm[hit[0]] if res.x_perm is not None
+                       else widen_bf16(x_bits.reshape(-1, x_bits.shape[-1])[g]))
     for e in range(lay.E_l):
         pairs = [(q, j) for q, g in enumerate(tokens) for j in range(res.ids.shape[1])
                  if int(res.ids[g, j]) - first == e]

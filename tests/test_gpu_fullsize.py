@@ -121,3 +121,106 @@ def test_full_size_parity(wid, layer, tb):
 
     say(f"[fullsize] {w.name}: role switching")
     check_role_switch(sh, ref, w, 0, w.name)
+
+
+@pytest.mark.timeout(900)
+def test_table2_shape_parity():
+    """A shape of the tile-signalling paper's Table 2 (sec. 4.1.3): the
+    expert GEMM K = 2048 -> N = 8192 as a non-gated FFN with F = 2048 and
+    H = 8192, 64 experts per rank (E = 256 over 4 ranks), 16384 tokens per
+    rank, top-2 softmax, stress_skew routing (reading: logits + ln Zipf(1.2)
+    over the expert id, the hottest experts local to the timed rank). The
+    plan in full, the combine buffers against y_perm bit for bit, sampled
+    expert rows and tokens against the fp64 oracle, and every form (overlap
+    at the model's c, sequential, role switching, the fused gather) with the
+    same bits."""
+    import torch
+    from synth import Workload
+    from combine_overlap_amd import MOE_CONSUMER_AUTO, MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL
+    w = Workload("table2_stress_tpr16384_n8192_e64", 4, 16384, 8192, 2048, 256, 2, False, "softmax",
+                 "zipf", zipf_s=1.2, w_std="0.02")
+    tb = 64
+    say(f"[fullsize] {w.name}: inputs")
+    W1, W3, W2 = make_local_weights(w, 0)
+    inp = ShareInputs(w, 0, make_logits(w, 0), make_x(w), W1, W3, W2)
+    sh, _ = make_gpu_share(w, 0, tb, None, inp)
+    b = sh.buf
+    ref = om.oracle_share(inp.logits, inp.x, W1, W3, W2, R=w.R, T=w.T, E=w.E, k=w.k, gate_kind=w.gate_kind,
+                          r_self=0, tb_m=tb, mgb=sh.shape.mgb, with_ffn=False, with_rows=False)
+    say(f"[fullsize] {w.name}: route + permute")
+    sh.route()
+    torch.cuda.synchronize()
+    assert np.array_equal(b.topk_ids.cpu().numpy(), ref.ids)
+    assert np.array_equal(b.counts.cpu().numpy(), ref.layout.counts)
+    sh.permute()
+    plan = sh.plan_arrays()
+    assert plan["status"] == 0
+    assert_plan_equal(plan, oracle_plan_arrays(ref))
+    check_row_tiles(plan, ref, sh.sizes.tile_m)
+    check_auto_partition(sh, w.name)
+    m_pad = plan["m_pad"]
+    rng = np.random.default_rng(2048)
+    x_flat = inp.x.reshape(-1, w.H)
+    valid = np.nonzero(ref.layout.row_src >= 0)[0]
+    rows = rng.choice(valid, size=256, replace=False)
+    got = b.x_perm[torch.from_numpy(rows).to(sh.device)].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, x_flat[ref.layout.row_src[rows]]), "x_perm rows"
+
+    c = sh.auto_consumer_cu()[0]
+    say(f"[fullsize] {w.name}: overlap c={c}")
+    for q in range(w.R):
+        if b.combine[q] is not None:
+            b.combine[q].fill_(float("nan"))
+    sh.expert_forward(MOE_MODE_OVERLAP, n_consumer_cu=MOE_CONSUMER_AUTO)
+    sh.combine()
+    torch.cuda.synchronize()
+    assert sh.status() == 0
+    y_bits = bits(b.y_perm[:m_pad])
+    share_bits = bits(b.y_share).copy()
+    bd = ref.bands
+    for i in range(bd.n_remote):
+        s, r0, rc, n = int(bd.dest[i]), int(bd.row0[i]), int(bd.recv0[i]), int(bd.valid[i])
+        got = b.combine[s][rc:rc + n].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, y_bits[r0:r0 + n]), f"band {i}"
+    pick = rng.choice(valid, size=64, replace=False)
+    y_ref = np.zeros((pick.size, w.H))
+    for e in range(w.E_local):
+        lo, hi = ref.layout.expert_base[e], ref.layout.expert_base[e] + ref.layout.M_e[e]
+        sel = np.nonzero((pick >= lo) & (pick < hi))[0]
+        if sel.size:
+            X = om.widen_bf16(x_flat[ref.layout.row_src[pick[sel]]])
+            y_ref[sel] = om.expert_ffn(X, om.widen_bf16(W1[e]), None, om.widen_bf16(W2[e]))
+    y_gpu = (y_bits[pick].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    check_rows(y_gpu, y_ref, f"{w.name} y_perm sample", layer_output=False)
+    nloc = ((ref.ids >= 0) & (ref.ids < w.E_local)).sum(axis=1)
+    toks = []
+    for want in sorted(set(nloc.tolist())):
+        cand = np.nonzero(nloc == want)[0]
+        toks += rng.choice(cand, size=min(cand.size, 16), replace=False).tolist()
+    t_ref = om.token_rows(ref, W1, W3, W2, toks, x_bits=inp.x)
+    t_gpu = (share_bits.reshape(-1, w.H)[toks].astype(np.uint32) << 16).view(np.float32)
+    check_rows(t_gpu.astype(np.float64), t_ref, f"{w.name} y_share sample")
+
+    say(f"[fullsize] {w.name}: sequential baseline, fused gather, role switching")
+    sh.expert_forward(MOE_MODE_SEQUENTIAL, n_consumer_cu=MOE_CONSUMER_AUTO)
+    sh.combine()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits)
+    assert np.array_equal(bits(b.y_share), share_bits)
+    b.x_perm = None   # frees the materialized rows before the gathered run
+    torch.cuda.empty_cache()
+    sh.fused_gather = True
+    try:
+        sh.permute()
+        for q in range(w.R):
+            if b.combine[q] is not None:
+                b.combine[q].fill_(float("nan"))
+        sh.expert_forward(MOE_MODE_OVERLAP, n_consumer_cu=c)
+        sh.combine()
+        torch.cuda.synchronize()
+        assert sh.status() == 0
+        assert np.array_equal(bits(b.y_perm[:m_pad]), y_bits), "gathered y_perm"
+        assert np.array_equal(bits(b.y_share), share_bits), "gathered y_share"
+        check_role_switch(sh, ref, w, 0, w.name)
+    finally:
+        sh.fused_gather = False
