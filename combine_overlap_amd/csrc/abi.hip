@@ -5,6 +5,44 @@
 #include "common.hpp"
 #include "partition_model.hpp"
 
+#include <mutex>
+
+// ---- scratch of moe_expert_forward_noalloc ------------------------------
+// The K-split partial tiles and the tile-queue / tail / copy counters of the
+// two GEMM launches, in a file-scope device array instead of the caller's
+// workspace, for callers that cannot allocate. Each GPU holds its own copy
+// until the process ends. Host code never uses the array's name as an
+// address: the per-device address comes from hipGetSymbolAddress (taken
+// once per device in moe_ctx_create, with that device current).
+constexpr size_t kScratchCtrBytes = 4096;   // counters (moe::kCtrWords int32)
+constexpr size_t kScratchPartialBytes = (size_t)moe::kXcds * moe::kTailSlots * moe::kTileM * 256 * 4;
+constexpr size_t kScratchBytes = kScratchCtrBytes + kScratchPartialBytes;   // 62 MiB + 4 KiB
+static_assert(moe::kCtrWords * 4 <= (int)kScratchCtrBytes, "counters fit the scratch header");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// the current device's address of `scratch` (looked up once per device)
+static int scratch_address(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return MOE_OK;
+}
+
+// zeroes the scratch counters before a call (a kernel, not a memset node, so
+// a captured call replays it)
+__global__ void k_clear_scratch_ctr(int32_t* ctr, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ctr[i] = 0;
+}
+
 struct moe_ctx {
   int device;
   int n_cu;
@@ -17,6 +55,7 @@ struct moe_ctx {
   const int32_t* timed_meta;   // workspace meta words of the last timed call (device stamps)
   uint64_t wait_ticks;      // bound on each wait for a ready flag (100 MHz ticks)
   moe::GemmKnobs knobs;     // test knobs of the GEMM launches (moe_ctx_set_debug)
+  void* scratch;            // this device's address of `scratch`
 };
 
 namespace moe {
@@ -202,6 +241,11 @@ int moe_ctx_create(moe_ctx_t** out) {
     delete c;
     return MOE_ERR_HIP;
   }
+  const int src = scratch_address(c->device, &c->scratch);
+  if (src != MOE_OK) {
+    delete c;
+    return src;
+  }
   *out = c;
   return MOE_OK;
 }
@@ -329,10 +373,13 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
 // Both expert-phase entry points: `a` is x_perm (gathered = false) or x
 // (gathered = true: the first projection reads packed row r from x row
 // row_src[r], or the workspace's zero row for padding).
+// use_scratch: the GEMMs' counters and K-split partials come from the
+// library's static scratch instead of the workspace (moe_expert_forward_noalloc)
 static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16_t* a, bool gathered,
                           const uint16_t* w1, const uint16_t* w3, const uint16_t* w2, void* ws,
                           uint16_t* h, uint16_t* y_perm, uint16_t* const* combine_buf, uint32_t* flags,
-                          uint32_t epoch, int32_t n_consumer_cu, int32_t mode, void* stream) {
+                          uint32_t epoch, int32_t n_consumer_cu, int32_t mode, void* stream,
+                          bool use_scratch = false) {
   Geometry g;
   int rc = make_geometry(shape, &g);
   if (rc != MOE_OK) return rc;
@@ -360,6 +407,17 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
   moe_plan_t p;
   plan_from_ws(g, ws, &p);
   hipStream_t ps = static_cast<hipStream_t>(stream);
+  if (use_scratch) {
+    // the largest partial tile either GEMM writes is tile_m x 256 fp32
+    const size_t need = kScratchCtrBytes + (size_t)kXcds * kTailSlots * g.tile_m *
+                                               (size_t)(g.bn1 > g.bn2 ? g.bn1 : g.bn2) * 4;
+    if (need > kScratchBytes || ctx->scratch == nullptr) return MOE_ERR_UNSUPPORTED;
+    p.tile_ctr = static_cast<int32_t*>(ctx->scratch);
+    p.partial = reinterpret_cast<float*>(static_cast<char*>(ctx->scratch) + kScratchCtrBytes);
+    // the array keeps the last call's counters: clear them first
+    hipLaunchKernelGGL(k_clear_scratch_ctr, dim3(1), dim3(256), 0, ps, p.tile_ctr, (int)kCtrWords);
+    if ((rc = hip_rc(hipGetLastError())) != MOE_OK) return rc;
+  }
   const int ncu = ctx->n_cu;
   const bool tm = ctx->timing != 0;
   auto rec = [&](int i, hipStream_t st) { return tm ? hip_rc(hipEventRecord(ctx->tev[i], st)) : MOE_OK; };
@@ -428,6 +486,15 @@ int moe_expert_forward_gathered(moe_ctx_t* ctx, const moe_shape_t* shape, const 
                                 int32_t n_consumer_cu, int32_t mode, void* stream) {
   return expert_forward(ctx, shape, x, true, w1, w3, w2, ws, h, y_perm, combine_buf, flags, epoch,
                         n_consumer_cu, mode, stream);
+}
+
+int moe_expert_forward_noalloc(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16_t* x_perm,
+                               const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                               void* ws, uint16_t* h, uint16_t* y_perm,
+                               uint16_t* const* combine_buf, uint32_t* flags, uint32_t epoch,
+                               int32_t n_consumer_cu, int32_t mode, void* stream) {
+  return expert_forward(ctx, shape, x_perm, false, w1, w3, w2, ws, h, y_perm, combine_buf, flags, epoch,
+                        n_consumer_cu, mode, stream, true);
 }
 
 int moe_combine(const moe_shape_t* shape, uint16_t* const* combine_buf, const uint16_t* y_perm,

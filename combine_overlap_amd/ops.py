@@ -137,6 +137,14 @@ def moe_expert_forward_gathered(ctx: Context, shape, x, w1, w3, w2, ws, h, y_per
         int(n_consumer_cu), int(mode), _stream(stream)))
 
 
+def moe_expert_forward_noalloc(ctx: Context, shape, x_perm, w1, w3, w2, ws, h, y_perm, combine_bufs,
+                               flags, epoch: int, n_consumer_cu: int, mode: int, stream=None):
+    check("moe_expert_forward_noalloc", lib().moe_expert_forward_noalloc(
+        ctx.handle, C.byref(shape), _ptr(x_perm), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws), _ptr(h),
+        _ptr(y_perm), _buf_array(shape, combine_bufs), _ptr(flags), C.c_uint32(epoch),
+        int(n_consumer_cu), int(mode), _stream(stream)))
+
+
 def moe_combine(shape, combine_bufs, y_perm, gates, ws, y_share, stream=None):
     check("moe_combine", lib().moe_combine(C.byref(shape), _buf_array(shape, combine_bufs),
                                            _ptr(y_perm), _ptr(gates), _ptr(ws), _ptr(y_share),

@@ -366,6 +366,30 @@ int moe_expert_forward_gathered(moe_ctx_t* ctx, const moe_shape_t* shape,
                                 uint32_t* flags, uint32_t epoch, int32_t n_consumer_cu,
                                 int32_t mode, void* stream);
 
+/* moe_expert_forward_overlap for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, modes and results (bit-identical to
+ * moe_expert_forward_overlap for the same plan, mode and n_consumer_cu), but
+ * the GEMM launches' scratch, i.e. their tile-queue, tail and copy counters
+ * and the fp32 partial tiles of their K-split tail tiles, lives in one
+ * static device array of the library (62 MiB + 4 KiB, held by every GPU the
+ * library runs on until the process ends; its address is looked up once per
+ * device by moe_ctx_create) instead of the workspace. The workspace still
+ * carries the plan of the preceding moe_permute (its counter and partial
+ * sections are left untouched). The call allocates nothing: it clears the
+ * array's counters with a kernel on `stream`, then launches as
+ * moe_expert_forward_overlap does. Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU race (as calls sharing a
+ * workspace do). Returns MOE_ERR_UNSUPPORTED if a shape needed more scratch
+ * than the array holds (none does: the largest partial tile is 256 x 256),
+ * else as moe_expert_forward_overlap. */
+int moe_expert_forward_noalloc(moe_ctx_t* ctx, const moe_shape_t* shape,
+                               const uint16_t* x_perm, const uint16_t* w1,
+                               const uint16_t* w3, const uint16_t* w2, void* ws,
+                               uint16_t* h, uint16_t* y_perm, uint16_t* const* combine_buf,
+                               uint32_t* flags, uint32_t epoch, int32_t n_consumer_cu,
+                               int32_t mode, void* stream);
+
 /* Step 5, weighted reduction ([TLS] sec. 2.1 step 5): for every token (s, t),
  * y_share[s, t] = sum over slots j ascending whose expert is local of
  * gates[s*T+t, j] * row, with row = combine_buf[s][recv_row] for s != r_self
