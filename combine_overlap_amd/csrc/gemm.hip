@@ -330,7 +330,7 @@ __device__ __forceinline__ int xcc_id() {
 // stored; a segment is below 2 GiB, which the host checks).
 template <int NT>
 __device__ __forceinline__ void copy_segment(const GemmArgs& a, int sg, int tid) {
-  constexpr int kRound = 16;   // 16-byte loads per thread in flight
+  constexpr int kRound = 32;   // 16-byte loads per thread in flight
   const int H = a.Nout;
   const uint32_t words = (uint32_t)a.seg_rows[sg] * (uint32_t)(H / 8);
   const uint16_t* src = a.C + (size_t)a.seg_src_row[sg] * H;
