@@ -364,8 +364,8 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MOE_ERR_HIP;
   const moe_calib_t calib = default_calib(n_cu);
-  if ((rc = hip_rc(launch_plan(g, counts, p, zero_row_of(g, ws), calib, st))) != MOE_OK) return rc;
-  return hip_rc(launch_gather(g, x, topk_ids, x_perm, p, st));
+  if ((rc = hip_rc(launch_plan(g, counts, topk_ids, p, zero_row_of(g, ws), calib, st))) != MOE_OK) return rc;
+  return hip_rc(launch_gather(g, x, x_perm, p, st));
 }
 
 }  // extern "C"

@@ -23,9 +23,10 @@ constexpr int kPlanMaxElRoute = 256;
 // chose (MOE_CONSUMER_AUTO); META_PRED: its predicted time (double, two words).
 // META_T_PROD / META_T_CONS: uint64 device clock stamps (two words each) of the
 // overlapped output projection's last producer exit and last consumer completion
+// META_HISTCTR: arrivals of the routing histogram blocks (zeroed by k_route)
 enum { META_MPAD = 0, META_NBANDS = 1, META_NREMOTE = 2, META_NSEG = 3, META_STATUS = 4, META_NUNITS = 5,
        META_NTILES = 6, META_NRTILES = 7, META_CAUTO = 8, META_T_PROD = 16, META_T_CONS = 18,
-       META_PRED = 20, META_WORDS = 64 };
+       META_PRED = 20, META_HISTCTR = 22, META_WORDS = 64 };
 // GEMM row-tile height: the producer computes tiles of this many rows over each
 // expert's tb_m-aligned rows, independently of the (possibly smaller) band
 constexpr int kTileM = 256;
@@ -127,12 +128,13 @@ hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, fl
                         const moe_plan_t& p, hipStream_t st);
 hipError_t launch_count(const Geometry& g, const int32_t* ids, int32_t* counts, const moe_plan_t& p,
                         hipStream_t st);
-// also evaluates the CU-split model for `calib` (META_CAUTO, META_PRED)
-hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, uint16_t* zero_row,
-                       const moe_calib_t& calib, hipStream_t st);
-// x_perm null: only the indexes (row_src, with -1 for every padding row, and recv_row)
-hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
-                         uint16_t* x_perm, const moe_plan_t& p, hipStream_t st);
+// the plan, the index of the routed rows (row_src with -1 for every padding
+// row, recv_row) and the CU-split model for `calib` (META_CAUTO, META_PRED)
+hipError_t launch_plan(const Geometry& g, const int32_t* counts, const int32_t* ids, const moe_plan_t& p,
+                       uint16_t* zero_row, const moe_calib_t& calib, hipStream_t st);
+// the rows into x_perm (nothing when x_perm is null)
+hipError_t launch_gather(const Geometry& g, const uint16_t* x, uint16_t* x_perm, const moe_plan_t& p,
+                         hipStream_t st);
 // a_rows null: A = x_perm (packed rows); else A = x and packed row r reads x row
 // a_rows[r] (a_zero for padding), the gather fused into the tile loads.
 // flags (may be null): the output projection's ready flags, cleared here

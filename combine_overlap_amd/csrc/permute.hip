@@ -19,6 +19,14 @@
 // schedule's order, then the remaining tiles by expert id. A segment's rows
 // lie in one expert, so the tiles covering it are consecutive.
 //
+// One launch (k_plan) builds all of it, its workgroups taking three roles:
+// block 0 the plan (layout, schedule, combine plan, segments, GEMM row tiles,
+// copy units, padding marks), block 1 the CU-split model of the layer
+// (partition_model.hpp) evaluated from the counts, the other blocks the
+// index of the routed rows (row_src, recv_row), four routing chunks each.
+// Each role derives what it needs from the counts, so none waits for
+// another. A second launch copies the rows into x_perm (k_gather_copy).
+//
 // With the gather fused into the first projection's tile loads the rows are
 // not copied: only the indexes are built (row_src, -1 for padding). The plan
 // also zeroes the one row of H zeros that padding rows read there when x is
@@ -60,10 +68,15 @@ __device__ int block_exscan(int* a, int n, int* s_w) {
   }
   if (lane == 63) s_w[wave] = incl;
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) { const int v = s_w[w]; s_w[w] = acc; acc += v; }
-    s_w[16] = acc;
+  if (wave == 0) {   // the 16 wave totals: one shuffle scan in the first wave
+    const int v = lane < kPlanThreads / 64 ? s_w[lane] : 0;
+    int x = v;
+    for (int d = 1; d < kPlanThreads / 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane < kPlanThreads / 64) s_w[lane] = x - v;
+    if (lane == kPlanThreads / 64 - 1) s_w[16] = x;
   }
   __syncthreads();
   int run = s_w[wave] + incl - local;
@@ -83,8 +96,35 @@ __device__ __forceinline__ int find_run(const int* a, int n, int v) {
   return lo;
 }
 
-// Single workgroup; every phase is parallel over experts, groups, bands,
-// segments or tiles, and every offset is an exclusive scan.
+// bump allocation of a role's tables in the kernel's LDS block
+template <class T>
+__device__ __forceinline__ T* carve(unsigned char*& p, int n) {
+  T* r = reinterpret_cast<T*>(p);
+  p += ((size_t)n * sizeof(T) + 15) / 16 * 16;
+  return r;
+}
+
+// the k-th remote owner of a group (ascending ranks, skipping r_self)
+__device__ __forceinline__ int remote_owner(int q, int r_self) { return q < r_self ? q : q + 1; }
+
+// Rank of expert e under rule (ii) of the band schedule ([TLS] sec. 3.2.2):
+// remote band count descending, then remote rows descending, then id. One
+// compare per expert pair; rank[] must be zero on entry.
+__device__ void rank_experts(const int* nrb, const int* nrr, int* rank, int* order, int El) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < El * El; i += kPlanThreads) {
+    const int e = i / El, f = i - (i / El) * El;
+    const bool before = nrb[f] > nrb[e] || (nrb[f] == nrb[e] && (nrr[f] > nrr[e] || (nrr[f] == nrr[e] && f < e)));
+    if (before) atomicAdd(&rank[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < El; e += kPlanThreads) order[rank[e]] = e;
+  __syncthreads();
+}
+
+// ---- role 0: the plan ----------------------------------------------------
+// Every phase is parallel over experts, groups, bands, segments or tiles,
+// and every offset is an exclusive scan.
 //  * groups (e, s) are indexed e * R + s (layout order inside an expert:
 //    remote owners ascending, then the local owner);
 //  * remote groups in schedule order are k = o (R - 1) + q: expert order[o]
@@ -92,26 +132,20 @@ __device__ __forceinline__ int find_run(const int* a, int n, int v) {
 //  * bands: the remote groups' bands in schedule order, then the local
 //    bands by expert id (rule (i)); segments: per remote group 1, mgb, ...,
 //    mgb, (remainder), 1 bands.
-__global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict__ counts, moe_plan_t p,
-                                                        u32x4* __restrict__ zero_row, const moe_calib_t calib,
-                                                        int R, int El, int r_self, int tb, int mgb, int H,
-                                                        int F) {
-  __shared__ int s_cnt[kPlanMaxGroups];
-  __shared__ int s_rel[kPlanMaxGroups];            // group start relative to its expert base
-  __shared__ int s_goff[2 * kPlanMaxGroups + 1];   // remote groups (schedule order): bands | segments
-  __shared__ int s_eoff[5 * kPlanMaxEl + 1];       // per expert: rows | tiles | local bands | remote tiles | other tiles
-  __shared__ int s_alg[kPlanMaxEl];                // tb-aligned rows of expert e
-  __shared__ int s_nrb[kPlanMaxEl], s_nrr[kPlanMaxEl], s_rank[kPlanMaxEl], s_order[kPlanMaxEl];
-  __shared__ int s_trpos[kPlanMaxEl];              // schedule position of e's first remote tile
-  __shared__ int s_w[17];
-  __shared__ double s_tt[kPartPos];      // model: instance time of the row tile at each position
-  __shared__ double s_wv[kPartWaves];    // model: wave lengths, then wave ends, per candidate
-  __shared__ int s_spos[kPartSegs];      // model: position of each segment's last row tile
-  __shared__ int s_sfrom[kPartSegs];     // model: valid rows of segments i, i+1, ...
-  __shared__ int s_woff[kPartCand + 1];  // model: first wave of each candidate
-  __shared__ double s_tprod[kPartCand];
-  __shared__ double s_total[kPartCand];
-  __shared__ int s_fit;
+//  * padding rows of every band slot (past its valid rows) get row_src = -1.
+__device__ void plan_role(const int32_t* __restrict__ counts, moe_plan_t p, u32x4* __restrict__ zero_row,
+                          int R, int El, int r_self, int tb, int mgb, int H, unsigned char* smem) {
+  int* s_cnt = carve<int>(smem, kPlanMaxGroups);
+  int* s_rel = carve<int>(smem, kPlanMaxGroups);          // group start relative to its expert base
+  int* s_goff = carve<int>(smem, 2 * kPlanMaxGroups + 1);  // remote groups (schedule order): bands | segments
+  int* s_eoff = carve<int>(smem, 5 * kPlanMaxEl + 1);      // per expert: rows | tiles | local bands | remote tiles | other tiles
+  int* s_alg = carve<int>(smem, kPlanMaxEl);               // tb-aligned rows of expert e
+  int* s_nrb = carve<int>(smem, kPlanMaxEl);
+  int* s_nrr = carve<int>(smem, kPlanMaxEl);
+  int* s_rank = carve<int>(smem, kPlanMaxEl);
+  int* s_order = carve<int>(smem, kPlanMaxEl);
+  int* s_trpos = carve<int>(smem, kPlanMaxEl);             // schedule position of e's first remote tile
+  int* s_w = carve<int>(smem, 17);
   const int tid = threadIdx.x;
   const int G = El * R, Rr = R - 1, K = El * Rr;
   const int tsh = __ffs(tb) - 1;   // tb is a power of two
@@ -125,7 +159,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   for (int e = tid; e < El; e += kPlanThreads) {
     int rel = 0, nrb = 0, nrr = 0;
     for (int q = 0; q < R; ++q) {           // remote owners ascending, then the local owner
-      const int s = (q < Rr) ? (q < r_self ? q : q + 1) : r_self;
+      const int s = (q < Rr) ? remote_owner(q, r_self) : r_self;
       const int c = s_cnt[e * R + s];
       s_rel[e * R + s] = rel;
       if (s != r_self) {
@@ -149,16 +183,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
     p.recv_off[s * El + e] = acc;
   }
   __syncthreads();
-  // rule (ii): rank of expert e under (remote bands desc, remote rows desc, id asc)
-  for (int i = tid; i < El * El; i += kPlanThreads) {
-    const int e = i / El, f = i - (i / El) * El;
-    const bool before = s_nrb[f] > s_nrb[e] ||
-                        (s_nrb[f] == s_nrb[e] && (s_nrr[f] > s_nrr[e] || (s_nrr[f] == s_nrr[e] && f < e)));
-    if (before) atomicAdd(&s_rank[e], 1);
-  }
-  __syncthreads();
-  for (int e = tid; e < El; e += kPlanThreads) s_order[s_rank[e]] = e;
-  __syncthreads();
+  rank_experts(s_nrb, s_nrr, s_rank, s_order, El);
 
   // per-expert offsets, one scan over five concatenated runs
   for (int e = tid; e < El; e += kPlanThreads) {
@@ -172,13 +197,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   // per remote group in schedule order: bands | segments
   for (int k = tid; k < K; k += kPlanThreads) {
     const int o = k / Rr, q = k - (k / Rr) * Rr;
-    const int e = s_order[o], s = q < r_self ? q : q + 1;
+    const int e = s_order[o], s = remote_owner(q, r_self);
     const int nb = (s_cnt[e * R + s] + tb - 1) >> tsh;
     s_goff[k] = nb;
     s_goff[K + k] = nseg_of(nb, mgb);
   }
   __syncthreads();
-  const int etot = block_exscan(s_eoff, 5 * El, s_w);
+  block_exscan(s_eoff, 5 * El, s_w);
   const int gtot = block_exscan(s_goff, 2 * K, s_w);
   const int* e_base = s_eoff;                   // first packed row of expert e
   const int m_pad = s_eoff[El];
@@ -189,7 +214,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   const int n_remote = K > 0 ? s_goff[K] : 0;   // remote bands
   const int n_seg = gtot - n_remote;
   const int n_bands = n_remote + (s_eoff[3 * El] - s_eoff[2 * El]);
-  (void)etot;
   for (int e = tid; e < El; e += kPlanThreads)
     s_trpos[e] = s_eoff[3 * El + s_rank[e]] - s_eoff[3 * El];
   if (tid == 0) {
@@ -204,7 +228,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   for (int e = tid; e <= El; e += kPlanThreads) p.expert_base[e] = e < El ? e_base[e] : m_pad;
   __syncthreads();
 
-  // one pass: row tiles, groups, bands, segments
+  // one pass: row tiles, groups, bands (with their padding rows), segments
   const int n_work = n_tiles + G + n_bands + n_seg;
   for (int i = tid; i < n_work; i += kPlanThreads) {
     if (i < n_tiles) {
@@ -231,8 +255,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
       if (b < n_remote) {
         const int k = find_run(s_goff, K, b);
         e = s_order[k / Rr];
-        const int q = k - (k / Rr) * Rr;
-        s = q < r_self ? q : q + 1;
+        s = remote_owner(k - (k / Rr) * Rr, r_self);
         j = b - s_goff[k];
       } else {
         const int lb = b - n_remote + e_loff[0];
@@ -249,13 +272,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
       p.band_recv0[b] = (s != r_self) ? p.recv_off[s * El + e] + (j << tsh) : -1;
       p.band_valid[b] = valid;
       p.slot_valid[row0 >> tsh] = valid;
+      // the band slot's rows past its valid ones are padding (zero rows);
+      // the slots tile [0, m_pad), so this marks every padding row once
+      for (int r = valid; r < tb; ++r) p.row_src[row0 + r] = -1;
       continue;
     }
     const int sg = w - n_bands;
     const int k = find_run(s_goff + K, K, sg + n_remote);
     const int e = s_order[k / Rr];
-    const int q = k - (k / Rr) * Rr;
-    const int s = q < r_self ? q : q + 1;
+    const int s = remote_owner(k - (k / Rr) * Rr, r_self);
     const int c = s_cnt[e * R + s];
     const int nb = (c + tb - 1) >> tsh;
     const int ns = nseg_of(nb, mgb);
@@ -281,32 +306,109 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   auto units = [&](int sg) {
     return (int)(((long)p.seg_rows[sg] * H * 2 + kCopyUnitBytes - 1) / kCopyUnitBytes);
   };
-  {
-    int local = 0;
-    for (int sg = lo; sg < hi; ++sg) local += units(sg);
-    int incl = local;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += y;
-    }
-    if (lane == 63) s_w[wave] = incl;
-    __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      for (int w = 0; w < kPlanThreads / 64; ++w) { const int v = s_w[w]; s_w[w] = acc; acc += v; }
-      p.meta[META_NUNITS] = acc;
-    }
-    __syncthreads();
-    int acc = s_w[wave] + incl - local;
-    for (int sg = lo; sg < hi; ++sg) { p.seg_unit0[sg] = acc; acc += units(sg); }
+  int local = 0;
+  for (int sg = lo; sg < hi; ++sg) local += units(sg);
+  int incl = local;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
   }
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int v = lane < kPlanThreads / 64 ? s_w[lane] : 0;
+    int x = v;
+    for (int d = 1; d < kPlanThreads / 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane < kPlanThreads / 64) s_w[lane] = x - v;
+    if (lane == kPlanThreads / 64 - 1) p.meta[META_NUNITS] = x;
+  }
+  __syncthreads();
+  int acc = s_w[wave] + incl - local;
+  for (int sg = lo; sg < hi; ++sg) { p.seg_unit0[sg] = acc; acc += units(sg); }
+}
 
-  // ---- the CU-split model (partition_model.hpp) for this plan's row tiles
-  // and segments, the same closed form as moe_plan_partition
-  const int n_pos = n_tiles;
+// ---- role 1: the CU-split model (partition_model.hpp) --------------------
+// The model of moe_plan_partition, evaluated from the counts in the same
+// closed form and order (bit-identical predictions): the GEMM's row tiles in
+// schedule order and the segments in band-schedule order, derived here from
+// the counts as the plan derives them, then per candidate c the producer's
+// wave ends and the copy's end. Writes META_CAUTO and META_PRED; past its
+// table bounds it takes calib.c_min with META_PRED = -1.
+__device__ void model_role(const int32_t* __restrict__ counts, moe_plan_t p, const moe_calib_t calib, int R,
+                           int El, int r_self, int tb, int mgb, int H, int F, unsigned char* smem) {
+  int* s_cnt = carve<int>(smem, kPlanMaxGroups);
+  int* s_rel = carve<int>(smem, kPlanMaxGroups);    // group start relative to its expert base
+  // one scan over three runs: remote row tiles by rank | other row tiles by
+  // expert | segments per remote group (schedule order)
+  int* s_sc = carve<int>(smem, 2 * kPlanMaxEl + kPlanMaxGroups + 1);
+  int* s_me = carve<int>(smem, kPlanMaxEl);         // packed rows of expert e
+  int* s_nrb = carve<int>(smem, kPlanMaxEl);
+  int* s_nrr = carve<int>(smem, kPlanMaxEl);
+  int* s_rank = carve<int>(smem, kPlanMaxEl);
+  int* s_order = carve<int>(smem, kPlanMaxEl);
+  int* s_trpos = carve<int>(smem, kPlanMaxEl);      // schedule position of e's first remote tile
+  int* s_w = carve<int>(smem, 17);
+  double* s_tt = carve<double>(smem, kPartPos);     // instance time of the row tile at each position
+  double* s_wv = carve<double>(smem, kPartWaves);   // wave lengths, then wave ends, per candidate
+  int* s_spos = carve<int>(smem, kPartSegs);        // position of each segment's last row tile
+  int* s_sfrom = carve<int>(smem, kPartSegs);       // valid rows of segments i, i+1, ...
+  int* s_woff = carve<int>(smem, kPartCand + 1);    // first wave of each candidate
+  double* s_tprod = carve<double>(smem, kPartCand);
+  double* s_total = carve<double>(smem, kPartCand);
+  int* s_fit = carve<int>(smem, 1);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = El * R, Rr = R - 1, K = El * Rr;
+  const int tsh = __ffs(tb) - 1;
+  int* s_rt = s_sc;             // schedule position of rank r's first remote tile
+  int* s_lt = s_sc + El;        // schedule position of expert e's first other tile
+  int* s_gseg = s_sc + 2 * El;  // + n_pos: first segment of remote group k
+  for (int i = tid; i < G; i += kPlanThreads) s_cnt[i] = counts[i];
+  for (int e = tid; e < El; e += kPlanThreads) s_rank[e] = 0;
+  __syncthreads();
+  for (int e = tid; e < El; e += kPlanThreads) {
+    int rel = 0, nrb = 0, nrr = 0;
+    for (int q = 0; q < R; ++q) {
+      const int s = (q < Rr) ? remote_owner(q, r_self) : r_self;
+      const int c = s_cnt[e * R + s];
+      s_rel[e * R + s] = rel;
+      if (s != r_self) {
+        const int nb = (c + tb - 1) >> tsh;
+        rel += nb << tsh;
+        nrb += nb;
+        nrr += c;
+      } else {
+        rel += c;
+      }
+    }
+    s_me[e] = rel;
+    s_nrb[e] = nrb;
+    s_nrr[e] = nrr;
+  }
+  __syncthreads();
+  rank_experts(s_nrb, s_nrr, s_rank, s_order, El);
+  for (int r = tid; r < El; r += kPlanThreads) {
+    const int e = s_order[r];
+    s_rt[r] = ceil_div(s_nrb[e] << tsh, kTileM);   // row tiles holding a remote band
+  }
+  for (int e = tid; e < El; e += kPlanThreads) {
+    const int alg = ((s_me[e] + tb - 1) >> tsh) << tsh;
+    s_lt[e] = ceil_div(alg, kTileM) - ceil_div(s_nrb[e] << tsh, kTileM);
+  }
+  for (int k = tid; k < K; k += kPlanThreads) {
+    const int e = s_order[k / Rr], s = remote_owner(k - (k / Rr) * Rr, r_self);
+    s_gseg[k] = nseg_of((s_cnt[e * R + s] + tb - 1) >> tsh, mgb);
+  }
+  __syncthreads();
+  const int sc_total = block_exscan(s_sc, 2 * El + K, s_w);
+  const int n_rpos = s_sc[El];
+  const int n_pos = K > 0 ? s_sc[2 * El] : sc_total;
+  const int n_seg = sc_total - n_pos;
+  for (int r = tid; r < El; r += kPlanThreads) s_trpos[s_order[r]] = s_rt[r];
   const int tiles2 = (H + kModelTileCols - 1) / kModelTileCols;
   const int n_cand = (calib.c_max - calib.c_min) / calib.c_step + 1;
-  __syncthreads();   // s_w is reused below
   if (tid == 0) {
     int fit = n_pos <= kPartPos && n_seg <= kPartSegs && n_cand >= 1 && n_cand <= kPartCand;
     int w = 0;
@@ -317,31 +419,46 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
       if (w > kPartWaves) fit = 0;
     }
     if (fit) s_woff[n_cand] = w;
-    s_fit = fit;
+    *s_fit = fit;
   }
   __syncthreads();
-  if (!s_fit) {
+  if (!*s_fit) {
     if (tid == 0) {
       p.meta[META_CAUTO] = calib.c_min;
       *reinterpret_cast<double*>(p.meta + META_PRED) = -1.0;
     }
     return;
   }
-  for (int q = tid; q < n_pos; q += kPlanThreads) {   // instance time per schedule position
-    const int rt = p.tile_sched[q];
-    const int e = p.tile_expert[rt];
-    const long m_e = (long)s_rel[e * R + r_self] + s_cnt[e * R + r_self];   // the local group is last
-    s_tt[q] = model_tile_time(p.tile_rows[rt], F, model_rate(calib, m_e));
+  // instance time per schedule position: the remote-holding tiles of the
+  // experts in rank order, then the other tiles by expert id
+  for (int q = tid; q < n_pos; q += kPlanThreads) {
+    int e, j;
+    if (q < n_rpos) {
+      const int r = find_run(s_rt, El, q);
+      e = s_order[r];
+      j = q - s_rt[r];
+    } else {
+      e = find_run(s_lt, El, q);
+      j = ceil_div(s_nrb[e] << tsh, kTileM) + (q - s_lt[e]);
+    }
+    const int alg = ((s_me[e] + tb - 1) >> tsh) << tsh;
+    s_tt[q] = model_tile_time(min(kTileM, alg - j * kTileM), F, model_rate(calib, s_me[e]));
   }
-  // segments: position of the last row tile (remote tiles of expert e sit at
-  // positions s_trpos[e] + j) and the valid rows from each segment on
-  // (integers: the total minus an exclusive prefix)
+  // segments in schedule order: valid rows and the position of the last row tile
   for (int sg = tid; sg < n_seg; sg += kPlanThreads) {
-    const int e = p.band_expert[p.seg_band0[sg]];
-    s_spos[sg] = s_trpos[e] + (p.seg_tile1[sg] - (e_tbase[e] - m_pad));
-    s_sfrom[sg] = p.seg_rows[sg];
+    const int k = find_run(s_gseg, K, sg + n_pos);
+    const int e = s_order[k / Rr], s = remote_owner(k - (k / Rr) * Rr, r_self);
+    const int c = s_cnt[e * R + s];
+    const int nb = (c + tb - 1) >> tsh;
+    const int ns = nseg_of(nb, mgb);
+    const int qi = sg + n_pos - s_gseg[k];
+    const int j = qi == 0 ? 0 : (qi == ns - 1 ? nb - 1 : 1 + (qi - 1) * mgb);
+    const int sz = (qi == 0 || qi == ns - 1) ? 1 : min(mgb, nb - 1 - j);
+    s_sfrom[sg] = min(c - (j << tsh), sz << tsh);
+    s_spos[sg] = s_trpos[e] + (s_rel[e * R + s] + ((j + sz) << tsh) - 1) / kTileM;
   }
   __syncthreads();
+  // valid rows of segments i, i+1, ... (integers: the total minus an exclusive prefix)
   const int rtot = block_exscan(s_sfrom, n_seg, s_w);
   for (int sg = tid; sg < n_seg; sg += kPlanThreads) s_sfrom[sg] = rtot - s_sfrom[sg];
   // producer waves: lengths (maxima over the positions each wave covers)
@@ -397,69 +514,113 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict
   }
 }
 
-// index: every local (token, slot) -> its packed row; writes row_src and recv_row.
-// One block per routing chunk (<= 256 tokens of one source rank); thread = token.
-// Rank inside the (expert, owner) group = rows of earlier chunks + rows of
-// earlier waves of this chunk + earlier lanes of this wave. Each (token, slot)
-// sets its lane's bit in an LDS bitmap of expert e and its wave (tokens hold
-// distinct experts), so a rank is one popcount; the chunk's group bases sit
-// in LDS. The blocks also mark every padding row of [0, m_pad) (row_src = -1;
-// a row is padding unless it is one of the valid rows of its band slot),
-// rows grid-stride: disjoint from the rows the tokens fill.
-__global__ __launch_bounds__(256) void k_gather_index(const int32_t* __restrict__ ids, moe_plan_t p,
-                                                       int R, int T, int k, int El, int first_local,
-                                                       int r_self, int chunks_per_rank, int tb) {
-  __shared__ unsigned long long s_bits[kPlanMaxEl][4];   // tokens of this chunk per (expert, wave)
-  __shared__ int s_wbase[kPlanMaxEl][4];                 // rows before (expert, wave) in the group
-  __shared__ int s_gr[kPlanMaxEl];   // first packed row of group (e, s)
-  __shared__ int s_ro[kPlanMaxEl];   // first combine-buffer row of group (e, s)
-  const int chunk = blockIdx.x;
-  const int s = chunk / chunks_per_rank;
-  const int t0 = (chunk % chunks_per_rank) * kChunk;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t = t0 + tid;
-  const bool active = t < T;
-  const int g = s * T + (active ? t : 0);
-  for (int i = tid; i < El * 4; i += blockDim.x) s_bits[i >> 2][i & 3] = 0ull;
-  for (int e = tid; e < El; e += blockDim.x) {
-    s_wbase[e][0] = p.chunk_base[chunk * El + e];
-    s_gr[e] = p.group_row[e * R + s];
-    s_ro[e] = p.recv_off[s * El + e];
+// ---- role 2: the index of the routed rows ---------------------------------
+// Every local (token, slot) -> its packed row; writes row_src (valid rows) and
+// recv_row. A block serves kIndexChunks routing chunks (<= 256 tokens of one
+// source rank), 256 threads each, thread = token. Rank inside the (expert,
+// owner) group = rows of earlier chunks (chunk_base) + rows of earlier waves
+// of this chunk + earlier lanes of this wave. Each (token, slot) sets its
+// lane's bit in an LDS bitmap of expert e and its wave (tokens hold distinct
+// experts), so a rank is one popcount. The group bases come from the counts
+// (the plan's layout arithmetic: owner groups remote-ascending then local,
+// remote groups padded to tb, experts at tb-aligned bases).
+constexpr int kIndexChunks = kPlanThreads / 256;
+__device__ void index_role(int first_chunk, const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
+                           moe_plan_t p, int R, int T, int k, int El, int r_self, int chunks_per_rank,
+                           int n_chunks, int tb, unsigned char* smem) {
+  int* s_cnt = carve<int>(smem, kPlanMaxGroups);
+  int* s_gr = carve<int>(smem, kPlanMaxGroups);     // [e * R + s]: first packed row of group (e, s)
+  int* s_ro = carve<int>(smem, kPlanMaxGroups);     // [s * El + e]: first combine-buffer row of (e, s)
+  int* s_base = carve<int>(smem, kPlanMaxEl + 1);   // expert bases
+  int* s_w = carve<int>(smem, 17);
+  unsigned long long* s_bits = carve<unsigned long long>(smem, kIndexChunks * kPlanMaxEl * 4);
+  int* s_wbase = carve<int>(smem, kIndexChunks * kPlanMaxEl * 4);
+  const int tid = threadIdx.x;
+  const int G = El * R, Rr = R - 1;
+  const int tsh = __ffs(tb) - 1;
+  const int first_local = r_self * El;
+  for (int i = tid; i < G; i += kPlanThreads) s_cnt[i] = counts[i];
+  for (int i = tid; i < kIndexChunks * kPlanMaxEl * 4; i += kPlanThreads) s_bits[i] = 0ull;
+  __syncthreads();
+  for (int e = tid; e < El; e += kPlanThreads) {
+    int rel = 0;
+    for (int q = 0; q < R; ++q) {
+      const int s = (q < Rr) ? remote_owner(q, r_self) : r_self;
+      const int c = s_cnt[e * R + s];
+      s_gr[e * R + s] = rel;
+      rel += (s != r_self) ? ((c + tb - 1) >> tsh) << tsh : c;
+    }
+    s_base[e] = ((rel + tb - 1) >> tsh) << tsh;
   }
+  for (int s = tid; s < R; s += kPlanThreads) {
+    int acc = 0;
+    for (int e = 0; e < El; ++e) { s_ro[s * El + e] = acc; acc += s_cnt[e * R + s]; }
+  }
+  __syncthreads();
+  block_exscan(s_base, El, s_w);
+  for (int i = tid; i < G; i += kPlanThreads) s_gr[i] += s_base[i / R];
+  // this thread's chunk and token
+  const int grp = tid >> 8, lt = tid & 255, wave = lt >> 6, lane = tid & 63;
+  const int chunk = first_chunk + grp;
+  const bool have = chunk < n_chunks;
+  const int s = have ? chunk / chunks_per_rank : 0;
+  const int t = (have ? (chunk % chunks_per_rank) * kChunk : 0) + lt;
+  const bool active = have && t < T;
+  const int g = s * T + (active ? t : 0);
+  unsigned long long* bits = s_bits + grp * kPlanMaxEl * 4;
+  int* wbase = s_wbase + grp * kPlanMaxEl * 4;
+  if (have)
+    for (int e = lt; e < El; e += 256) wbase[e * 4] = p.chunk_base[chunk * El + e];
   // unconditional loads with clamped indices (predicated ones would each wait
   // for the previous), then the selection
   int my[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) my[j] = ids[g * k + (j < k ? j : k - 1)] - first_local;
+  for (int j = 0; j < 16; ++j) my[j] = ids[(size_t)g * k + (j < k ? j : k - 1)] - first_local;
 #pragma unroll
   for (int j = 0; j < 16; ++j) my[j] = (active && j < k && my[j] >= 0 && my[j] < El) ? my[j] : -1;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    if (my[j] >= 0) atomicOr(&s_bits[my[j]][wave], 1ull << lane);
+    if (my[j] >= 0) atomicOr(&bits[my[j] * 4 + wave], 1ull << lane);
   __syncthreads();
-  for (int e = tid; e < El; e += blockDim.x) {   // prefix over the 4 waves
-    int acc = s_wbase[e][0];
-    for (int w = 0; w < 4; ++w) { s_wbase[e][w] = acc; acc += __popcll(s_bits[e][w]); }
-  }
+  if (have)
+    for (int e = lt; e < El; e += 256) {   // prefix over the 4 waves
+      int acc = wbase[e * 4];
+      for (int w = 0; w < 4; ++w) { wbase[e * 4 + w] = acc; acc += __popcll(bits[e * 4 + w]); }
+    }
   __syncthreads();
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t ltm = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (!active || j >= k) continue;
     const int e = my[j];
     if (e < 0) {   // expert not local
-      p.recv_row[g * k + j] = -1;
+      p.recv_row[(size_t)g * k + j] = -1;
       continue;
     }
-    const int rank = s_wbase[e][wave] + __popcll(s_bits[e][wave] & lt);
-    const int row = s_gr[e] + rank;
+    const int rank = wbase[e * 4 + wave] + __popcll(bits[e * 4 + wave] & ltm);
+    const int row = s_gr[e * R + s] + rank;
     p.row_src[row] = g;
-    p.recv_row[g * k + j] = (s == r_self) ? row : s_ro[e] + rank;
+    p.recv_row[(size_t)g * k + j] = (s == r_self) ? row : s_ro[s * El + e] + rank;
   }
-  const int m_pad = p.meta[META_MPAD];
-  for (int r = blockIdx.x * 256 + tid; r < m_pad; r += gridDim.x * 256)
-    if ((r % tb) >= p.slot_valid[r / tb]) p.row_src[r] = -1;
+}
+
+// LDS of the plan kernel: the largest of the three roles' tables
+constexpr size_t kPlanLdsBytes = 88 * 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ ids, moe_plan_t p,
+                                                        u32x4* __restrict__ zero_row, const moe_calib_t calib,
+                                                        int R, int T, int k, int El, int r_self, int tb, int mgb,
+                                                        int H, int F, int chunks_per_rank, int n_chunks) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPlanLdsBytes];
+  if (blockIdx.x == 0)
+    plan_role(counts, p, zero_row, R, El, r_self, tb, mgb, H, smem);
+  else if (blockIdx.x == 1)
+    model_role(counts, p, calib, R, El, r_self, tb, mgb, H, F, smem);
+  else
+    index_role((blockIdx.x - 2) * kIndexChunks, ids, counts, p, R, T, k, El, r_self, chunks_per_rank, n_chunks,
+               tb, smem);
 }
 
 // copy: row r of [0, m_pad) gets x of token row_src[r] when it is one of the
@@ -489,19 +650,18 @@ __global__ __launch_bounds__(256) void k_gather_copy(const uint16_t* __restrict_
   }
 }
 
-hipError_t launch_plan(const Geometry& g, const int32_t* counts, const moe_plan_t& p, uint16_t* zero_row,
-                       const moe_calib_t& calib, hipStream_t st) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, st, counts, p, reinterpret_cast<u32x4*>(zero_row), calib,
-                     g.R, g.El, g.r_self, g.tb_m, g.mgb, g.H, g.F);
+hipError_t launch_plan(const Geometry& g, const int32_t* counts, const int32_t* ids, const moe_plan_t& p,
+                       uint16_t* zero_row, const moe_calib_t& calib, hipStream_t st) {
+  const int grid = 2 + (g.n_chunks + kIndexChunks - 1) / kIndexChunks;
+  hipLaunchKernelGGL(k_plan, dim3(grid), dim3(kPlanThreads), 0, st, counts, ids, p,
+                     reinterpret_cast<u32x4*>(zero_row), calib, g.R, g.T, g.k, g.El, g.r_self, g.tb_m, g.mgb, g.H,
+                     g.F, g.chunks_per_rank, g.n_chunks);
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const Geometry& g, const uint16_t* x, const int32_t* ids,
-                         uint16_t* x_perm, const moe_plan_t& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_gather_index, dim3(g.n_chunks), dim3(256), 0, st, ids, p, g.R, g.T, g.k, g.El,
-                     g.r_self * g.El, g.r_self, g.chunks_per_rank, g.tb_m);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || x_perm == nullptr) return err;
+hipError_t launch_gather(const Geometry& g, const uint16_t* x, uint16_t* x_perm, const moe_plan_t& p,
+                         hipStream_t st) {
+  if (x_perm == nullptr) return hipSuccess;
   // grid-stride over at most m_pad_max rows, four rows per block
   const int64_t blocks = (g.m_pad_max + 3) / 4;
   const int grid = (int)(blocks < 4096 ? blocks : 4096);

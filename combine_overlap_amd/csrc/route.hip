@@ -15,9 +15,9 @@
 // CU has many tokens' loads in flight.
 //
 // k_chunk_hist: per routing chunk (kChunk tokens of one source rank), how
-// many of its (token, slot) pairs chose each local expert; k_count turns the
-// chunk histograms into counts[e][s] and each chunk's first row inside its
-// (e, s) group (the gather ranks rows by token inside a group).
+// many of its (token, slot) pairs chose each local expert; its last block
+// turns the chunk histograms into counts[e][s] and each chunk's first row
+// inside its (e, s) group (the index ranks rows by token inside a group).
 #include "common.hpp"
 
 namespace moe {
@@ -38,7 +38,10 @@ template <int G, int NQ>
 __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict__ logits,
                                                           int32_t* __restrict__ ids_out,
                                                           float* __restrict__ gates_out,
+                                                          int32_t* __restrict__ hist_arrivals,
                                                           int n_tok, int E, int k, int gate_kind) {
+  // the next launch's arrival counter (k_chunk_hist) starts from zero
+  if (blockIdx.x == 0 && threadIdx.x == 0) *hist_arrivals = 0;
   const int lane = threadIdx.x & 63;
   const int gi = lane & (G - 1);                         // lane inside the routing group
   constexpr int per_block = kRouteThreads / G;
@@ -122,11 +125,17 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
   }
 }
 
-// per chunk: local-expert histogram of its tokens' selected ids
-__global__ __launch_bounds__(256) void k_chunk_hist(const int32_t* __restrict__ ids,
-                                                     int32_t* __restrict__ chunk_counts, int T, int k,
-                                                     int El, int first_local, int chunks_per_rank) {
+// Per chunk: the local-expert histogram of its tokens' selected ids. The
+// last block to finish (an arrival counter that k_route zeroed) then turns
+// the chunk histograms into counts[e][s] and each chunk's first row inside
+// its (e, s) group (the index ranks rows by token inside a group): one
+// launch instead of a histogram launch and a one-workgroup count launch.
+__global__ __launch_bounds__(256) void k_chunk_hist(const int32_t* __restrict__ ids, int32_t* __restrict__ chunk_counts,
+                                                     int32_t* __restrict__ chunk_base, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ arrivals, int T, int k, int R, int El,
+                                                     int first_local, int chunks_per_rank) {
   __shared__ int cnt[kPlanMaxElRoute];
+  __shared__ int s_last;
   const int chunk = blockIdx.x;
   const int s = chunk / chunks_per_rank;
   const int t0 = (chunk % chunks_per_rank) * kChunk;
@@ -140,35 +149,41 @@ __global__ __launch_bounds__(256) void k_chunk_hist(const int32_t* __restrict__ 
     if (el >= 0 && el < El) atomicAdd(&cnt[el], 1);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < El; i += blockDim.x) chunk_counts[chunk * El + i] = cnt[i];
-}
-
-// counts[e][s] and the exclusive per-chunk row offsets inside each (e, s) group
-__global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ chunk_counts,
-                                                int32_t* __restrict__ chunk_base,
-                                                int32_t* __restrict__ counts, int R, int El,
-                                                int chunks_per_rank) {
-  for (int p = threadIdx.x; p < El * R; p += blockDim.x) {
-    const int e = p / R, s = p % R;
+  // device-scope stores: they write through this XCD's L2, so the last block
+  // (on any XCD) reads them with device-scope loads once it has seen every
+  // arrival, which each block counts after its stores have completed
+  for (int i = threadIdx.x; i < El; i += blockDim.x)
+    __hip_atomic_store(chunk_counts + chunk * El + i, cnt[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  // counts[e][s] and the exclusive per-chunk row offsets inside each (e, s) group
+  for (int pp = threadIdx.x; pp < El * R; pp += blockDim.x) {
+    const int e = pp / R, q = pp % R;
     int acc = 0;
     for (int c0 = 0; c0 < chunks_per_rank; c0 += 8) {   // 8 loads in flight, then the 8 stores
       int v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        v[u] = c0 + u < chunks_per_rank ? chunk_counts[(s * chunks_per_rank + c0 + u) * El + e] : 0;
+        v[u] = c0 + u < chunks_per_rank
+                   ? __hip_atomic_load(chunk_counts + (q * chunks_per_rank + c0 + u) * El + e, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (c0 + u < chunks_per_rank) chunk_base[(s * chunks_per_rank + c0 + u) * El + e] = acc;
+        if (c0 + u < chunks_per_rank) chunk_base[(q * chunks_per_rank + c0 + u) * El + e] = acc;
         acc += v[u];
       }
     }
-    counts[e * R + s] = acc;
+    counts[e * R + q] = acc;
   }
 }
 
 hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, float* gates,
                         const moe_plan_t& p, hipStream_t st) {
-  (void)p;
   // group width: the fewest lanes with at most 32 logits each (E <= 512: G <= 16)
   int G = 1;
   while (G * 32 < g.E) G <<= 1;
@@ -179,8 +194,8 @@ hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, fl
   dim3 grid((n_tok + per_block - 1) / per_block), block(kRouteThreads);
 #define MOE_ROUTE_CASE(GG, QQ)                                                                 \
   if (G == GG && NQ == QQ) {                                                                   \
-    hipLaunchKernelGGL((k_route<GG, QQ>), grid, block, 0, st, logits, ids, gates, n_tok, g.E, g.k, \
-                       g.gate_kind);                                                           \
+    hipLaunchKernelGGL((k_route<GG, QQ>), grid, block, 0, st, logits, ids, gates, p.meta + META_HISTCTR, \
+                       n_tok, g.E, g.k, g.gate_kind);                                          \
     return hipGetLastError();                                                                  \
   }
   MOE_ROUTE_CASE(1, 8)
@@ -196,10 +211,8 @@ hipError_t launch_route(const Geometry& g, const float* logits, int32_t* ids, fl
 
 hipError_t launch_count(const Geometry& g, const int32_t* ids, int32_t* counts, const moe_plan_t& p,
                         hipStream_t st) {
-  hipLaunchKernelGGL(k_chunk_hist, dim3(g.n_chunks), dim3(256), 0, st, ids, p.chunk_counts, g.T, g.k,
-                     g.El, g.r_self * g.El, g.chunks_per_rank);
-  hipLaunchKernelGGL(k_count, dim3(1), dim3(256), 0, st, p.chunk_counts, p.chunk_base, counts,
-                     g.R, g.El, g.chunks_per_rank);
+  hipLaunchKernelGGL(k_chunk_hist, dim3(g.n_chunks), dim3(256), 0, st, ids, p.chunk_counts, p.chunk_base, counts,
+                     p.meta + META_HISTCTR, g.T, g.k, g.R, g.El, g.r_self * g.El, g.chunks_per_rank);
   return hipGetLastError();
 }
 

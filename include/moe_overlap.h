@@ -118,7 +118,8 @@ typedef struct {
                              [8]=consumer CUs chosen by the plan (MOE_CONSUMER_AUTO)
                              [20..21]=its predicted time in seconds (a double; -1 if
                              the device evaluation fell back to c_min)
-                             [16..19]=internal clock stamps of the overlapped forward */
+                             [16..19]=internal clock stamps of the overlapped forward
+                             [22]=internal: arrivals of the routing histogram */
   int32_t* group_row;     /* [E_l*R] first packed row of group (e, s)                */
   int32_t* expert_base;   /* [E_l+1] first packed row of expert e, tb_m-aligned      */
   int32_t* recv_off;      /* [R*E_l] first row of (e, s) in rank s's combine buffer */
