@@ -72,6 +72,8 @@ def parse(argv=None):
     ap.add_argument("--timeline", default="",
                     help="write a device-timeline summary (markdown) of the headline workload's CU-partition "
                          "expert phase to this path")
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip timing the vendor library's dense GEMM at the projections' shapes")
     ap.add_argument("--table2-sweep", action="store_true",
                     help="the shape sweep of the tile-signalling paper's Table 2 on this GPU (tokens per "
                          "rank 8192/16384, K = 2048, N = 4096/8192, experts per rank 4..64, three router "
@@ -339,6 +341,37 @@ def timeline(sh, torch, path, name, mode_overlap):
     log(f"[bench] timeline written to {path}")
 
 
+def vendor_dense_gemm(torch, m_pad, H, F, gated, reps=10):
+    """Context for the grouped GEMM: torch.mm (the vendor BLAS) on dense bf16
+    operands with the same row count (the padded rows) and the projections'
+    K and N, weights stored [N, K] as in the share. One dense matrix, no
+    expert boundaries, no flags: the rate the vendor's tuned kernels reach on
+    this chip at this size, not a target of the path."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    out = {}
+    for name, K, N in (("first_projection", H, (2 if gated else 1) * F), ("output_projection", F, H)):
+        a = (torch.randn(m_pad, K, device=dev, generator=g) * 0.05).to(torch.bfloat16)
+        b = (torch.randn(N, K, device=dev, generator=g) * 0.05).to(torch.bfloat16)
+        for _ in range(3):
+            torch.mm(a, b.t())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            torch.mm(a, b.t())
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        out[name] = {"m_k_n": [m_pad, K, N], "ms": round(ms, 4),
+                     "tflops_executed": round(2.0 * m_pad * K * N / ms / 1e9, 1)}
+        del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_workload(wid, args, torch, want_cpu, headline):
     from synth import WORKLOADS, make_logits, make_x, make_local_weights
     from synth.workloads import ShareInputs
@@ -513,6 +546,17 @@ def bench_workload(wid, args, torch, want_cpu, headline):
         log(f"[bench] {w.name}: layer sweep totals " + json.dumps(out["layer_sweep"]["total_ms"]))
     del sh
     torch.cuda.empty_cache()
+    if not args.no_vendor_gemm:
+        # the same padded rows through this path's GEMMs (sequential form), for comparison
+        s = ph[(b_fused, MOE_MODE_SEQUENTIAL)]
+        ours = {"first_projection": s["gemm1"], "output_projection": s["producer"]}
+        vg = vendor_dense_gemm(torch, m_pad, w.H, w.F, w.gated)
+        for name, v in vg.items():
+            K, N = v["m_k_n"][1], v["m_k_n"][2]
+            v["this_path_ms"] = round(ours[name], 4)
+            v["this_path_tflops_executed"] = round(2.0 * m_pad * K * N / ours[name] / 1e9, 1)
+        out["vendor_dense_gemm"] = vg
+        log(f"[bench] {w.name}: vendor dense GEMM at the same shapes " + json.dumps(vg))
     if want_cpu:
         log(f"[bench] {w.name}: timing the CPU oracle on the whole workload")
         out["cpu_baseline"] = cpu_baseline(w, inp, tb, layer)
@@ -661,7 +705,7 @@ def main(argv=None):
     }
     if "cpu_baseline" in h:
         out["cpu_baseline"] = h["cpu_baseline"]
-    for k in ("c_sweep", "layer_sweep"):
+    for k in ("c_sweep", "layer_sweep", "vendor_dense_gemm"):
         if k in h:
             out[k] = h[k]
     out["configs"] = {results[w]["workload"]: {k: v for k, v in results[w].items() if k != "workload"}
