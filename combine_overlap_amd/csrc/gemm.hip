@@ -55,7 +55,8 @@
 //    Each lane fetches the 16-byte chunk that belongs at its LDS slot under an
 //    XOR swizzle that keeps MFMA fragment reads free of bank conflicts. One
 //    barrier per k-step: wait for this wave's copies of stage kt, barrier,
-//    issue stage kt+NS-1 into the slot freed by stage kt-1, run the MFMAs.
+//    issue stage kt+NS-1 into the slot freed by stage kt-1 in two halves
+//    around the step's last MFMAs, run the MFMAs.
 //
 // Epilogues:
 //   EPI_PLAIN  C = A B^T (output projection y = h W2^T). With flags the tile
@@ -619,22 +620,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       bbase[i] = reinterpret_cast<const char*>(w) + ((size_t)e * a.Nw * K + (size_t)wrow * K) * 2;
     }
     const uint32_t lds0 = lds_addr(lds);
-    auto issue = [&](int kt) {
+    // this wave's DMA instructions q in [q0, q1) of stage kt: q < A_PW are its
+    // A rows, the rest its B rows
+    auto issue_part = [&](int kt, int q0, int q1) {
       const uint32_t st = lds0 + (uint32_t)((kt % NS) * C::STAGE * 2);
       const size_t ko = (size_t)(kb + kt) * BK * 2;
 #pragma unroll
-      for (int i = 0; i < C::A_PW; ++i) {
-        const int blk = wave_u * C::A_PW + i;
-        if constexpr (GATHER == 2) dma16_buf(aoff[i] + (uint32_t)ko, a_rsrc, st + (uint32_t)(blk * C::RPI * BK * 2));
-        else if constexpr (GATHER) dma16_v(abase[i] + ko, st + (uint32_t)(blk * C::RPI * BK * 2));
-        else dma16(abase[i] + ko, lane_off[blk & 1], st + (uint32_t)(blk * C::RPI * BK * 2));
-      }
-#pragma unroll
-      for (int i = 0; i < C::B_PW; ++i) {
-        const int blk = wave_u * C::B_PW + i;
-        dma16(bbase[i] + ko, lane_off[blk & 1], st + (uint32_t)((BM + blk * C::RPI) * BK * 2));
+      for (int q = 0; q < C::LPW; ++q) {
+        if (q < q0 || q >= q1) continue;
+        if (q < C::A_PW) {
+          const int blk = wave_u * C::A_PW + q;
+          if constexpr (GATHER == 2) dma16_buf(aoff[q] + (uint32_t)ko, a_rsrc, st + (uint32_t)(blk * C::RPI * BK * 2));
+          else if constexpr (GATHER) dma16_v(abase[q] + ko, st + (uint32_t)(blk * C::RPI * BK * 2));
+          else dma16(abase[q] + ko, lane_off[blk & 1], st + (uint32_t)(blk * C::RPI * BK * 2));
+        } else {
+          const int blk = wave_u * C::B_PW + (q - C::A_PW);
+          dma16(bbase[q - C::A_PW] + ko, lane_off[blk & 1], st + (uint32_t)((BM + blk * C::RPI) * BK * 2));
+        }
       }
     };
+    auto issue = [&](int kt) { issue_part(kt, 0, C::LPW); };
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -646,7 +651,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 
     // k-loop, software-pipelined:
     //  * all NS ring slots are in flight: stage kt+NS is issued into stage kt's
-    //    slot as soon as every wave has finished reading stage kt;
+    //    slot as soon as every wave has finished reading stage kt, half of a
+    //    wave's DMA instructions after the barrier and half after the step's
+    //    last MFMAs (one burst of all of them made the issuing waves queue
+    //    behind the texture path: the first projection took 4% longer at
+    //    K = 4096; a third or more of them in the next step, less time to land);
     //  * MFMA fragments are double-buffered: substep kk+1's fragments load
     //    while substep kk's MFMAs run;
     //  * the stage barrier sits before the last substep's MFMAs (whose
@@ -692,13 +701,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
           load_frags(kt, kk + 1, (kk + 1) & 1);
           mfmas(kk & 1, partial);
         }
+        const bool more = kt + NS < nkc;
         if (kt + 1 < nkc) {
           if (kt + NS <= nkc) wait_vm_barrier<(NS - 2) * C::LPW>();
           else wait_vm_barrier<0>();
-          if (kt + NS < nkc) issue(kt + NS);
+          if (more) issue_part(kt + NS, 0, C::LPW / 2);
           load_frags(kt + 1, 0, 0);
         }
         mfmas((KK - 1) & 1, partial);
+        if (more) issue_part(kt + NS, C::LPW / 2, C::LPW);
       }
     };
     if (fm_act == C::FM) kloop(std::false_type{});
