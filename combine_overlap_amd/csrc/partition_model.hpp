@@ -65,8 +65,10 @@ __host__ __device__ inline double model_tile_time(long rows, int F, double rate)
   return 2.0 * (double)((rows + 31) / 32 * 32) * (double)kModelTileCols * (double)F / rate;
 }
 
-// wave end after a wave of `len` holding n of P instances
-__host__ __device__ inline double model_wave_end(double t, double len, long n, long P) {
+// wave end after a wave of `len` holding n of P instances (I: long on the
+// host, int in the plan kernel, whose values fit; both give the same doubles)
+template <typename I>
+__host__ __device__ inline double model_wave_end(double t, double len, I n, I P) {
 #pragma clang fp contract(off)
   if (n >= P) return t + len;
   const double f = (double)n / (double)P;
@@ -91,9 +93,10 @@ __host__ __device__ inline double model_total(double t_prod, double t_copy, bool
 }
 
 // positions of row tiles covered by wave w of P instances (tiles2 per row tile)
-__host__ __device__ inline void model_wave_span(long w, long P, int tiles2, long n_pos, long* p0, long* p1) {
+template <typename I>
+__host__ __device__ inline void model_wave_span(I w, I P, int tiles2, I n_pos, I* p0, I* p1) {
   *p0 = w * P / tiles2;
-  const long last = ((w + 1) * P - 1) / tiles2;
+  const I last = ((w + 1) * P - 1) / tiles2;
   *p1 = last < n_pos - 1 ? last : n_pos - 1;
 }
 

@@ -409,17 +409,28 @@ __device__ void model_role(const int32_t* __restrict__ counts, moe_plan_t p, con
   for (int r = tid; r < El; r += kPlanThreads) s_trpos[s_order[r]] = s_rt[r];
   const int tiles2 = (H + kModelTileCols - 1) / kModelTileCols;
   const int n_cand = (calib.c_max - calib.c_min) / calib.c_step + 1;
-  if (tid == 0) {
-    int fit = n_pos <= kPartPos && n_seg <= kPartSegs && n_cand >= 1 && n_cand <= kPartCand;
-    int w = 0;
-    for (int ci = 0; fit && ci < n_cand; ++ci) {
-      const long P = calib.n_cu - (calib.c_min + ci * calib.c_step);
-      s_woff[ci] = w;
-      w += (int)(((long)n_pos * tiles2 + P - 1) / P);
-      if (w > kPartWaves) fit = 0;
+  // 32-bit integer arithmetic from here on: positions, waves and instances
+  // stay far below 2^31 inside the tables' bounds (64-bit division is a long
+  // instruction sequence on the GPU)
+  if (tid < 64) {   // producer waves per candidate, their prefix and the fit test, in one wave
+    int nw = 0;
+    if (tid < n_cand && n_pos <= kPartPos) {
+      const int P = calib.n_cu - (calib.c_min + tid * calib.c_step);
+      nw = (n_pos * tiles2 + P - 1) / P;
     }
-    if (fit) s_woff[n_cand] = w;
-    *s_fit = fit;
+    int incl = nw;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    if (tid < n_cand && tid < kPartCand) s_woff[tid] = incl - nw;
+    const int total = __shfl(incl, 63, 64);
+    if (tid == 0) {
+      const int fit = n_pos <= kPartPos && n_seg <= kPartSegs && n_cand >= 1 && n_cand <= kPartCand &&
+                      total <= kPartWaves;
+      if (fit) s_woff[n_cand] = total;
+      *s_fit = fit;
+    }
   }
   __syncthreads();
   if (!*s_fit) {
@@ -466,20 +477,20 @@ __device__ void model_role(const int32_t* __restrict__ counts, moe_plan_t p, con
   for (int idx = tid; idx < tw; idx += kPlanThreads) {
     int ci = 0;
     while (s_woff[ci + 1] <= idx) ++ci;
-    const long P = calib.n_cu - (calib.c_min + ci * calib.c_step);
-    long p0, p1;
+    const int P = calib.n_cu - (calib.c_min + ci * calib.c_step);
+    int p0, p1;
     model_wave_span(idx - s_woff[ci], P, tiles2, n_pos, &p0, &p1);
     double len = 0.0;
-    for (long q = p0; q <= p1; ++q) len = len > s_tt[q] ? len : s_tt[q];
+    for (int q = p0; q <= p1; ++q) len = len > s_tt[q] ? len : s_tt[q];
     s_wv[idx] = len;
   }
   __syncthreads();
   if (tid < n_cand) {   // wave ends, in order
-    const long P = calib.n_cu - (calib.c_min + tid * calib.c_step);
-    const long n_inst = (long)n_pos * tiles2;
+    const int P = calib.n_cu - (calib.c_min + tid * calib.c_step);
+    const int n_inst = n_pos * tiles2;
     double t = 0.0;
     for (int w = s_woff[tid]; w < s_woff[tid + 1]; ++w) {
-      const long wi = w - s_woff[tid];
+      const int wi = w - s_woff[tid];
       t = model_wave_end(t, s_wv[w], n_inst - wi * P < P ? n_inst - wi * P : P, P);
       s_wv[w] = t;
     }
@@ -489,11 +500,11 @@ __device__ void model_role(const int32_t* __restrict__ counts, moe_plan_t p, con
   // copy end per candidate: one wave each
   for (int ci = wave; ci < n_cand; ci += kPlanThreads / 64) {
     const int c = calib.c_min + ci * calib.c_step;
-    const long P = calib.n_cu - c;
+    const int P = calib.n_cu - c;
     const double bw = model_copy_bw(calib, c);
     double tc = 0.0;
     for (int sg = lane; sg < n_seg; sg += 64) {
-      const double r = s_wv[s_woff[ci] + (int)(((long)s_spos[sg] * tiles2 + tiles2 - 1) / P)];
+      const double r = s_wv[s_woff[ci] + (s_spos[sg] * tiles2 + tiles2 - 1) / P];
       const double v = model_copy_end(r, s_sfrom[sg], H, bw);
       tc = tc > v ? tc : v;
     }
