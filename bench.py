@@ -674,8 +674,8 @@ def table2_sweep(args, torch, reps=5):
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU's share only (this build runs on a single MI355X); "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        print(f"bench.py measures one expert-parallel rank's share on one MI355X; the transfer to "
+              f"other GPUs is not implemented, so --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     import torch
     ids = [args.config] if args.config else [int(c) for c in args.configs.split(",") if c.strip()]
