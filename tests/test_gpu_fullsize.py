@@ -123,22 +123,33 @@ def test_full_size_parity(wid, layer, tb):
     check_role_switch(sh, ref, w, 0, w.name)
 
 
+# (tokens per rank, N, experts per rank, router) of the tile-signalling
+# paper's Table 2: its largest, most skewed corner and a small balanced one
+TABLE2_CASES = [(16384, 8192, 64, "stress_skew"), (8192, 4096, 4, "balanced")]
+
+
 @pytest.mark.timeout(900)
-def test_table2_shape_parity():
-    """A shape of the tile-signalling paper's Table 2 (sec. 4.1.3): the
-    expert GEMM K = 2048 -> N = 8192 as a non-gated FFN with F = 2048 and
-    H = 8192, 64 experts per rank (E = 256 over 4 ranks), 16384 tokens per
-    rank, top-2 softmax, stress_skew routing (reading: logits + ln Zipf(1.2)
-    over the expert id, the hottest experts local to the timed rank). The
-    plan in full, the combine buffers against y_perm bit for bit, sampled
-    expert rows and tokens against the fp64 oracle, and every form (overlap
-    at the model's c, sequential, role switching, the fused gather) with the
-    same bits."""
+@pytest.mark.parametrize("tpr,N,E_l,router", TABLE2_CASES,
+                         ids=[f"{r}_tpr{t}_n{n}_e{e}" for t, n, e, r in TABLE2_CASES])
+def test_table2_shape_parity(tpr, N, E_l, router):
+    """Shapes of the tile-signalling paper's Table 2 (sec. 4.1.3): the expert
+    GEMM K = 2048 -> N as a non-gated FFN with F = 2048 and H = N, E_l
+    experts per rank over 4 ranks, top-2 softmax; stress_skew routing =
+    logits + ln Zipf(1.2) over the expert id (the hottest experts local to
+    the timed rank), balanced = unbiased logits (readings of router modes
+    the pages name but do not define). The plan in full, the combine buffers
+    against y_perm bit for bit, sampled expert rows and tokens against the
+    fp64 oracle, and every form (overlap at the model's c, sequential, role
+    switching, the fused gather) with the same bits."""
     import torch
     from synth import Workload
     from combine_overlap_amd import MOE_CONSUMER_AUTO, MOE_MODE_OVERLAP, MOE_MODE_SEQUENTIAL
-    w = Workload("table2_stress_tpr16384_n8192_e64", 4, 16384, 8192, 2048, 256, 2, False, "softmax",
-                 "zipf", zipf_s=1.2, w_std="0.02")
+    if router == "stress_skew":
+        w = Workload(f"table2_stress_tpr{tpr}_n{N}_e{E_l}", 4, tpr, N, 2048, 4 * E_l, 2, False, "softmax",
+                     "zipf", zipf_s=1.2, w_std="0.02")
+    else:
+        w = Workload(f"table2_balanced_tpr{tpr}_n{N}_e{E_l}", 4, tpr, N, 2048, 4 * E_l, 2, False, "softmax",
+                     "normal", w_std="0.02")
     tb = 64
     say(f"[fullsize] {w.name}: inputs")
     W1, W3, W2 = make_local_weights(w, 0)
