@@ -42,12 +42,12 @@
 //  * Short tiles: the 32-row blocks past an expert's last row skip their
 //    MFMAs, and their DMA re-reads the tile's first rows (L2 hits).
 //  * Role switching (optional, output projection): the workgroups also do
-//    the consumer's work. Before each tile a workgroup claims the next
-//    remote segment (one atomic) if all its row tiles are flagged and copies
-//    it into its owner's combine buffer, repeating while segments are ready;
-//    once the tiles run out the workgroups wait for and copy the rest. The
-//    copy thus takes the few CU-microseconds it costs instead of a standing
-//    partition of CUs.
+//    the consumer's work. Before each tile a workgroup claims the next eight
+//    64 KiB copy units (one fetch-and-add) if the segment holding them has
+//    all its row tiles flagged and copies them into their owner's combine
+//    buffer, repeating while units are ready; once the tiles run out the
+//    workgroups claim, wait for and copy the rest. The copy thus takes the
+//    CU-microseconds it costs instead of a standing partition of CUs.
 //  * 4 or 8 waves per workgroup in a WM x WN grid (8 = two waves per SIMD);
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 //  * The k-loop streams BK-wide slices of A and B straight from global memory
@@ -152,11 +152,12 @@ struct GemmArgs {
                                // first projection: the flags it clears for the output projection
   // role switching (output projection): the consumer's copy duty between tiles
   int copy_duty;
-  int32_t* my_copy;            // [0] next remote segment to claim
+  int32_t* my_copy;            // copy duty: [0] next unclaimed copy unit, [1] segment search hint
   int32_t* other_copy;         // the other launch's copy words (cleared here)
   BufPtrs bufs;                // combine buffers by source rank
   const int32_t* seg_tile0;
   const int32_t* seg_tile1;
+  const int32_t* seg_unit0;    // first 64 KiB copy unit of each segment
   const int32_t* seg_rows;
   const int32_t* seg_src_row;
   const int32_t* seg_dst_row;
@@ -324,28 +325,28 @@ __device__ __forceinline__ int xcc_id() {
 }
 
 
-// Copies remote segment sg's valid rows (y rows published by other
-// workgroups) into its owner's combine buffer with all NT threads: rounds of
-// kRound device-scope 16-byte loads per thread through a buffer resource
-// over the segment's bytes (loads past its end return zeros and are not
-// stored; a segment is below 2 GiB, which the host checks).
+// Copies 16-byte words [w0, w1) of remote segment sg's valid rows (y rows
+// published by other workgroups) into its owner's combine buffer with all NT
+// threads: rounds of kRound device-scope 16-byte loads per thread through a
+// buffer resource over those words (loads past its end return zeros and are
+// not stored; a segment is below 2 GiB, which the host checks).
 template <int NT>
-__device__ __forceinline__ void copy_segment(const GemmArgs& a, int sg, int tid) {
+__device__ __forceinline__ void copy_words(const GemmArgs& a, int sg, uint32_t w0, uint32_t w1, int tid) {
   constexpr int kRound = 32;   // 16-byte loads per thread in flight
   const int H = a.Nout;
-  const uint32_t words = (uint32_t)a.seg_rows[sg] * (uint32_t)(H / 8);
-  const uint16_t* src = a.C + (size_t)a.seg_src_row[sg] * H;
-  u32x4* dst = reinterpret_cast<u32x4*>(a.bufs.p[a.seg_dest[sg]] + (size_t)a.seg_dst_row[sg] * H);
+  const uint32_t words = w1 - w0;
+  const uint16_t* src = a.C + (size_t)a.seg_src_row[sg] * H + (size_t)w0 * 8;
+  u32x4* dst = reinterpret_cast<u32x4*>(a.bufs.p[a.seg_dest[sg]] + (size_t)a.seg_dst_row[sg] * H) + w0;
   const __amdgpu_buffer_rsrc_t r = buf_rsrc(src, words * 16u);
-  for (uint32_t w0 = 0; w0 < words; w0 += NT * kRound) {
+  for (uint32_t i0 = 0; i0 < words; i0 += NT * kRound) {
     u32x4 v[kRound];
 #pragma unroll
     for (int z = 0; z < kRound; ++z)
-      v[z] = __builtin_amdgcn_raw_buffer_load_b128(r, (w0 + (uint32_t)(z * NT + tid)) * 16u, 0,
+      v[z] = __builtin_amdgcn_raw_buffer_load_b128(r, (i0 + (uint32_t)(z * NT + tid)) * 16u, 0,
                                                    MOE_DEVICE_SCOPE_PUBLISH ? kCpolDevice : 0);
 #pragma unroll
     for (int z = 0; z < kRound; ++z) {
-      const uint32_t i = w0 + (uint32_t)(z * NT + tid);
+      const uint32_t i = i0 + (uint32_t)(z * NT + tid);
       if (i < words) store16_nt(dst + i, v[z]);
     }
   }
@@ -360,24 +361,29 @@ __device__ __forceinline__ void stamp_max(const int32_t* meta, int word) {
   __hip_atomic_fetch_max(w, (uint64_t)wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The copy duty, segments in schedule order.
-//  wait = false (between tiles): if the next unclaimed segment's row tiles are
-//    all flagged, claim it together with the following segments those same
-//    flags cover (one compare-and-swap), copy them, and look again; return as
-//    soon as the next segment is not ready.
-//  wait = true (no tiles left): take segments by ticket (fetch-and-add), so
-//    the workgroups claim in parallel; wait (bounded) for each one's flags and
-//    copy it; return once every segment is taken.
-// At most this many segments per claim: one segment per claim makes the
-// workgroups race on the claim word, and large claims leave single
-// workgroups with megabytes to copy before their next tile.
-constexpr int kMaxClaim = 4;
+// The copy duty, in the 64 KiB copy units of the remote segments (schedule
+// order). Word 0 of the copy words is the next unclaimed unit; units are
+// claimed kClaimUnits at a time by fetch-and-add, so claiming never retries
+// and a large segment is copied by several workgroups. A claim stays with
+// its workgroup (s_copy[3..4]) until copied, one segment piece at a time.
+//  wait = false (between tiles): copy the pieces of the workgroup's claim
+//    whose segments have all their row tiles flagged; with no claim left,
+//    claim the next units if the segment holding the first unclaimed unit
+//    is ready. Return at the first piece that is not ready.
+//  wait = true (no tiles left): the same, but wait (bounded) for each
+//    piece's flags; return once every unit is taken and copied.
+// Word 1 is a segment search hint: the largest segment found so far.
+constexpr int kClaimUnits = 8;
 
 template <int NT>
 __device__ void copy_duty(const GemmArgs& a, bool wait, int tid, int* s_copy) {
   const int n_seg = a.meta[META_NSEG];
+  const int n_units = a.meta[META_NUNITS];
   const int lane = tid & 63;
-  auto tiles_ready = [&](int t0, int t1) {
+  int32_t* next_unit = a.my_copy;
+  int32_t* seg_hint = a.my_copy + 1;
+  auto tiles_ready = [&](int sg) {
+    const int t0 = a.seg_tile0[sg], t1 = a.seg_tile1[sg];
     const int nf = (t1 - t0 + 1) * a.tiles_n;
     const uint32_t* f = a.flags + (size_t)t0 * a.tiles_n;
     bool ok = true;
@@ -386,37 +392,81 @@ __device__ void copy_duty(const GemmArgs& a, bool wait, int tid, int* s_copy) {
                                __HIP_MEMORY_SCOPE_AGENT) == a.epoch);
     return __ballot(!ok) == 0ull;
   };
+  auto unit_end = [&](int sg) { return sg + 1 < n_seg ? a.seg_unit0[sg + 1] : n_units; };
+  // wave 0: the segment holding unit u < n_units, i.e. the last one starting
+  // at or below u (segment starts are non-decreasing), searched 64 segments
+  // at a time from `from`, a segment starting at or below u. The shared hint
+  // is used instead when it too starts at or below u.
+  auto find_seg = [&](int u, int from) {
+    const int h = __hip_atomic_load(seg_hint, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int s0 = (h > from && a.seg_unit0[h] <= u) ? h : from;
+    while (true) {
+      const int sc = s0 + 1 + lane;
+      const int cnt = __popcll(__ballot(sc < n_seg && a.seg_unit0[sc] <= u));
+      s0 += cnt;
+      if (cnt < 64) break;
+    }
+    if (lane == 0 && s0 > h) __hip_atomic_fetch_max(seg_hint, s0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return s0;
+  };
+  int known = -1;   // wave 0: the last segment seen with all its flags
   while (true) {
+    // wave 0: the next piece to copy, s_copy = (segment or -1 none now / -2
+    // done, first unit, end unit); s_copy[3..5] = the claim's units [p0, p1)
+    // and the segment holding p0, kept across calls
     if (tid < 64) {
-      int d0 = -1, d1 = -1;   // claimed segments [d0, d1); d0 < 0: nothing now (-2: all taken)
-      if (!wait) {
-        while (true) {
-          const int sg = __hip_atomic_load(a.my_copy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (sg >= n_seg) { d0 = -2; break; }
-          const int t0 = a.seg_tile0[sg], t1 = a.seg_tile1[sg];
-          if (!tiles_ready(t0, t1)) break;
-          int n = 1;
-          while (n < kMaxClaim && sg + n < n_seg && a.seg_tile0[sg + n] >= t0 && a.seg_tile1[sg + n] <= t1) ++n;
-          int won = 0;
-          if (lane == 0) {
-            int expected = sg;
-            won = __hip_atomic_compare_exchange_strong(a.my_copy, &expected, sg + n, __ATOMIC_RELAXED,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int state = -1, c0 = 0, c1 = 0;
+      int p0 = s_copy[3], p1 = s_copy[4], ps = s_copy[5];
+      if (p0 >= p1) {
+        bool take = true;
+        if (!wait) {
+          const int u = __hip_atomic_load(next_unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (u >= n_units) {
+            take = false;
+            state = -2;
+          } else {
+            const int sg = find_seg(u, ps);
+            if (sg != known && !tiles_ready(sg)) {
+              take = false;
+            } else {
+              known = sg;
+              // a claim races with others and may land past u: take one only
+              // with two claims' worth of ready units ahead (else the units
+              // would wait here, claimed, while this workgroup runs a tile)
+              if (u + 2 * kClaimUnits > unit_end(sg) && sg + 1 < n_seg && !tiles_ready(sg + 1)) take = false;
+            }
+            ps = sg;   // starts at or below u, so at or below every later claim
           }
-          if (__shfl(won, 0)) { d0 = sg; d1 = sg + n; break; }
         }
-      } else {
-        int sg = 0;
-        if (lane == 0) sg = __hip_atomic_fetch_add(a.my_copy, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sg = __shfl(sg, 0);
-        if (sg >= n_seg) {
-          d0 = -2;
-        } else {
-          const int t0 = a.seg_tile0[sg], t1 = a.seg_tile1[sg];
+        if (take) {
+          int t = 0;
+          // with no tiles left, the units still unclaimed are spread over at
+          // least 64 workgroups (a small copy would otherwise fall to one
+          // workgroup, segment after segment)
+          int nc = kClaimUnits;
+          if (wait) {
+            const int left = n_units - __hip_atomic_load(next_unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            nc = max(1, min(kClaimUnits, left / 64));
+          }
+          if (lane == 0) t = __hip_atomic_fetch_add(next_unit, nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          t = __shfl(t, 0);
+          if (t >= n_units) {
+            state = -2;
+          } else {
+            p0 = t;
+            p1 = min(t + nc, n_units);
+            ps = find_seg(p0, ps);
+          }
+        }
+      }
+      if (p0 < p1) {
+        const int sg = ps;
+        bool ready = sg == known;
+        if (!ready) {
           const uint64_t t_start = wall_clock64();
-          d0 = sg;
-          d1 = sg + 1;
-          while (!tiles_ready(t0, t1)) {
+          while (true) {
+            ready = tiles_ready(sg);
+            if (ready || !wait) break;
             if (wall_clock64() - t_start > a.wait_ticks) {
               if (lane == 0) {
                 int expected = 0;
@@ -424,21 +474,37 @@ __device__ void copy_duty(const GemmArgs& a, bool wait, int tid, int* s_copy) {
                                                      MOE_ERR_TIMEOUT, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
               }
-              d0 = -2;
+              state = -2;
               break;
             }
             __builtin_amdgcn_s_sleep(2);
           }
         }
+        if (ready) {
+          known = sg;
+          state = sg;
+          c0 = p0;
+          c1 = min(p1, unit_end(sg));
+          p0 = c1;
+          if (p0 < p1) ps = sg + 1;   // the claim goes on in the next segment
+        }
       }
-      if (lane == 0) { s_copy[0] = d0; s_copy[1] = d1; }
+      if (lane == 0) {
+        s_copy[0] = state; s_copy[1] = c0; s_copy[2] = c1;
+        s_copy[3] = p0; s_copy[4] = p1; s_copy[5] = ps;
+      }
     }
     __syncthreads();
-    const int d0 = s_copy[0], d1 = s_copy[1];
+    const int sg = s_copy[0], c0 = s_copy[1], c1 = s_copy[2];
     __syncthreads();
-    if (d0 < 0) return;
+    if (sg < 0) return;
     if (!MOE_DEVICE_SCOPE_PUBLISH) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    for (int sg = d0; sg < d1; ++sg) copy_segment<NT>(a, sg, tid);
+    // units relative to the segment, as 16-byte words of its rows
+    constexpr uint32_t kUnitWords = kCopyUnitBytes / 16;
+    const int base = a.seg_unit0[sg];
+    const uint32_t seg_words = (uint32_t)a.seg_rows[sg] * (uint32_t)(a.Nout / 8);
+    copy_words<NT>(a, sg, (uint32_t)(c0 - base) * kUnitWords, min((uint32_t)(c1 - base) * kUnitWords, seg_words),
+                   tid);
     // these copies have completed: the latest such stamp is the transfer's end
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -454,7 +520,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   static_assert(EPI != EPI_GATED || C::FN % 2 == 0, "gated tiles pair W1/W3 32-column blocks per wave");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
   __shared__ int s_item[5];   // tile, chunk, nsplit, slot, queue
-  __shared__ int s_copy[2];   // copy duty: claimed segments [s_copy[0], s_copy[1])
+  __shared__ int s_copy[6];   // copy duty: the piece to copy, this workgroup's claim
   // output projection: the chunks of a split tail tile share its reduction
   constexpr bool kShared = EPI == EPI_PLAIN;
   constexpr int kBlocks = C::FM * C::FN;   // 32x32 accumulator blocks per wave
@@ -480,6 +546,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   }
   const int px = max(1, a.px > 0 ? a.px : ((int)gridDim.x - a.meta[META_CAUTO]) / kXcds);
   if (a.trace != nullptr && blockIdx.x == 0 && tid == 0) a.trace[0] = wall_clock64();
+  if (COPY && tid == 0) { s_copy[3] = 0; s_copy[4] = 0; s_copy[5] = 0; }   // no claim yet
   if constexpr (CONS) {
     const int n_cons = a.n_cons > 0 ? a.n_cons : a.meta[META_CAUTO];
     if ((int)blockIdx.x < n_cons) {
@@ -1104,6 +1171,7 @@ hipError_t launch_gemm2(const Geometry& g, const uint16_t* h, const uint16_t* w2
     a.bufs = *copy_bufs;
     a.seg_tile0 = p.seg_tile0;
     a.seg_tile1 = p.seg_tile1;
+    a.seg_unit0 = p.seg_unit0;
     a.seg_rows = p.seg_rows;
     a.seg_src_row = p.seg_src_row;
     a.seg_dst_row = p.seg_dst_row;
