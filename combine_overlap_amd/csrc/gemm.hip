@@ -189,21 +189,33 @@ struct GemmArgs {
 // XCD x owns row tiles b = bx + k*xb and column tiles t = nx + l*xn; its queue walks
 // blocks of gp row tiles x gq column tiles (in schedule order, so remote rows
 // still finish first) so that the ~32 tiles an XCD runs at once share A rows
-// and weight columns in its L2. Returns -1 past the end of the queue.
-__device__ __forceinline__ int queue_tile(const GemmArgs& a, int n_rt, int x, int i) {
+// and weight columns in its L2. The row tiles holding a remote band (the first
+// n_rrt schedule positions) and the others are blocked separately, so no block
+// mixes them: the last tiles to finish are then local ones where there are
+// enough, and the copy of the remote rows need not wait for the launch's last
+// round. Returns -1 past the end of the queue.
+__device__ __forceinline__ int queue_tile(const GemmArgs& a, int n_rt, int n_rrt, int x, int i) {
   const int bx = x / a.xn, nx = x - (x / a.xn) * a.xn;
   if (bx >= n_rt || nx >= a.tiles_n) return -1;
   const int nb = (n_rt - bx + a.xb - 1) / a.xb;         // row tiles of this XCD
   const int nn = (a.tiles_n - nx + a.xn - 1) / a.xn;    // column tiles of this XCD
   if (i >= nb * nn) return -1;
+  // row tiles k < kr of this XCD hold a remote band
+  const int kr = min(nb, max(0, (n_rrt - bx + a.xb - 1) / a.xb));
+  int k0 = 0, nk = kr;
+  if (i >= kr * nn) {
+    i -= kr * nn;
+    k0 = kr;
+    nk = nb - kr;
+  }
   const int per_group = a.gp * nn;
   const int g = i / per_group;
-  const int pg = min(a.gp, nb - g * a.gp);              // row tiles in this group
+  const int pg = min(a.gp, nk - g * a.gp);              // row tiles in this group
   const int rem = i - g * per_group;
   const int h = rem / (pg * a.gq);
   const int qh = min(a.gq, nn - h * a.gq);              // column tiles in this block
   const int rem2 = rem - h * pg * a.gq;
-  const int k = g * a.gp + rem2 / qh;
+  const int k = k0 + g * a.gp + rem2 / qh;
   const int l = h * a.gq + rem2 % qh;
   return (bx + k * a.xb) * a.tiles_n + (nx + l * a.xn);
 }
@@ -219,7 +231,7 @@ struct Item {
   int tile, chunk, nsplit, slot;
 };
 
-__device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int x, int i, int px, int nk,
+__device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int n_rrt, int x, int i, int px, int nk,
                                            int max_split) {
   Item it{-1, 0, 1, 0};
   const int bx = x / a.xn, nx = x - (x / a.xn) * a.xn;
@@ -234,17 +246,17 @@ __device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int x, i
   // test knob: the whole tiles in reverse queue order (the split tail tiles
   // stay the same tiles, so every tile is summed as without the knob)
   if (s < 2) {
-    if (i < T) it.tile = queue_tile(a, n_rt, x, a.dbg_reverse ? T - 1 - i : i);
+    if (i < T) it.tile = queue_tile(a, n_rt, n_rrt, x, a.dbg_reverse ? T - 1 - i : i);
     return it;
   }
   const int full = T - tail;
   if (i < full) {
-    it.tile = queue_tile(a, n_rt, x, a.dbg_reverse ? full - 1 - i : i);
+    it.tile = queue_tile(a, n_rt, n_rrt, x, a.dbg_reverse ? full - 1 - i : i);
     return it;
   }
   const int j = i - full;
   if (j >= tail * s) return it;
-  it.tile = queue_tile(a, n_rt, x, full + j / s);
+  it.tile = queue_tile(a, n_rt, n_rrt, x, full + j / s);
   it.chunk = j % s;
   it.nsplit = s;
   it.slot = j;
@@ -601,7 +613,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       while (tried < kXcds) {
         const int i = __hip_atomic_fetch_add(a.my_ctr + q * kCtrStride, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-        it = queue_item(a, n_rt, q, i, px, nk, kMaxSplit);
+        it = queue_item(a, n_rt, n_rrt, q, i, px, nk, kMaxSplit);
         if (it.tile >= 0) break;
         q = (q + 1) & (kXcds - 1);
         ++tried;
