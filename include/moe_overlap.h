@@ -332,11 +332,12 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *            on all CUs, then one bulk copy of all remote rows on all CUs.
  *            MOE_MODE_ROLE_SWITCH: both projections on all CUs, the output
  *            projection's workgroups doing the consumer's work as well: before
- *            each tile a workgroup copies the next remote segments whose tiles are
- *            all flagged (claimed in schedule order, up to 4 segments whose
- *            tiles are covered by the same flags per claim),
- *            and once the tiles run out the workgroups copy the rest (each
- *            wait bounded like the consumer's). No CU is reserved; c is
+ *            each tile a workgroup claims the next 64 KiB copy units of the
+ *            remote segments (schedule order, up to 8 per claim, one
+ *            fetch-and-add) once the segment holding them has all its tiles
+ *            flagged, and copies them; a claim stays with its workgroup until
+ *            copied. Once the tiles run out the workgroups claim and copy the
+ *            rest (each wait bounded like the consumer's). No CU is reserved; c is
  *            ignored and the K-split is sized for all CUs (the same bits as
  *            SEQUENTIAL with c = 0). The per-layer worker split of [Weave]
  *            taken to its temporal end.
