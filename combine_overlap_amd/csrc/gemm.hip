@@ -188,8 +188,8 @@ struct GemmArgs {
 // Queue index i of XCD x -> tile (row-tile schedule position * tiles_n + column tile).
 // XCD x owns row tiles b = bx + k*xb and column tiles t = nx + l*xn; its queue walks
 // blocks of gp row tiles x gq column tiles (in schedule order, so remote rows
-// still finish first) so that the ~32 tiles an XCD runs at once share A rows
-// and weight columns in its L2. The row tiles holding a remote band (the first
+// still finish first) so that the tiles an XCD runs at about the same time
+// share A rows and weight columns in its L2. The row tiles holding a remote band (the first
 // n_rrt schedule positions) and the others are blocked separately, so no block
 // mixes them: the last tiles to finish are then local ones where there are
 // enough, and the copy of the remote rows need not wait for the launch's last
@@ -1099,13 +1099,19 @@ static hipError_t launch_t(const GemmArgs& a, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-// XCD grid and block shape for a launch with tiles_n column tiles
-static inline void set_xcd_grid(GemmArgs& a) {
-  a.xn = a.tiles_n >= 32 ? 8 : (a.tiles_n >= 8 ? 4 : (a.tiles_n >= 2 ? 2 : 1));
+// XCD grid and block shape for a launch with tiles_n column tiles: at most
+// 4 column groups (so each XCD takes every other row tile); blocks of 32
+// tiles (one round of an XCD's 32 workgroups), or of 64 in the first
+// projection (16 row tiles x 4 column tiles). Measured against 8 column
+// groups and 32-tile blocks: the first projection 1-3% faster on the five
+// workloads; 64-tile blocks in the output projection make its row tiles
+// finish in coarser bursts, and the consumer fell behind (workload 4).
+static inline void set_xcd_grid(GemmArgs& a, bool first_projection) {
+  a.xn = a.tiles_n >= 8 ? 4 : (a.tiles_n >= 2 ? 2 : 1);
   a.xb = kXcds / a.xn;
   const int nn = (a.tiles_n + a.xn - 1) / a.xn;
   a.gq = nn < 4 ? nn : 4;
-  a.gp = 32 / a.gq;
+  a.gp = (first_projection ? 64 : 32) / a.gq;
 }
 
 // per-shape tile table (row tiles of kTileM rows; BN from the geometry).
@@ -1113,7 +1119,7 @@ static inline void set_xcd_grid(GemmArgs& a) {
 // waits; measured on MI355X for the Mixtral-shaped projections.
 template <int EPI>
 static hipError_t dispatch(GemmArgs a, int bm, int bn, int grid, hipStream_t st) {
-  set_xcd_grid(a);
+  set_xcd_grid(a, EPI != EPI_PLAIN);
   if (bm == 256 && bn == 256) return launch_t<256, 256, 64, 2, 4, 2, EPI>(a, grid, st);
   if (bm == 256 && bn == 128) return launch_t<256, 128, 64, 3, 4, 2, EPI>(a, grid, st);
   return hipErrorInvalidValue;
