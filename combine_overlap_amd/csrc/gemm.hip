@@ -49,7 +49,7 @@
 //    workgroups claim, wait for and copy the rest. The copy thus takes the
 //    CU-microseconds it costs instead of a standing partition of CUs.
 //  * 4 or 8 waves per workgroup in a WM x WN grid (8 = two waves per SIMD);
-//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
+//    v_mfma_f32_16x16x32_bf16 with fp32 accumulators (four per 32x32 block).
 //  * The k-loop streams BK-wide slices of A and B straight from global memory
 //    into an NS-stage LDS ring with global_load_lds_dwordx4 (no VGPR staging).
 //    Each lane fetches the 16-byte chunk that belongs at its LDS slot under an
@@ -581,15 +581,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 #pragma unroll
   for (int par = 0; par < 2; ++par)
     lane_off[par] = (uint32_t)(d_row * K * 2 + swz<C::CPR>(par * C::RPI + d_row, d_pch) * 16);
-  // MFMA fragment geometry: rows (lane & 31) + 32 i; logical chunk 2 kk + (lane >> 5)
-  int a_off[C::CPR / 2], b_off[C::CPR / 2];
+  // MFMA fragment geometry (v_mfma_f32_16x16x32_bf16): lane l reads row
+  // (l & 15) + 16 i of A (column 16 j of B) and the 8 k's of logical chunk
+  // 4 s + (l >> 4) of k32 substep s; the swizzle only depends on the row mod
+  // 16, so one offset per substep covers every 16-row block
+  int a_off[C::CPR / 4], b_off[C::CPR / 4];
   {
-    const int ra = wm * C::WTM + (lane & 31), rb = wn * C::WTN + (lane & 31);
+    const int ra = wm * C::WTM + (lane & 15), rb = wn * C::WTN + (lane & 15);
 #pragma unroll
-    for (int kk = 0; kk < C::CPR / 2; ++kk) {
-      const int lc = kk * 2 + (lane >> 5);
-      a_off[kk] = ra * BK + swz<C::CPR>(ra, lc) * 8;
-      b_off[kk] = BM * BK + rb * BK + swz<C::CPR>(rb, lc) * 8;
+    for (int s = 0; s < C::CPR / 4; ++s) {
+      const int lc = s * 4 + (lane >> 4);
+      a_off[s] = ra * BK + swz<C::CPR>(ra, lc) * 8;
+      b_off[s] = BM * BK + rb * BK + swz<C::CPR>(rb, lc) * 8;
     }
   }
 
@@ -720,13 +723,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     };
     auto issue = [&](int kt) { issue_part(kt, 0, C::LPW); };
 
-    f32x16 acc[C::FM][C::FN];
+    // accumulators per 32x32 block (i, j) of the wave tile, as four 16x16
+    // MFMA results: acc[i][j][sub][rr] is row 32 i + 16 (sub >> 1) + 4 (l >> 4)
+    // + rr, column 32 j + 16 (sub & 1) + (l & 15); r = 4 sub + rr runs over a
+    // block's 16 values
+    f32x4 acc[C::FM][C::FN][4];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[i][j][r >> 2][r & 3] = 0.f;
 
     // k-loop, software-pipelined:
     //  * all NS ring slots are in flight: stage kt+NS is issued into stage kt's
@@ -735,33 +742,46 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     //    last MFMAs (one burst of all of them made the issuing waves queue
     //    behind the texture path: the first projection took 4% longer at
     //    K = 4096; a third or more of them in the next step, less time to land);
-    //  * MFMA fragments are double-buffered: substep kk+1's fragments load
-    //    while substep kk's MFMAs run;
-    //  * the stage barrier sits before the last substep's MFMAs (whose
+    //  * a stage is four quarters: k32 substep s = q / 2 against half h = q % 2
+    //    of the wave's 16-column B blocks (v_mfma_f32_16x16x32_bf16; 16 x 16
+    //    MFMAs interleave with the DMA and fragment reads better than 32 x 32
+    //    ones of the same flops: both projections 3-5% faster on the
+    //    Mixtral-shaped shares, the extra fragment registers spill only in
+    //    the item set-up and the epilogue). Fragments are
+    //    double-buffered: quarter q+1's load while quarter q's MFMAs run
+    //    (quarter (s, 0) loads substep s's A blocks with its B half);
+    //  * the stage barrier sits before the last quarter's MFMAs (whose
     //    fragments are already in registers), so stage kt+1's first
     //    fragments load while they run.
-    constexpr int KK = BK / 16;
-    bf16x8 fa[2][C::FM], fb[2][C::FN];
-    auto load_frags = [&](int kt, int kk, int buf) {
+    constexpr int KK = BK / 16;   // quarters per stage
+    bf16x8 fa[2][2 * C::FM], fb[2][C::FN];
+    auto load_frags = [&](int kt, int q, int buf) {
       const uint16_t* st = lds + (kt % NS) * C::STAGE;
+      const int s = q >> 1, h = q & 1;
+      if (h == 0) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-        fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + a_off[kk] + i * 32 * BK);
+        for (int i = 0; i < 2 * C::FM; ++i)
+          fa[s & 1][i] = *reinterpret_cast<const bf16x8*>(st + a_off[s] + i * 16 * BK);
+      }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + b_off[kk] + j * 32 * BK);
+        fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + b_off[s] + (h * C::FN + j) * 16 * BK);
     };
-    // 32-row blocks of this wave that hold stored rows (a short last row tile
+    // 16-row blocks of this wave that hold stored rows (a short last row tile
     // of an expert skips the MFMAs of the blocks past them; with 16-row bands
-    // the last block may be half the next expert's rows, computed, not stored)
-    const int fm_act = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (vrows - wm * C::WTM + 31) / 32)));
-    auto mfmas = [&](int buf, auto partial) {
+    // the last block may be the next expert's rows, computed, not stored)
+    const int fm_act = __builtin_amdgcn_readfirstlane(min(2 * C::FM, max(0, (vrows - wm * C::WTM + 15) / 16)));
+    auto mfmas = [&](int q, int buf, auto partial) {
+      const int s = q >> 1, h = q & 1;
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        if (decltype(partial)::value && i >= fm_act) continue;
+      for (int j = 0; j < C::FN; ++j) {
+        const int jb = h * C::FN + j;   // 16-column block of the wave tile
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 2 * C::FM; ++i) {
+          if (decltype(partial)::value && i >= fm_act) continue;
+          f32x4& d = acc[i >> 1][jb >> 1][(i & 1) * 2 + (jb & 1)];
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][i], fb[buf][j], d, 0, 0, 0);
+        }
       }
     };
 
@@ -778,7 +798,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
           load_frags(kt, kk + 1, (kk + 1) & 1);
-          mfmas(kk & 1, partial);
+          mfmas(kk, kk & 1, partial);
         }
         const bool more = kt + NS < nkc;
         if (kt + 1 < nkc) {
@@ -787,11 +807,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
           if (more) issue_part(kt + NS, 0, C::LPW / 2);
           load_frags(kt + 1, 0, 0);
         }
-        mfmas((KK - 1) & 1, partial);
+        mfmas(KK - 1, (KK - 1) & 1, partial);
         if (more) issue_part(kt + NS, C::LPW / 2, C::LPW);
       }
     };
-    if (fm_act == C::FM) kloop(std::false_type{});
+    if (fm_act == 2 * C::FM) kloop(std::false_type{});
     else kloop(std::true_type{});
 
     if (a.dbg_seed != 0u) {
@@ -812,13 +832,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     constexpr int OUTW = (EPI == EPI_GATED) ? BN / 2 : BN;
     constexpr int LROW = OUTW + 8;
     constexpr int CH = OUTW / 8;   // 16-byte chunks per output row
-    const int ncol = lane & 31;
-    const int mrow = (lane >> 5) * 4;
+    const int ncol = lane & 15;          // column inside a 16 x 16 result
+    const int mrow = (lane >> 4) * 4;    // first of the lane's four rows in it
     uint16_t* cbase = a.C + (size_t)row0 * a.Nout + (size_t)tn * OUTW;
     // accumulator blocks q in [q0, q1) of every wave (q = j * FM + i) -> LDS ->
-    // the tile's rows. 32x32 accumulator layout: lane l holds column l%32 and
-    // rows 8*(r/4) + 4*(l/32) + r%4, r = 0..15. The bf16 tile is staged in LDS
-    // (row stride OUTW + 8 keeps the two row groups of a store on disjoint
+    // the tile's rows (layout at acc above). The bf16 tile is staged in LDS
+    // (row stride OUTW + 8 keeps the four row groups of a store on disjoint
     // banks) and leaves as 16-byte row chunks.
     auto store_blocks = [&](int q0, int q1) {
       __syncthreads();   // every wave is done reading the ring (or the last staging)
@@ -827,11 +846,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int p = 0; p < C::FN / 2; ++p) {
-            const int c = wn * (C::WTN / 2) + p * 32 + ncol;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int m = wm * C::WTM + i * 32 + (r >> 2) * 8 + mrow + (r & 3);
-              lds[m * LROW + c] = f32_to_bf16_rne(silu_f32(acc[i][2 * p][r]) * acc[i][2 * p + 1][r]);
+              const int sub = r >> 2, rr = r & 3;
+              const int c = wn * (C::WTN / 2) + p * 32 + (sub & 1) * 16 + ncol;
+              const int m = wm * C::WTM + i * 32 + (sub >> 1) * 16 + mrow + rr;
+              lds[m * LROW + c] = f32_to_bf16_rne(silu_f32(acc[i][2 * p][sub][rr]) * acc[i][2 * p + 1][sub][rr]);
             }
           }
       } else {
@@ -839,12 +859,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j) {
-            const int c = wn * C::WTN + j * 32 + ncol;
             if (j * C::FM + i < q0 || j * C::FM + i >= q1) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int m = wm * C::WTM + i * 32 + (r >> 2) * 8 + mrow + (r & 3);
-              float v = acc[i][j][r];
+              const int sub = r >> 2, rr = r & 3;
+              const int c = wn * C::WTN + j * 32 + (sub & 1) * 16 + ncol;
+              const int m = wm * C::WTM + i * 32 + (sub >> 1) * 16 + mrow + rr;
+              float v = acc[i][j][sub][rr];
               if constexpr (EPI == EPI_SILU) v = silu_f32(v);
               lds[m * LROW + c] = f32_to_bf16_rne(v);
             }
@@ -913,7 +934,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+          for (int r = 0; r < 16; ++r) acc[i][j][r >> 2][r & 3] = 0.f;
       if (kShared && q1 - q0 < kBlocks) {
         // a few blocks: the partials of up to four chunks of a block in flight
         // at once (clamped loads, so none is predicated), added in chunk order
@@ -938,8 +959,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
                 if (cb + u >= nsplit) break;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                  acc[i][j][2 * r] += __uint_as_float((uint32_t)v[u][r]);
-                  acc[i][j][2 * r + 1] += __uint_as_float((uint32_t)(v[u][r] >> 32));
+                  acc[i][j][r >> 1][(r & 1) * 2] += __uint_as_float((uint32_t)v[u][r]);
+                  acc[i][j][r >> 1][(r & 1) * 2 + 1] += __uint_as_float((uint32_t)(v[u][r] >> 32));
                 }
               }
               __builtin_amdgcn_sched_barrier(0);
@@ -956,8 +977,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
               for (int r = 0; r < 8; ++r) {
                 const uint64_t v = __hip_atomic_load(part + ((i * C::FN + j) * 8 + r) * 64, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-                acc[i][j][2 * r] += __uint_as_float((uint32_t)v);
-                acc[i][j][2 * r + 1] += __uint_as_float((uint32_t)(v >> 32));
+                acc[i][j][r >> 1][(r & 1) * 2] += __uint_as_float((uint32_t)v);
+                acc[i][j][r >> 1][(r & 1) * 2 + 1] += __uint_as_float((uint32_t)(v >> 32));
               }
               // one 32x32 block of loads in flight at a time (the accumulators stay live)
               __builtin_amdgcn_sched_barrier(0);
@@ -991,8 +1012,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
-            const uint64_t v = (uint64_t)__float_as_uint(acc[i][j][2 * r]) |
-                               ((uint64_t)__float_as_uint(acc[i][j][2 * r + 1]) << 32);
+            const uint64_t v = (uint64_t)__float_as_uint(acc[i][j][r >> 1][(r & 1) * 2]) |
+                               ((uint64_t)__float_as_uint(acc[i][j][r >> 1][(r & 1) * 2 + 1]) << 32);
             __hip_atomic_store(mine + ((i * C::FN + j) * 8 + r) * 64, v, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
           }
