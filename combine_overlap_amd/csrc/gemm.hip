@@ -583,17 +583,23 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     lane_off[par] = (uint32_t)(d_row * K * 2 + swz<C::CPR>(par * C::RPI + d_row, d_pch) * 16);
   // MFMA fragment geometry (v_mfma_f32_16x16x32_bf16): lane l reads row
   // (l & 15) + 16 i of A (column 16 j of B) and the 8 k's of logical chunk
-  // 4 s + (l >> 4) of k32 substep s; the swizzle only depends on the row mod
-  // 16, so one offset per substep covers every 16-row block
-  int a_off[C::CPR / 4], b_off[C::CPR / 4];
-  {
-    const int ra = wm * C::WTM + (lane & 15), rb = wn * C::WTN + (lane & 15);
+  // 4 s + (l >> 4) of k32 substep s. The swizzle only depends on the row mod
+  // 16 and XORs the chunk index, so one lane offset f_off (substep 0) covers
+  // every 16-row block of A and B; substep s reads f_off ^ 32 s (chunk ^ 4).
+  // The instances without copy duty keep the four sums (per substep and
+  // operand) in registers; the copying one, whose copy state leaves it no
+  // room for them, forms them per substep from f_off (kept in registers,
+  // they had spilled into its k-loop, and the reload's vmcnt wait drained
+  // the DMA ring every stage: its output projection 25-30% slower).
+  static_assert(C::CPR == 8 && C::WTM % 16 == 0 && C::WTN % 16 == 0, "fragment offsets assume BK = 64");
+  const int f_off = (lane & 15) * BK + swz<C::CPR>(lane & 15, lane >> 4) * 8;
+  const int a_woff = __builtin_amdgcn_readfirstlane(wm * C::WTM * BK);
+  const int b_woff = __builtin_amdgcn_readfirstlane(BM * BK + wn * C::WTN * BK);
+  int a_off[2], b_off[2];
 #pragma unroll
-    for (int s = 0; s < C::CPR / 4; ++s) {
-      const int lc = s * 4 + (lane >> 4);
-      a_off[s] = ra * BK + swz<C::CPR>(ra, lc) * 8;
-      b_off[s] = BM * BK + rb * BK + swz<C::CPR>(rb, lc) * 8;
-    }
+  for (int s = 0; s < 2; ++s) {
+    a_off[s] = a_woff + (f_off ^ (s * 32));
+    b_off[s] = b_woff + (f_off ^ (s * 32));
   }
 
   const int n_rt = a.meta[META_NTILES];   // row tiles, in schedule positions
@@ -758,14 +764,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
     auto load_frags = [&](int kt, int q, int buf) {
       const uint16_t* st = lds + (kt % NS) * C::STAGE;
       const int s = q >> 1, h = q & 1;
+      const int ao = COPY ? a_woff + (f_off ^ (s * 32)) : a_off[s];
+      const int bo = COPY ? b_woff + (f_off ^ (s * 32)) : b_off[s];
       if (h == 0) {
 #pragma unroll
         for (int i = 0; i < 2 * C::FM; ++i)
-          fa[s & 1][i] = *reinterpret_cast<const bf16x8*>(st + a_off[s] + i * 16 * BK);
+          fa[s & 1][i] = *reinterpret_cast<const bf16x8*>(st + ao + i * 16 * BK);
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + b_off[s] + (h * C::FN + j) * 16 * BK);
+        fb[buf][j] = *reinterpret_cast<const bf16x8*>(st + bo + (h * C::FN + j) * 16 * BK);
     };
     // 16-row blocks of this wave that hold stored rows (a short last row tile
     // of an expert skips the MFMAs of the blocks past them; with 16-row bands
