@@ -185,9 +185,11 @@ def cpu_baseline(w, inp, tb, layer):
 def hbm_phases(sh, w, torch, M, m_pad, remote, bulk_copy_ms, reps=20):
     """The HBM-bound steps timed alone (HIP events on the stream they run on),
     each against the 8 TB/s HBM peak with its algorithmic bytes per launch:
-    route (logits read, ids and gates written), the gather into x_perm (valid
-    rows read, padded rows written), combine (the local rows read once, the
-    share written) and the baseline's bulk copy (remote rows read and written)."""
+    route (logits read, ids and gates written), the permute into x_perm (plan
+    and copy; valid rows read, padded rows written, indexes), the gather copy
+    kernel alone (the same rows), combine (the local rows read once, the share
+    written) and the baseline's bulk copy (remote rows read and written); and
+    the front end (route and plan) per layer."""
     s = torch.cuda.current_stream()
     RT, H = w.R * w.T, w.H
     b_route = RT * (4 * w.E + 8 * w.k)
@@ -212,12 +214,23 @@ def hbm_phases(sh, w, torch, M, m_pad, remote, bulk_copy_ms, reps=20):
                              ("permute_materialized", lambda: sh.permute(s), b_gather),
                              ("combine", lambda: sh.combine(s), b_combine)):
         out[name] = {"us": time_it(fn) * 1e3, "bytes": nbytes}
+    # the plan alone (indexes, no row copy), then the copy kernel alone as the
+    # difference: both permute forms run the same plan launch first
+    sh.fused_gather = True
+    plan_us = time_it(lambda: sh.permute(s)) * 1e3
+    out["gather_copy"] = {"us": max(out["permute_materialized"]["us"] - plan_us, 1e-3),
+                          "bytes": 2 * H * (M + m_pad),
+                          "how": "permute into x_perm minus the plan-only permute (same plan launch)"}
     sh.fused_gather = fused
     sh.permute(s)
     out["bulk_copy"] = {"us": bulk_copy_ms * 1e3, "bytes": b_bulk}
     for d in out.values():
         gbs = d["bytes"] / (d["us"] * 1e-6) / 1e9
         d.update({"us": round(d["us"], 2), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    # the launches before the expert phase in the fused-gather layer: route
+    # (two kernels) and the plan; latency-bound, so no byte rate
+    out["front_end"] = {"us": round(out["route"]["us"] + plan_us, 2), "route_us": out["route"]["us"],
+                        "plan_us": round(plan_us, 2)}
     return out
 
 
@@ -471,7 +484,8 @@ def bench_workload(wid, args, torch, want_cpu, headline):
     mfma = stored_mfma(w.name, tb, b_fused)
     hbm = hbm_phases(sh, w, torch, M, m_pad, remote, ph[(b_fused, MOE_MODE_SEQUENTIAL)]["exposed"])
     log(f"[bench] {w.name} HBM-bound steps: " + ", ".join(
-        f"{k} {v['us']:.1f} us {v['GB/s']:.0f} GB/s ({v['frac']:.2f})" for k, v in hbm.items()))
+        f"{k} {v['us']:.1f} us {v['GB/s']:.0f} GB/s ({v['frac']:.2f})" for k, v in hbm.items() if "GB/s" in v)
+        + f"; front end (route, plan) {hbm['front_end']['us']:.1f} us")
 
     layer_d = {"valid_rows": M, "remote_rows": remote, "padded_rows": m_pad,
                "algorithmic_tflop": round(flops / 1e12, 4),

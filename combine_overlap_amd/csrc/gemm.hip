@@ -98,6 +98,13 @@ enum { EPI_PLAIN = 0, EPI_SILU = 1, EPI_GATED = 2 };
 constexpr int kMaxSplitSerial = 4;
 constexpr int kMaxSplitShared = 8;
 constexpr int kMinSplitSteps = 8;   // k-steps per chunk at least
+// ... and in the output projection when a queue holds less than one round of
+// tiles (a launch-bound layer: H = 512, F = 1024 gives 6 tiles of 16 k-steps
+// for 256 workgroups), where the chunks share the reduction: its output
+// projection 38 -> 30 us on MI355X. Not in the first projection, whose last
+// chunk sums the whole tile alone (there 4-step chunks were slower: 28 ->
+// 35 us), nor past one round, where the split only evens out the last one.
+constexpr int kMinSplitStepsSparse = 4;
 // buffer offset of gathered padding rows: past any x a resource describes
 // (x must stay below 2 GiB for the buffer form, so offset + k offset < 2^32)
 constexpr uint32_t kBufOutOfRange = 0x80000000u;
@@ -232,7 +239,7 @@ struct Item {
 };
 
 __device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int n_rrt, int x, int i, int px, int nk,
-                                           int max_split) {
+                                           int max_split, int min_steps_sparse) {
   Item it{-1, 0, 1, 0};
   const int bx = x / a.xn, nx = x - (x / a.xn) * a.xn;
   if (bx >= n_rt || nx >= a.tiles_n) return it;
@@ -241,7 +248,7 @@ __device__ __forceinline__ Item queue_item(const GemmArgs& a, int n_rt, int n_rr
   const int T = nb * nn;
   const int tail = T % px;
   int s = tail > 0 ? px / tail : 1;
-  s = min(s, min(max_split, nk / kMinSplitSteps));
+  s = min(s, min(max_split, nk / (T < px ? min_steps_sparse : kMinSplitSteps)));
   if (tail * s > kTailSlots) s = kTailSlots / tail;
   // test knob: the whole tiles in reverse queue order (the split tail tiles
   // stay the same tiles, so every tile is summed as without the knob)
@@ -622,7 +629,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
       while (tried < kXcds) {
         const int i = __hip_atomic_fetch_add(a.my_ctr + q * kCtrStride, 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-        it = queue_item(a, n_rt, n_rrt, q, i, px, nk, kMaxSplit);
+        it = queue_item(a, n_rt, n_rrt, q, i, px, nk, kMaxSplit, kShared ? kMinSplitStepsSparse : kMinSplitSteps);
         if (it.tile >= 0) break;
         q = (q + 1) & (kXcds - 1);
         ++tried;
