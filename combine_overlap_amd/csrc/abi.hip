@@ -7,6 +7,10 @@
 
 #include <mutex>
 
+#ifndef MOE_BULK_WG_PER_CU
+#define MOE_BULK_WG_PER_CU 4   // workgroups per CU of the baseline's bulk copy
+#endif
+
 // ---- scratch of moe_expert_forward_noalloc ------------------------------
 // The K-split partial tiles and the tile-queue / tail / copy counters of the
 // two GEMM launches, in a file-scope device array instead of the caller's
@@ -434,7 +438,7 @@ static int expert_forward(moe_ctx_t* ctx, const moe_shape_t* shape, const uint16
                                   ctx->knobs, ps))) != MOE_OK)
       return rc;
     if ((rc = rec(2, ps)) != MOE_OK) return rc;
-    if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, 4 * ncu, ps))) != MOE_OK) return rc;
+    if ((rc = hip_rc(launch_bulk_copy(g, y_perm, bufs, p, MOE_BULK_WG_PER_CU * ncu, ps))) != MOE_OK) return rc;
     if ((rc = rec(3, ps)) != MOE_OK) return rc;
     if ((rc = rec(4, ps)) != MOE_OK) return rc;
     ctx->timed = tm;
