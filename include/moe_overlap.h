@@ -333,7 +333,8 @@ int moe_plan_partition(const moe_shape_t* shape, const int32_t* counts_host,
  *            MOE_MODE_ROLE_SWITCH: both projections on all CUs, the output
  *            projection's workgroups doing the consumer's work as well: before
  *            each tile a workgroup claims the next 64 KiB copy units of the
- *            remote segments (schedule order, up to 8 per claim, one
+ *            remote segments (schedule order, up to 8 per claim and at most
+ *            an even share of those left over 64 workgroups, one
  *            fetch-and-add) once the segment holding them has all its tiles
  *            flagged, and copies them; a claim stays with its workgroup until
  *            copied. Once the tiles run out the workgroups claim and copy the
