@@ -570,7 +570,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void k_gemm(const GemmArgs a) {
   if constexpr (CONS) {
     const int n_cons = a.n_cons > 0 ? a.n_cons : a.meta[META_CAUTO];
     if ((int)blockIdx.x < n_cons) {
-      consume<C::NT, 4, 32>(a.cons, blockIdx.x, n_cons, reinterpret_cast<int*>(lds), s_copy);
+      // a copy of fewer units than four per consumer workgroup goes one unit
+      // per workgroup, so as many workgroups as it has units share it
+      if (a.meta[META_NUNITS] < 4 * n_cons)
+        consume<C::NT, 1, (int)(kCopyUnitBytes / 16 / C::NT)>(a.cons, blockIdx.x, n_cons,
+                                                               reinterpret_cast<int*>(lds), s_copy);
+      else
+        consume<C::NT, 4, 32>(a.cons, blockIdx.x, n_cons, reinterpret_cast<int*>(lds), s_copy);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this workgroup's copies have completed
       __syncthreads();
       if (tid == 0) stamp_max(a.meta, META_T_CONS);
