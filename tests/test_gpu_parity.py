@@ -19,6 +19,9 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("tiny_full_tb64", WORKLOADS[1], 0, 64, 1, 4, 0),
     ("tiny_full_tb128_r2", WORKLOADS[1], 2, 128, 2, 2, 0),
+    # more consumer workgroups than copy units: one unit per workgroup, the
+    # rest copy nothing and join the producer at once
+    ("tiny_full_c48", WORKLOADS[1], 0, 64, 2, 48, 0),
     ("mixtral_mini_tb128", Workload("mixtral_mini", 4, 512, 1024, 2048, 8, 2, True, "softmax",
                                     "normal", w_std="fan_in"), 0, 128, 1, 8, 0),
     ("zipf_mini_tb256", Workload("zipf_mini", 4, 512, 1024, 1024, 8, 2, True, "softmax", "zipf",
